@@ -1,0 +1,178 @@
+"""CPU oracle for the strided, batched fp32 matrix product.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The
+product library neither imports nor links it, and this package imports
+nothing from the product: the two share no code.
+
+The arithmetic lives in ``ref_sgemm.c`` (plain C, fp64 accumulation, one
+output element at a time).  This module only compiles it with gcc, checks that
+every operand view stays inside its host buffer, and passes pointers through
+ctypes.
+
+Definition (StaleyNET "GPU Implementation", section "The matrix product"):
+for b < batch, i < m, j < n
+
+    C[b,i,j] <- alpha * sum_{p<k} A[b,i,p] * B[b,p,j]  (+ C[b,i,j] if accumulate)
+
+with X[b,r,c] = X_storage[b*sX_batch + r*sX_row + c*sX_col], strides counted in
+elements.  Sums are formed in fp64 in ascending p and rounded to fp32 once.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ref_sgemm.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_sgemm.so")
+
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_int = ctypes.c_int
+_fptr = ctypes.POINTER(ctypes.c_float)
+_i64ptr = ctypes.POINTER(ctypes.c_int64)
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH, extra_flags=()) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+           *extra_flags, src, "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _bind(lib):
+    lib.oracle_sgemm.restype = _int
+    lib.oracle_sgemm.argtypes = [
+        _i64, _i64, _i64, _i64, _f32,
+        _fptr, _i64, _i64, _i64,
+        _fptr, _i64, _i64, _i64,
+        _int,
+        _fptr, _i64, _i64, _i64,
+        _int,
+    ]
+    lib.oracle_sgemm_entries.restype = _int
+    lib.oracle_sgemm_entries.argtypes = [
+        _i64, _i64, _i64, _i64, _f32,
+        _fptr, _i64, _i64, _i64,
+        _fptr, _i64, _i64, _i64,
+        _int,
+        _fptr, _i64, _i64, _i64,
+        _i64, _i64ptr, _fptr,
+    ]
+    lib.oracle_num_threads.restype = _int
+    lib.oracle_num_threads.argtypes = []
+    return lib
+
+
+def load_library(path: str):
+    """Load an oracle build from `path` (used for the default build and for
+    deliberately broken copies in the oracle's own mutation tests)."""
+    return _bind(ctypes.CDLL(path))
+
+
+def _get_lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def _as_storage(x, name, writable=False):
+    if not isinstance(x, np.ndarray) or x.dtype != np.float32 or x.ndim != 1:
+        raise TypeError(f"{name} must be a 1-D float32 numpy array (the flat storage)")
+    if not x.flags.c_contiguous:
+        raise TypeError(f"{name} storage must be contiguous")
+    if writable and not x.flags.writeable:
+        raise TypeError(f"{name} must be writable")
+    return x
+
+
+def _check_view(storage, name, extents, strides):
+    """Every element the view can address must lie inside `storage`."""
+    if any(s < 0 for s in strides):
+        raise ValueError(f"{name}: negative stride")
+    if any(e == 0 for e in extents):
+        return
+    last = sum((e - 1) * s for e, s in zip(extents, strides))
+    if last >= storage.size:
+        raise ValueError(f"{name}: view reaches element {last}, storage has {storage.size}")
+
+
+def _ptr(x):
+    return x.ctypes.data_as(_fptr)
+
+
+def ref_sgemm(batch, m, n, k, alpha,
+              A, sA_batch, sA_row, sA_col,
+              B, sB_batch, sB_row, sB_col,
+              accumulate,
+              C, sC_batch, sC_row, sC_col,
+              reverse=False, lib=None):
+    """C <- alpha*A*B (+C) over host storages; writes C in place."""
+    lib = lib or _get_lib()
+    A = _as_storage(A, "A")
+    B = _as_storage(B, "B")
+    C = _as_storage(C, "C", writable=True)
+    if min(batch, m, n, k) < 0:
+        raise ValueError("negative size")
+    if batch and m and k:
+        _check_view(A, "A", (batch, m, k), (sA_batch, sA_row, sA_col))
+    if batch and n and k:
+        _check_view(B, "B", (batch, k, n), (sB_batch, sB_row, sB_col))
+    _check_view(C, "C", (batch, m, n), (sC_batch, sC_row, sC_col))
+    rc = lib.oracle_sgemm(batch, m, n, k, float(alpha),
+                          _ptr(A), sA_batch, sA_row, sA_col,
+                          _ptr(B), sB_batch, sB_row, sB_col,
+                          int(bool(accumulate)),
+                          _ptr(C), sC_batch, sC_row, sC_col,
+                          int(bool(reverse)))
+    if rc != 0:
+        raise RuntimeError(f"oracle_sgemm returned {rc}")
+    return C
+
+
+def ref_entries(batch, m, n, k, alpha,
+                A, sA_batch, sA_row, sA_col,
+                B, sB_batch, sB_row, sB_col,
+                accumulate,
+                C, sC_batch, sC_row, sC_col,
+                idx, lib=None):
+    """Return the float32 values the full product would store at the (b,i,j)
+    rows of `idx` (shape [count, 3]); C is only read (as C_old)."""
+    lib = lib or _get_lib()
+    A = _as_storage(A, "A")
+    B = _as_storage(B, "B")
+    C = _as_storage(C, "C")
+    idx = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 3)
+    if batch and m and k:
+        _check_view(A, "A", (batch, m, k), (sA_batch, sA_row, sA_col))
+    if batch and n and k:
+        _check_view(B, "B", (batch, k, n), (sB_batch, sB_row, sB_col))
+    if accumulate:
+        _check_view(C, "C", (batch, m, n), (sC_batch, sC_row, sC_col))
+    out = np.empty(idx.shape[0], dtype=np.float32)
+    rc = lib.oracle_sgemm_entries(batch, m, n, k, float(alpha),
+                                  _ptr(A), sA_batch, sA_row, sA_col,
+                                  _ptr(B), sB_batch, sB_row, sB_col,
+                                  int(bool(accumulate)),
+                                  _ptr(C), sC_batch, sC_row, sC_col,
+                                  idx.shape[0], idx.ctypes.data_as(_i64ptr), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_sgemm_entries: index outside the product")
+    return out
+
+
+def num_threads(lib=None) -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return (lib or _get_lib()).oracle_num_threads()

@@ -1,0 +1,266 @@
+"""Seeded synthetic inputs for the strided, batched fp32 product.
+
+This module only draws numbers and lays them out in memory; it performs none
+of the product's arithmetic.  Both sides of every parity check (the HIP
+library and the CPU oracle) receive the very same host bytes from here.
+
+Recipe (stated once, used everywhere):
+  * numpy ``SeedSequence(2024)`` -- the seed kael's device tests use (kael
+    book ch. 09 "CUDA backend", section "How it is tested") -- is spawned once
+    per workload, and each workload's child is spawned once per tensor; every
+    tensor is drawn from its own ``Generator(PCG64)``.
+  * Values are drawn in float64 and rounded to float32 on the host.
+  * "Stored" arrays are row-major and contiguous; a transposed read is the
+    stored array with its row and column strides exchanged (StaleyNET
+    "GPU Implementation", section "The matrix product").
+  * Strides are (batch, row, col), counted in float elements.
+
+The five workloads mirror the users of the product the pages name: a tiny
+square product, a linear layer y = x W^T with W read transposed (rvllm post,
+section "Matmuls go to cuBLAS"), both attention products over all heads and
+sequences in one batch with 1/sqrt(head_dim) folded into alpha (same
+section), a spectrogram-style product against a shared DFT basis (StaleyNET
+"GPU Implementation", "The matrix product" names the spectrogram), and a large
+square product with A read transposed, alpha = 0.5 and accumulation.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+ROOT_SEED = 2024
+
+# Workload names in the order they are spawned from the root seed.
+WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc")
+
+
+@dataclasses.dataclass
+class Operand:
+    """A flat float32 host storage plus the (batch, row, col) strides of the
+    logical matrix view over it."""
+    storage: np.ndarray
+    strides: tuple
+
+    @property
+    def s_batch(self):
+        return self.strides[0]
+
+    @property
+    def s_row(self):
+        return self.strides[1]
+
+    @property
+    def s_col(self):
+        return self.strides[2]
+
+
+@dataclasses.dataclass
+class Problem:
+    """One call: C <- alpha*A*B (+C) over batch x (m x k)(k x n)."""
+    name: str
+    batch: int
+    m: int
+    n: int
+    k: int
+    alpha: float
+    accumulate: bool
+    A: Operand
+    B: Operand
+    C: Operand          # storage holds C_old (read only when accumulating)
+    notes: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.m * self.n * self.k
+
+    def call_args(self, a, b, c):
+        """Positional argument list of the entry point with the three storages
+        replaced by `a`, `b`, `c` (pointers or arrays)."""
+        return [self.batch, self.m, self.n, self.k, self.alpha,
+                a, *self.A.strides, b, *self.B.strides,
+                int(self.accumulate), c, *self.C.strides]
+
+
+def _children(name: str):
+    idx = WORKLOADS.index(name)
+    return np.random.SeedSequence(ROOT_SEED).spawn(len(WORKLOADS))[idx]
+
+
+def _gens(name: str, count: int):
+    return [np.random.Generator(np.random.PCG64(s)) for s in _children(name).spawn(count)]
+
+
+def _f32(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32).ravel())
+
+
+def square64() -> Problem:
+    """1 x 64x64x64, A and B row-major U[-1,1], alpha 1, no accumulate."""
+    ga, gb, gc = _gens("square64", 3)
+    A = _f32(ga.uniform(-1.0, 1.0, (64, 64)))
+    B = _f32(gb.uniform(-1.0, 1.0, (64, 64)))
+    C = np.zeros(64 * 64, np.float32)
+    return Problem("square64", 1, 64, 64, 64, 1.0, False,
+                   Operand(A, (4096, 64, 1)), Operand(B, (4096, 64, 1)), Operand(C, (4096, 64, 1)))
+
+
+def linear_xWt() -> Problem:
+    """y = x W^T: x [2048][960] N(0,1), W stored [2560][960] N(0,0.02) and
+    read transposed (B[p][j] = W[j][p], strides (0, 1, 960))."""
+    gx, gw = _gens("linear_xWt", 2)
+    x = _f32(gx.normal(0.0, 1.0, (2048, 960)))
+    W = _f32(gw.normal(0.0, 0.02, (2560, 960)))
+    y = np.zeros(2048 * 2560, np.float32)
+    return Problem("linear_xWt", 1, 2048, 2560, 960, 1.0, False,
+                   Operand(x, (0, 960, 1)), Operand(W, (0, 1, 960)), Operand(y, (0, 2560, 1)))
+
+
+def attn_qk() -> Problem:
+    """S = (1/8) Q K^T for 8 sequences x 15 heads = 120 batches, head-major
+    [120][512][64]; K read transposed (strides (32768, 1, 64))."""
+    gq, gk = _gens("attn_qk", 2)
+    Q = _f32(gq.normal(0.0, 1.0, (120, 512, 64)))
+    K = _f32(gk.normal(0.0, 1.0, (120, 512, 64)))
+    S = np.zeros(120 * 512 * 512, np.float32)
+    return Problem("attn_qk", 120, 512, 512, 64, 1.0 / math.sqrt(64.0), False,
+                   Operand(Q, (32768, 64, 1)), Operand(K, (32768, 1, 64)),
+                   Operand(S, (262144, 512, 1)))
+
+
+def attn_pv() -> Problem:
+    """O = P V: P [120][512][512] i.i.d. U[0, 1/512] (softmax-like row scale,
+    not renormalised), V [120][512][64] N(0,1)."""
+    gp, gv = _gens("attn_pv", 2)
+    P = _f32(gp.uniform(0.0, 1.0 / 512.0, (120, 512, 512)))
+    V = _f32(gv.normal(0.0, 1.0, (120, 512, 64)))
+    O = np.zeros(120 * 512 * 64, np.float32)
+    return Problem("attn_pv", 120, 512, 64, 512, 1.0, False,
+                   Operand(P, (262144, 512, 1)), Operand(V, (32768, 64, 1)),
+                   Operand(O, (32768, 64, 1)))
+
+
+SPEC_BATCH, SPEC_FRAMES, SPEC_WIN, SPEC_HOP, SPEC_BINS = 4, 4096, 512, 128, 257
+SPEC_RATE = 16000.0
+
+
+def dft_basis(win: int = SPEC_WIN, bins: int = SPEC_BINS) -> np.ndarray:
+    """[win][2*bins] real DFT basis: column j < bins is cos(2 pi j t / win),
+    column bins + j is sin(2 pi j t / win); computed in fp64, rounded to fp32."""
+    t = np.arange(win, dtype=np.float64)[:, None]
+    j = np.arange(bins, dtype=np.float64)[None, :]
+    ang = 2.0 * math.pi * ((t * j) % win) / win
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def spectrogram() -> Problem:
+    """frames [4][4096][512] of a 3-tone signal plus N(0, 0.1) noise (hop 128)
+    times the shared basis [512][514] (batch stride 0)."""
+    gs = _gens("spectrogram", 2)
+    gsig, gnoise = gs
+    length = (SPEC_FRAMES - 1) * SPEC_HOP + SPEC_WIN
+    s = np.arange(length, dtype=np.float64)
+    frames = np.empty((SPEC_BATCH, SPEC_FRAMES, SPEC_WIN), np.float64)
+    starts = np.arange(SPEC_FRAMES)[:, None] * SPEC_HOP + np.arange(SPEC_WIN)[None, :]
+    for b in range(SPEC_BATCH):
+        amp = gsig.uniform(0.1, 1.0, 3)
+        freq = gsig.uniform(50.0, 4000.0, 3)
+        phase = gsig.uniform(0.0, 2.0 * math.pi, 3)
+        x = sum(amp[q] * np.sin(2.0 * math.pi * freq[q] * s / SPEC_RATE + phase[q]) for q in range(3))
+        x = x + gnoise.normal(0.0, 0.1, length)
+        frames[b] = x[starts]
+    n = 2 * SPEC_BINS
+    C = np.zeros(SPEC_BATCH * SPEC_FRAMES * n, np.float32)
+    return Problem("spectrogram", SPEC_BATCH, SPEC_FRAMES, n, SPEC_WIN, 1.0, False,
+                   Operand(_f32(frames), (SPEC_FRAMES * SPEC_WIN, SPEC_WIN, 1)),
+                   Operand(_f32(dft_basis()), (0, n, 1)),
+                   Operand(C, (SPEC_FRAMES * n, n, 1)))
+
+
+def square4096_acc(batch: int = 4, size: int = 4096) -> Problem:
+    """4 x 4096^3: A stored transposed [batch][k][m] and read with swapped
+    strides, B row-major, all U[-1,1]; C_old U[-1,1], alpha 0.5, accumulate."""
+    ga, gb, gc = _gens("square4096_acc", 3)
+    s2 = size * size
+    A = _f32(ga.uniform(-1.0, 1.0, batch * s2))
+    B = _f32(gb.uniform(-1.0, 1.0, batch * s2))
+    C = _f32(gc.uniform(-1.0, 1.0, batch * s2))
+    return Problem("square4096_acc", batch, size, size, size, 0.5, True,
+                   Operand(A, (s2, 1, size)), Operand(B, (s2, size, 1)), Operand(C, (s2, size, 1)))
+
+
+BUILDERS = {
+    "square64": square64,
+    "linear_xWt": linear_xWt,
+    "attn_qk": attn_qk,
+    "attn_pv": attn_pv,
+    "spectrogram": spectrogram,
+    "square4096_acc": square4096_acc,
+}
+
+
+def workload(name: str) -> Problem:
+    return BUILDERS[name]()
+
+
+# ---------------------------------------------------------------------------
+# Parametric problems for parity tests.
+# ---------------------------------------------------------------------------
+
+def layout_strides(rows: int, cols: int, contiguous: str, pad: int = 0, batch_gap: int = 0):
+    """Storage size and (batch, row, col) strides of a rows x cols logical
+    matrix stored with `contiguous` in {"row", "col"}: "row" means the column
+    index is the fast one (row-major), "col" means stored transposed.  `pad`
+    adds unused elements after every stored line, `batch_gap` after every
+    matrix."""
+    if contiguous == "row":
+        ld = cols + pad
+        per = rows * ld
+        return per + batch_gap, (per + batch_gap, ld, 1)
+    if contiguous == "col":
+        ld = rows + pad
+        per = cols * ld
+        return per + batch_gap, (per + batch_gap, 1, ld)
+    raise ValueError(contiguous)
+
+
+def random_problem(seed: int, batch: int, m: int, n: int, k: int, *,
+                   a_major: str = "row", b_major: str = "row", c_major: str = "row",
+                   alpha: float = 1.0, accumulate: bool = False,
+                   pad: int = 0, b_broadcast: bool = False,
+                   dist: str = "uniform", name: str = "random") -> Problem:
+    """Random problem with the requested storage orders.
+
+    dist: "uniform" U[-1,1]; "normal" N(0,1); "int" integers in [-3, 3]
+    (every partial sum is exact in fp32, so the result is unique);
+    "ones" every A and B entry 1.0.
+    """
+    ss = np.random.SeedSequence([ROOT_SEED, seed])
+    ga, gb, gc = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3)]
+
+    def draw(g, count):
+        if dist == "uniform":
+            return _f32(g.uniform(-1.0, 1.0, count))
+        if dist == "normal":
+            return _f32(g.normal(0.0, 1.0, count))
+        if dist == "int":
+            return _f32(g.integers(-3, 4, count))
+        if dist == "ones":
+            return np.ones(count, np.float32)
+        raise ValueError(dist)
+
+    per_a, sa = layout_strides(m, k, a_major, pad, pad)
+    per_b, sb = layout_strides(k, n, b_major, pad, pad)
+    per_c, sc = layout_strides(m, n, c_major, pad, pad)
+    nb_b = 1 if b_broadcast else batch
+    if b_broadcast:
+        sb = (0, sb[1], sb[2])
+    A = draw(ga, max(per_a * batch, 1))
+    B = draw(gb, max(per_b * nb_b, 1))
+    if dist == "int":
+        C = _f32(gc.integers(-3, 4, max(per_c * batch, 1)))
+    else:
+        C = _f32(gc.uniform(-1.0, 1.0, max(per_c * batch, 1)))
+    return Problem(name, batch, m, n, k, alpha, accumulate,
+                   Operand(A, sa), Operand(B, sb), Operand(C, sc))

@@ -1,0 +1,354 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, independent of the oracle's own code.
+
+Each `pin_*` takes an oracle library handle (the default build, or a
+deliberately broken copy in the mutation tests) and raises AssertionError on a
+mismatch.  None of them re-types the oracle's sum: they use closed forms
+(all-ones gives k*alpha), identities, the pages' printed worked examples
+(tests/golden/), exact integer brute force checked by numpy's int64 matmul,
+numpy's float64 matmul on strided views, and invariants the definition
+implies (stride exchange, C^T = B^T A^T, batch slicing, broadcast,
+accumulation, order independence).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from helpers import view, load_golden, ints, column_major_strides
+from strided_fp32_gemm_amd.workloads import random_problem, layout_strides
+
+LAYOUTS = [(a, b) for a in ("row", "col") for b in ("row", "col")]
+
+
+def _run(p, lib, C=None, reverse=False):
+    C = p.C.storage.copy() if C is None else C
+    oracle.ref_sgemm(*p.call_args(p.A.storage, p.B.storage, C), reverse=reverse, lib=lib)
+    return C
+
+
+def _out(p, C):
+    return np.array(view(C, p.batch, p.m, p.n, p.C.strides))
+
+
+def _mat_problem(A2, B2, a_major="row", b_major="row", alpha=1.0):
+    """Problem over explicit 2-D logical matrices stored in the given orders."""
+    from strided_fp32_gemm_amd.workloads import Operand, Problem
+    m, k = A2.shape
+    _, n = B2.shape
+
+    def store(M, major):
+        r, c = M.shape
+        if major == "row":
+            return Operand(np.ascontiguousarray(M, np.float32).ravel(), (r * c, c, 1))
+        return Operand(np.ascontiguousarray(M.T, np.float32).ravel(), (r * c, 1, r))
+    return Problem("mat", 1, m, n, k, alpha, False, store(A2, a_major), store(B2, b_major),
+                   Operand(np.zeros(max(m * n, 1), np.float32), (m * n, n, 1)))
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_all_ones(lib):
+    """A = 1, B = 1 => C = k*alpha exactly (+ C_old); every transpose case."""
+    for a_major, b_major in LAYOUTS:
+        for k in (1, 7, 64, 960, 4096):
+            for alpha in (1.0, 0.5):
+                for acc in (False, True):
+                    p = random_problem(k, 2, 3, 5, k, a_major=a_major, b_major=b_major,
+                                       alpha=alpha, accumulate=acc, dist="ones")
+                    C = _run(p, lib)
+                    c_old = view(p.C.storage, 2, 3, 5, p.C.strides).astype(np.float64)
+                    want = (c_old if acc else 0.0) + k * alpha
+                    got = _out(p, C)
+                    assert np.array_equal(got, np.float32(want) + np.zeros_like(got)), \
+                        (a_major, b_major, k, alpha, acc)
+
+
+def pin_identity(lib):
+    """A I = A and I B = B, bitwise, with each operand in both orientations."""
+    rng = np.random.default_rng(7)
+    A = rng.standard_normal((6, 9)).astype(np.float32)
+    for a_major in ("row", "col"):
+        for i_major in ("row", "col"):
+            p = _mat_problem(A, np.eye(9, dtype=np.float32), a_major, i_major)
+            assert np.array_equal(_out(p, _run(p, lib))[0], A), ("A I", a_major, i_major)
+            p = _mat_problem(np.eye(6, dtype=np.float32), A, i_major, a_major)
+            assert np.array_equal(_out(p, _run(p, lib))[0], A), ("I B", i_major, a_major)
+
+
+def pin_k_zero(lib):
+    """k = 0 is the empty sum: C <- 0, or C unchanged when accumulating."""
+    for acc in (False, True):
+        p = random_problem(3, 2, 4, 5, 0, accumulate=acc)
+        C = _run(p, lib)
+        want = view(p.C.storage, 2, 4, 5, p.C.strides) if acc else 0.0
+        assert np.array_equal(_out(p, C), np.zeros((2, 4, 5), np.float32) + want), acc
+
+
+# ---------------------------------------------------- the pages' worked values
+
+def pin_golden_transpose_trace(lib):
+    """kael ch. 09, "Moving tensors between devices": x.T of 0..5 read with
+    strides (1, 3) and copied contiguously is 0 3 1 4 2 5."""
+    g = load_golden("kael_transpose_trace.txt")
+    storage = np.array(ints(g["storage"]), np.float32)
+    rows, cols = ints(g["transposed_shape"])
+    s_row, s_col = ints(g["transposed_strides"])
+    from strided_fp32_gemm_amd.workloads import Operand, Problem
+    p = Problem("trace", 1, rows, cols, cols, 1.0, False,
+                Operand(storage, (0, s_row, s_col)),
+                Operand(np.eye(cols, dtype=np.float32).ravel(), (0, cols, 1)),
+                Operand(np.zeros(rows * cols, np.float32), (0, cols, 1)))
+    C = _run(p, lib)
+    assert C.tolist() == [float(v) for v in ints(g["transposed_contiguous"])]
+
+
+def pin_golden_column_major(lib):
+    """kael ch. 09, "cuBLAS": the bytes 1..6 read row-major as 2 x 3 give
+    [[1,2,3],[4,5,6]]; read column-major as 3 x 2 they give its transpose."""
+    g = load_golden("kael_column_major.txt")
+    storage = np.array(ints(g["storage"]), np.float32)
+    from strided_fp32_gemm_amd.workloads import Operand, Problem
+    for shape_key, vals_key, strides in (
+            ("row_major_shape", "row_major", None),
+            ("column_major_shape", "column_major", "cm")):
+        rows, cols = ints(g[shape_key])
+        st = (cols, 1) if strides is None else column_major_strides(rows)
+        p = Problem("cm", 1, rows, cols, cols, 1.0, False,
+                    Operand(storage, (0, *st)),
+                    Operand(np.eye(cols, dtype=np.float32).ravel(), (0, cols, 1)),
+                    Operand(np.zeros(rows * cols, np.float32), (0, cols, 1)))
+        assert _run(p, lib).tolist() == [float(v) for v in ints(g[vals_key])], shape_key
+
+
+def _blas_operand(trans: str, ld: int, rows: int, cols: int):
+    """(row, col) strides of op(X) for a column-major X with leading
+    dimension ld, where op(X) is rows x cols."""
+    r, c = column_major_strides(ld)
+    return (c, r) if trans == "T" else (r, c)
+
+
+def pin_blas_linear_mapping(lib):
+    """rvllm, "Matmuls go to cuBLAS": the column-major call (transa T, transb
+    N, m = out, n = rows, k = in, lda = ldb = in, ldc = out) on the row-major
+    buffers computes the same bytes as y = x W^T with W read transposed."""
+    g = load_golden("rvllm_linear_blas.txt")
+    rows, in_f, out_f = 7, 13, 5
+    sym = {"out_features": out_f, "rows": rows, "in_features": in_f}
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((rows, in_f)).astype(np.float32).ravel()
+    W = rng.standard_normal((out_f, in_f)).astype(np.float32).ravel()
+    bufs = {"weight": W, "x": x}
+    m, n, k = sym[g["m"]], sym[g["n"]], sym[g["k"]]
+    sa = _blas_operand(g["transa"], sym[g["lda"]], m, k)
+    sb = _blas_operand(g["transb"], sym[g["ldb"]], k, n)
+    sc = column_major_strides(sym[g["ldc"]])
+    y_blas = np.zeros(rows * out_f, np.float32)
+    oracle.ref_sgemm(1, m, n, k, float(g["alpha"]), bufs[g["first_operand"]], 0, *sa,
+                     bufs[g["second_operand"]], 0, *sb, 0, y_blas, 0, *sc, lib=lib)
+    y_rm = np.zeros(rows * out_f, np.float32)
+    oracle.ref_sgemm(1, rows, out_f, in_f, 1.0, x, 0, in_f, 1, W, 0, 1, in_f,
+                     0, y_rm, 0, out_f, 1, lib=lib)
+    assert np.array_equal(y_blas, y_rm)
+    ref = x.reshape(rows, in_f).astype(np.float64) @ W.reshape(out_f, in_f).astype(np.float64).T
+    assert np.allclose(y_rm.reshape(rows, out_f), ref, rtol=1e-6, atol=1e-6)
+
+
+def pin_blas_rowmajor_trick(lib):
+    """kael ch. 09, "cuBLAS": (N, N, columns, rows, inner) with b first
+    (ld columns) and a second (ld inner), output ld columns, is row-major
+    a @ b; also C^T = B^T A^T through an output with exchanged strides."""
+    g = load_golden("kael_cublas_rowmajor.txt")
+    rows, inner, cols = 6, 11, 9
+    sym = {"rows": rows, "inner": inner, "columns": cols}
+    rng = np.random.default_rng(12)
+    a = rng.standard_normal((rows, inner)).astype(np.float32).ravel()
+    b = rng.standard_normal((inner, cols)).astype(np.float32).ravel()
+    bufs = {"a": a, "b": b}
+    m, n, k = sym[g["m"]], sym[g["n"]], sym[g["k"]]
+    sa = _blas_operand(g["transa"], sym[g["lda"]], m, k)
+    sb = _blas_operand(g["transb"], sym[g["ldb"]], k, n)
+    sc = column_major_strides(sym[g["ldc"]])
+    out_blas = np.zeros(rows * cols, np.float32)
+    oracle.ref_sgemm(1, m, n, k, 1.0, bufs[g["first_operand"]], 0, *sa,
+                     bufs[g["second_operand"]], 0, *sb, 0, out_blas, 0, *sc, lib=lib)
+    out_rm = np.zeros(rows * cols, np.float32)
+    oracle.ref_sgemm(1, rows, cols, inner, 1.0, a, 0, inner, 1, b, 0, cols, 1,
+                     0, out_rm, 0, cols, 1, lib=lib)
+    assert np.array_equal(out_blas, out_rm)
+
+
+# ------------------------------------------------------ exact brute force
+
+def pin_exact_bruteforce(lib, sizes=range(1, 9)):
+    """Every m, n, k in 1..8, all four transpose cases, batch 1 and 3,
+    accumulate on/off, alpha 1 and 0.5, integer data in [-3, 3]: each partial
+    sum is exact, so the result is unique; numpy's int64 matmul gives it."""
+    rng = np.random.default_rng(2024)
+    for m in sizes:
+        for n in sizes:
+            for k in sizes:
+                for a_major, b_major in LAYOUTS:
+                    for batch in (1, 3):
+                        acc = (m + n + k + batch) % 2 == 0
+                        alpha = 0.5 if (m * n * k) % 2 else 1.0
+                        for acc_, alpha_ in ((acc, alpha), (not acc, 1.5 - alpha)):
+                            _exact_case(lib, rng, batch, m, n, k, a_major, b_major, alpha_, acc_)
+
+
+def _exact_case(lib, rng, batch, m, n, k, a_major, b_major, alpha, acc):
+    per_a, sa = layout_strides(m, k, a_major)
+    per_b, sb = layout_strides(k, n, b_major)
+    per_c, sc = layout_strides(m, n, "row")
+    A = rng.integers(-3, 4, per_a * batch).astype(np.float32)
+    B = rng.integers(-3, 4, per_b * batch).astype(np.float32)
+    C = rng.integers(-3, 4, per_c * batch).astype(np.float32)
+    Ai = view(A, batch, m, k, sa).astype(np.int64)
+    Bi = view(B, batch, k, n, sb).astype(np.int64)
+    exact = np.matmul(Ai, Bi).astype(np.float64) * alpha
+    if acc:
+        exact = exact + view(C, batch, m, n, sc)
+    out = C.copy()
+    oracle.ref_sgemm(batch, m, n, k, alpha, A, *sa, B, *sb, int(acc), out, *sc, lib=lib)
+    got = view(out, batch, m, n, sc)
+    assert np.array_equal(got, exact.astype(np.float32)), (batch, m, n, k, a_major, b_major, alpha, acc)
+
+
+# ------------------------------------------------ library cross-check (fp64)
+
+AWKWARD = [(17, 33, 9), (5, 129, 31), (1, 1, 1), (4, 4, 4), (5, 3, 9), (8, 16, 7),
+           (33, 20, 65), (64, 1, 64), (1, 64, 1), (127, 129, 128), (3, 514, 70)]
+
+
+def pin_numpy_float64(lib, shapes=AWKWARD):
+    """Against numpy float64 matmul on the strided views: the oracle must be
+    the fp32 rounding of the fp64 result (half an ulp, plus fp64 noise).
+    Shapes (rows, inner, columns) are the pages' awkward test sizes:
+    StaleyNET "Testing the kernels" and kael ch. 09 "How it is tested"."""
+    for idx, (m, k, n) in enumerate(shapes):
+        for a_major, b_major in LAYOUTS:
+            p = random_problem(100 + idx, 2, m, n, k, a_major=a_major, b_major=b_major,
+                               alpha=0.75, accumulate=True, pad=3)
+            C = _run(p, lib)
+            Av = view(p.A.storage, 2, m, k, p.A.strides).astype(np.float64)
+            Bv = view(p.B.storage, 2, k, n, p.B.strides).astype(np.float64)
+            Cold = view(p.C.storage, 2, m, n, p.C.strides).astype(np.float64)
+            ref = 0.75 * np.matmul(Av, Bv) + Cold
+            got = _out(p, C).astype(np.float64)
+            scale = k * np.abs(Av).max() * np.abs(Bv).max() + np.abs(Cold).max()
+            tol = 0.5 * np.spacing(np.abs(got).astype(np.float32)).astype(np.float64) + 1e-12 * scale
+            assert np.all(np.abs(got - ref) <= tol), (m, n, k, a_major, b_major)
+
+
+# ------------------------------------------------------------- invariants
+
+def pin_stride_swap(lib):
+    """Reading a stored X^T with exchanged strides equals using an explicit
+    row-major copy of X, bitwise (StaleyNET "The matrix product": a
+    transposed matrix is the same memory with the two distances exchanged)."""
+    for a_major, b_major in LAYOUTS:
+        p = random_problem(21, 2, 13, 11, 10, a_major=a_major, b_major=b_major, dist="normal")
+        Acopy = np.ascontiguousarray(view(p.A.storage, 2, 13, 10, p.A.strides)).ravel()
+        Bcopy = np.ascontiguousarray(view(p.B.storage, 2, 10, 11, p.B.strides)).ravel()
+        C1 = _run(p, lib)
+        C2 = p.C.storage.copy()
+        oracle.ref_sgemm(2, 13, 11, 10, p.alpha, Acopy, 130, 10, 1, Bcopy, 110, 11, 1,
+                         0, C2, *p.C.strides, lib=lib)
+        assert np.array_equal(C1, C2), (a_major, b_major)
+
+
+def pin_transpose_identity(lib):
+    """C^T = B^T A^T: the product of the exchanged-stride views of B and A,
+    written through C's exchanged strides, gives the same bytes as C."""
+    for a_major, b_major in LAYOUTS:
+        p = random_problem(22, 3, 9, 14, 12, a_major=a_major, b_major=b_major, dist="normal")
+        C1 = _run(p, lib)
+        C2 = p.C.storage.copy()
+        sa, sb, sc = p.A.strides, p.B.strides, p.C.strides
+        oracle.ref_sgemm(3, 14, 9, 12, p.alpha, p.B.storage, sb[0], sb[2], sb[1],
+                         p.A.storage, sa[0], sa[2], sa[1], 0, C2, sc[0], sc[2], sc[1], lib=lib)
+        assert np.array_equal(C1, C2), (a_major, b_major)
+
+
+def pin_batch_slices(lib):
+    """Each batch of a batched call equals a batch-1 call on its slice, and a
+    batch stride of 0 equals explicit replication, bitwise."""
+    p = random_problem(23, 3, 10, 7, 9, a_major="col", b_major="row", pad=2, dist="normal",
+                       accumulate=True, alpha=-1.25)
+    C = _run(p, lib)
+    for b in range(3):
+        Cb = p.C.storage.copy()
+        sa, sb, sc = p.A.strides, p.B.strides, p.C.strides
+        oracle.ref_sgemm(1, 10, 7, 9, p.alpha, p.A.storage[b * sa[0]:], 0, sa[1], sa[2],
+                         p.B.storage[b * sb[0]:], 0, sb[1], sb[2], 1,
+                         Cb[b * sc[0]:], 0, sc[1], sc[2], lib=lib)
+        assert np.array_equal(view(Cb, 3, 10, 7, sc)[b], view(C, 3, 10, 7, sc)[b]), b
+    q = random_problem(24, 4, 6, 5, 8, b_broadcast=True, dist="normal")
+    Cq = _run(q, lib)
+    per_b = 8 * 5
+    Brep = np.tile(q.B.storage[:per_b], 4)
+    Cr = q.C.storage.copy()
+    oracle.ref_sgemm(4, 6, 5, 8, 1.0, q.A.storage, *q.A.strides, Brep, per_b, 5, 1,
+                     0, Cr, *q.C.strides, lib=lib)
+    assert np.array_equal(Cq, Cr)
+
+
+def pin_accumulate(lib):
+    """accumulate = 1 equals C_old plus a separate fresh alpha*A*B call:
+    bitwise on integer data, within one rounding otherwise."""
+    p = random_problem(25, 2, 9, 8, 7, dist="int", accumulate=True, alpha=2.0)
+    acc = _out(p, _run(p, lib))
+    fresh_p = random_problem(25, 2, 9, 8, 7, dist="int", accumulate=False, alpha=2.0)
+    fresh = _out(fresh_p, _run(fresh_p, lib))
+    cold = view(p.C.storage, 2, 9, 8, p.C.strides)
+    assert np.array_equal(acc, cold + fresh)
+    p = random_problem(26, 2, 9, 8, 300, dist="normal", accumulate=True, alpha=0.3)
+    acc = _out(p, _run(p, lib)).astype(np.float64)
+    fresh_p = random_problem(26, 2, 9, 8, 300, dist="normal", accumulate=False, alpha=0.3)
+    fresh = _out(fresh_p, _run(fresh_p, lib)).astype(np.float64)
+    cold = view(p.C.storage, 2, 9, 8, p.C.strides).astype(np.float64)
+    both = cold + fresh
+    assert np.all(np.abs(acc - both) <= np.spacing(np.abs(acc).astype(np.float32)) + 1e-7 * np.abs(fresh))
+
+
+def pin_order_and_entries(lib):
+    """Visiting the elements in reverse order changes no bit (kael ch. 09,
+    "The host emulation" runs work items backwards for the same reason), and
+    the one-by-one entry routine returns exactly the full product's values."""
+    p = random_problem(27, 3, 21, 19, 33, a_major="col", b_major="col", dist="normal",
+                       accumulate=True, alpha=0.5, pad=1)
+    C1 = _run(p, lib)
+    C2 = _run(p, lib, reverse=True)
+    assert np.array_equal(C1, C2)
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.integers(0, 3, 50), rng.integers(0, 21, 50), rng.integers(0, 19, 50)], 1)
+    vals = oracle.ref_entries(*p.call_args(p.A.storage, p.B.storage, p.C.storage), idx=idx, lib=lib)
+    full = _out(p, C1)
+    assert np.array_equal(vals, full[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
+def pin_nan_and_canaries(lib):
+    """A NaN in A[0, 2, 1] makes row 2 of batch 0 NaN and nothing else;
+    gaps between C's rows keep their sentinel; with accumulate = 0 a
+    NaN-filled C is never read."""
+    p = random_problem(28, 2, 5, 6, 4, pad=3, dist="normal")
+    sa, sc = p.A.strides, p.C.strides
+    A = p.A.storage.copy()
+    A[0 * sa[0] + 2 * sa[1] + 1 * sa[2]] = np.nan
+    C = np.full_like(p.C.storage, np.nan)
+    oracle.ref_sgemm(2, 5, 6, 4, 1.0, A, *sa, p.B.storage, *p.B.strides, 0, C, *sc, lib=lib)
+    out = view(C, 2, 5, 6, sc)
+    nan_mask = np.zeros((2, 5, 6), bool)
+    nan_mask[0, 2, :] = True
+    assert np.array_equal(np.isnan(out), nan_mask)
+    covered = np.zeros(C.size, bool)
+    for b in range(2):
+        for i in range(5):
+            covered[b * sc[0] + i * sc[1]: b * sc[0] + i * sc[1] + 6] = True
+    assert np.all(np.isnan(C[~covered]))
+
+
+PINS = [pin_all_ones, pin_identity, pin_k_zero, pin_golden_transpose_trace,
+        pin_golden_column_major, pin_blas_linear_mapping, pin_blas_rowmajor_trick,
+        pin_exact_bruteforce, pin_numpy_float64, pin_stride_swap, pin_transpose_identity,
+        pin_batch_slices, pin_accumulate, pin_order_and_entries, pin_nan_and_canaries]

@@ -1,0 +1,96 @@
+"""Mutation check of the oracle's pins, on the CPU.
+
+Each case plants one plausible mistake in a private copy of the oracle's C
+source (a dropped term, a wrong sign, a transposed operand, a lost stride,
+alpha in the wrong place, single-precision accumulation, ...), builds it, and
+requires that at least one pin rejects it.  The unmodified source must pass
+every pin.  Nothing here touches the product library.
+"""
+import functools
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ref_sgemm.c")
+
+MUTANTS = {
+    "drop_last_term": [("for (int64_t p = 0; p < k; ++p)", "for (int64_t p = 0; p < k - 1; ++p)")],
+    "drop_first_term": [("for (int64_t p = 0; p < k; ++p)", "for (int64_t p = 1; p < k; ++p)")],
+    "wrong_sign": [("sum += a * bv;", "sum -= a * bv;")],
+    "transposed_A": [("elem_offset(b, i, p, sA_batch, sA_row, sA_col)",
+                      "elem_offset(b, p, i, sA_batch, sA_row, sA_col)")],
+    "transposed_B": [("elem_offset(b, p, j, sB_batch, sB_row, sB_col)",
+                      "elem_offset(b, j, p, sB_batch, sB_row, sB_col)")],
+    "strides_exchanged": [("return b * s_batch + r * s_row + c * s_col;",
+                           "return b * s_batch + r * s_col + c * s_row;")],
+    "alpha_dropped": [("double out = (double)alpha * sum;", "double out = sum;")],
+    "alpha_on_c_old": [("out += (double)c_old;", "out += (double)alpha * c_old;")],
+    "accumulate_inverted": [("if (accumulate)\n        out +=", "if (!accumulate)\n        out +=")],
+    "always_accumulate": [("float c_old = accumulate ? *c : 0.0f;", "float c_old = *c;"),
+                          ("if (accumulate)\n        out +=", "if (1)\n        out +=")],
+    "fp32_accumulation": [("double sum = 0.0;", "float sum = 0.0f;")],
+    "batch_row_swapped": [("int64_t b = row / m, i = row % m;", "int64_t b = row % m, i = row / m;")],
+    "B_batch_ignored": [("elem_offset(b, p, j, sB_batch", "elem_offset(0, p, j, sB_batch")],
+    "last_column_skipped": [("for (int64_t jj = 0; jj < n; ++jj)", "for (int64_t jj = 0; jj < n - 1; ++jj)")],
+    "alpha_rounded_to_int": [("double out = (double)alpha * sum;", "double out = (double)(int)alpha * sum;")],
+}
+
+# The brute-force pin at full size is slow; mutants see a smaller sweep.
+BATTERY = [p if p is not pins.pin_exact_bruteforce
+           else functools.partial(pins.pin_exact_bruteforce, sizes=range(1, 5))
+           for p in pins.PINS]
+
+
+def _build(tmp_path, edits):
+    src = open(SRC).read()
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+        src = src.replace(old, new)
+    path = tmp_path / "mutant.c"
+    path.write_text(src)
+    return oracle.build(str(path), str(tmp_path / "libmutant.so"))
+
+
+def _first_failing_pin(lib):
+    for pin in BATTERY:
+        try:
+            pin(lib)
+        except AssertionError:
+            return getattr(pin, "__name__", getattr(pin, "func", pin).__name__)
+    return None
+
+
+def _child(lib_path):
+    """Runs in a fresh interpreter: the battery against one build."""
+    return _first_failing_pin(oracle.load_library(lib_path))
+
+
+def _verdict(tmp_path, edits):
+    """Name of the first pin that rejects the build, "crash:<rc>" if the
+    mutant brings its process down (an index mutation can read outside its
+    buffer), or None if every pin passes."""
+    lib_path = _build(tmp_path, edits)
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    code = ("import sys; sys.path[:0] = [%r, %r]; import test_oracle_mutants as t; "
+            "print('VERDICT', t._child(%r))" % (here, root, lib_path))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return f"crash:{r.returncode}"
+    line = [l for l in r.stdout.splitlines() if l.startswith("VERDICT ")][-1]
+    v = line.split(" ", 1)[1]
+    return None if v == "None" else v
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    assert _verdict(tmp_path, MUTANTS[name]) is not None, f"no pin rejects mutant {name}"
+
+
+def test_pristine_copy_passes(tmp_path):
+    assert _verdict(tmp_path, []) is None
