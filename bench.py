@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Throughput of the strided, batched fp32 product on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of sgemm_strided_batched (validation, planning and the
+kernel launch) over the workload's inputs, which are resident in device
+memory before timing starts.  W untimed steps, then exactly K timed steps
+bracketed by device synchronisation; rank 0 prints one JSON line.
+
+Default workload: the large square product, 4 x 4096^3 with A read
+transposed, alpha 0.5 and accumulation into C.  `--workload all` prints one
+line per workload instead (for tables; not the headline).
+
+The JSON line carries:
+  value      whole-job TFLOP/s (2*m*n*k*batch per step, K steps / wall time)
+  roofline   the dominant (only) kernel: algorithmic FLOPs per launch divided
+             by its mean launch duration from HIP events recorded on the
+             launch stream, against the MI355X dense fp32 matrix peak
+             (157.3 TFLOP/s); `traffic` is the HBM bytes per launch measured
+             by rocprofv3 counters, when a committed record for the current
+             kernel sources exists, else null
+  cpu_baseline  the CPU oracle timed on a bounded slice of the same workload
+             (a block of rows of batch 0), as TFLOP/s, with its thread count.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
+DEFAULT_WORKLOAD = "square4096_acc"
+KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/kernels.hip", "strided_fp32_gemm_amd/csrc/plan.hpp",
+                  "strided_fp32_gemm_amd/csrc/plan.cpp"]
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_record(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary of this
+    kernel and workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, _, val = line.partition(":")
+                rec[key.strip("-* `").strip()] = val.strip().strip("`")
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p, seconds: float) -> dict:
+    """The oracle on rows 0..R-1 of batch 0 of the same product, R chosen so
+    the run takes roughly `seconds`."""
+    import oracle
+    threads = oracle.num_threads()
+    C = p.C.storage.copy()
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.ref_sgemm(1, rows, p.n, p.k, p.alpha,
+                         p.A.storage, 0, p.A.s_row, p.A.s_col,
+                         p.B.storage, 0, p.B.s_row, p.B.s_col,
+                         int(p.accumulate), C, 0, p.C.s_row, p.C.s_col)
+        return time.perf_counter() - t0
+
+    rows = min(p.m, threads)
+    t = run(rows)
+    while t < 0.5 and rows < p.m:
+        rows = min(p.m, rows * 4)
+        t = run(rows)
+    if t < seconds and rows < p.m:
+        rows = min(p.m, max(rows, int(rows * seconds / max(t, 1e-6)) // threads * threads))
+        t = run(rows)
+    flops = 2.0 * rows * p.n * p.k
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of batch 0 ({rows}x{p.n}x{p.k}, "
+                      f"{flops / 1e9:.1f} GFLOP in {t:.1f} s)"}
+
+
+def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
+    import torch
+    import strided_fp32_gemm_amd as sg
+    from strided_fp32_gemm_amd import workloads as wl
+
+    p = wl.workload(name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dA = torch.from_numpy(p.A.storage).to(dev)
+    dB = torch.from_numpy(p.B.storage).to(dev)
+    dC = torch.from_numpy(p.C.storage).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    args = p.call_args(dA, dB, dC)
+    info = sg.sgemm_plan_describe(*p.call_args(dA.data_ptr(), dB.data_ptr(), dC.data_ptr()),
+                                  num_cus=0)
+    for _ in range(warmup):
+        sg.sgemm_strided_batched(*args, stream=stream)
+    torch.cuda.synchronize(dev)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        sg.sgemm_strided_batched(*args, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+    flops = float(p.flops)
+    value = flops * steps / wall / 1e12
+    mean_ms = statistics.fmean(launch_ms)
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    traffic = traffic_record(name, info["kernel"])
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "batch": p.batch, "m": p.m, "n": p.n, "k": p.k,
+            "alpha": p.alpha, "accumulate": bool(p.accumulate),
+            "strides": {"A": list(p.A.strides), "B": list(p.B.strides), "C": list(p.C.strides)},
+            "kernel": info["kernel"],
+            "workgroups": info["workgroups"],
+        },
+        "frac_of_peak": round(value / PEAK_FP32_MATRIX_TFLOPS, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_FP32_MATRIX_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": info["kernel"],
+            "launch_ms_mean": round(mean_ms, 5),
+            "launch_ms_median": round(statistics.median(launch_ms), 5),
+            "launch_ms_min": round(min(launch_ms), 5),
+        },
+    }
+    if cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(p, cpu_seconds)
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    return line
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target duration of the CPU oracle baseline (0 skips it)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    from strided_fp32_gemm_amd import workloads as wl
+    names = list(wl.WORKLOADS) if args.workload == "all" else [args.workload]
+    for name in names:
+        line = bench_one(name, args.steps, args.warmup, args.cpu_seconds)
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

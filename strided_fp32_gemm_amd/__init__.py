@@ -1,0 +1,79 @@
+"""Strided, batched fp32 matrix product for AMD Instinct MI355X (gfx950).
+
+    C <- alpha * A @ B   (+ C when accumulate)
+
+over a batch, with every operand given by a pointer and (batch, row, col)
+element strides; a transposed operand is the same memory with its row and
+column strides exchanged (StaleyNET "GPU Implementation", section "The
+matrix product").  The computation runs in hand-written HIP kernels behind a
+C ABI (include/sgemm_strided.h); this package only marshals arguments.
+PyTorch is used for device memory and streams.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    PATH_AUTO,
+    PATH_GENERIC,
+    PATH_MFMA,
+    PATH_NAMES,
+    PATH_WAVE,
+    SgemmError,
+    load,
+    sgemm_last_error,
+    sgemm_plan_describe,
+    sgemm_status_string,
+    sgemm_strided_batched,
+    sgemm_strided_batched_path,
+)
+
+
+def _strides3(t, name):
+    if t.dim() == 2:
+        return 1, (0, t.stride(0), t.stride(1)), tuple(t.shape)
+    if t.dim() == 3:
+        return t.shape[0], tuple(t.stride()), tuple(t.shape[1:])
+    raise ValueError(f"{name} must be 2-D or 3-D, got {t.dim()}-D")
+
+
+def sgemm(A, B, C, alpha: float = 1.0, accumulate: bool = False, path: int = PATH_AUTO,
+          stream=None):
+    """C <- alpha*A@B (+C) for torch float32 views on one GPU.
+
+    A is [batch,] m x k, B is [batch,] k x n, C is [batch,] m x n; any of them
+    may be a strided or transposed view (``W.t()`` passes W with exchanged
+    strides, no copy).  A 2-D operand next to 3-D ones is broadcast over the
+    batch (batch stride 0).  Runs on ``stream`` (default: torch's current
+    stream) and returns C.
+    """
+    import torch
+
+    for t, nm in ((A, "A"), (B, "B"), (C, "C")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{nm} must be a torch.Tensor")
+        if t.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{nm} must be on the GPU")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on the same device")
+    ba, sa, (m, k) = _strides3(A, "A")
+    bb, sb, (k2, n) = _strides3(B, "B")
+    bc, sc, (m2, n2) = _strides3(C, "C")
+    if k != k2 or m != m2 or n != n2:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    batch = max(ba, bb, bc)
+    for b_, nm in ((ba, "A"), (bb, "B")):
+        if b_ not in (1, batch):
+            raise ValueError(f"{nm} batch {b_} does not match {batch}")
+    if bc != batch:
+        raise ValueError(f"C batch {bc} does not match {batch}")
+    if ba == 1 and batch > 1:
+        sa = (0, sa[1], sa[2])
+    if bb == 1 and batch > 1:
+        sb = (0, sb[1], sb[2])
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    with torch.cuda.device(C.device):
+        sgemm_strided_batched_path(batch, m, n, k, alpha, A, *sa, B, *sb, accumulate, C, *sc,
+                                   path=path, stream=stream)
+    return C

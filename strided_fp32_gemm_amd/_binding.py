@@ -1,0 +1,180 @@
+"""ctypes binding of libsgemm_strided.so (the C ABI in include/sgemm_strided.h).
+
+Argument marshalling only: every step of the product runs in the HIP
+library.  If the library has not been built, every call raises; there is no
+other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsgemm_strided.so")
+
+PATH_AUTO, PATH_MFMA, PATH_WAVE, PATH_GENERIC = 0, 1, 2, 3
+PATH_NAMES = {PATH_AUTO: "auto", PATH_MFMA: "mfma", PATH_WAVE: "wave", PATH_GENERIC: "generic"}
+
+STATUS = {
+    0: "SGEMM_OK",
+    -1: "SGEMM_ERR_INVALID_SIZE",
+    -2: "SGEMM_ERR_INVALID_STRIDE",
+    -3: "SGEMM_ERR_NULL_POINTER",
+    -4: "SGEMM_ERR_C_ALIAS",
+    -5: "SGEMM_ERR_UNSUPPORTED",
+    -6: "SGEMM_ERR_HIP",
+    -7: "SGEMM_ERR_INVALID_PATH",
+}
+
+# Every symbol include/sgemm_strided.h declares.
+EXPORTS = ("sgemm_strided_batched", "sgemm_strided_batched_path", "sgemm_plan_describe",
+           "sgemm_status_string", "sgemm_last_error")
+
+
+class SgemmError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int),
+        ("transposed", ctypes.c_int),
+        ("tile_m", ctypes.c_int),
+        ("tile_n", ctypes.c_int),
+        ("tile_k", ctypes.c_int),
+        ("waves", ctypes.c_int),
+        ("vec_a", ctypes.c_int),
+        ("vec_b", ctypes.c_int),
+        ("a_kfast", ctypes.c_int),
+        ("b_kfast", ctypes.c_int),
+        ("launches", ctypes.c_int),
+        ("workgroups", ctypes.c_int64),
+        ("kernel", ctypes.c_char * 64),
+    ]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["kernel"] = self.kernel.decode()
+        d["path_name"] = PATH_NAMES.get(self.path, str(self.path))
+        return d
+
+
+_i64, _f32, _int, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_void_p
+_GEMM_ARGS = [_i64, _i64, _i64, _i64, _f32,
+              _vp, _i64, _i64, _i64,
+              _vp, _i64, _i64, _i64,
+              _int,
+              _vp, _i64, _i64, _i64]
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load (once) and return the library; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library not built: {path} is missing. Build it with "
+            "`python -m strided_fp32_gemm_amd.build` (or __graft_entry__.build()).")
+    lib = ctypes.CDLL(path)
+    lib.sgemm_strided_batched.restype = _int
+    lib.sgemm_strided_batched.argtypes = _GEMM_ARGS + [_vp]
+    lib.sgemm_strided_batched_path.restype = _int
+    lib.sgemm_strided_batched_path.argtypes = _GEMM_ARGS + [_int, _vp]
+    lib.sgemm_plan_describe.restype = _int
+    lib.sgemm_plan_describe.argtypes = _GEMM_ARGS + [_int, _int, ctypes.POINTER(PlanInfo)]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_status_string.argtypes = [_int]
+    lib.sgemm_last_error.restype = ctypes.c_char_p
+    lib.sgemm_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> int:
+    """Device address of a pointer-like argument: an int, None, or anything
+    with data_ptr() (a torch tensor)."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    raise TypeError(f"expected a device pointer or tensor, got {type(x).__name__}")
+
+
+def _stream(s) -> int:
+    if s is None:
+        return 0
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream)
+    raise TypeError(f"expected a stream handle, got {type(s).__name__}")
+
+
+def _check(status: int):
+    if status != 0:
+        raise SgemmError(status, load().sgemm_last_error().decode())
+
+
+def _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row,
+               sB_col, accumulate, C, sC_batch, sC_row, sC_col):
+    return [int(batch), int(m), int(n), int(k), float(alpha),
+            _ptr(A), int(sA_batch), int(sA_row), int(sA_col),
+            _ptr(B), int(sB_batch), int(sB_row), int(sB_col),
+            int(bool(accumulate)),
+            _ptr(C), int(sC_batch), int(sC_row), int(sC_col)]
+
+
+def sgemm_strided_batched(batch, m, n, k, alpha,
+                          A, sA_batch, sA_row, sA_col,
+                          B, sB_batch, sB_row, sB_col,
+                          accumulate,
+                          C, sC_batch, sC_row, sC_col,
+                          stream=None) -> None:
+    """C <- alpha*A*B (+C) through the C ABI; strides in elements."""
+    args = _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
+                      sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col)
+    _check(load().sgemm_strided_batched(*args, _stream(stream)))
+
+
+def sgemm_strided_batched_path(batch, m, n, k, alpha,
+                               A, sA_batch, sA_row, sA_col,
+                               B, sB_batch, sB_row, sB_col,
+                               accumulate,
+                               C, sC_batch, sC_row, sC_col,
+                               path, stream=None) -> None:
+    """Same as sgemm_strided_batched with the kernel family forced."""
+    args = _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
+                      sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col)
+    _check(load().sgemm_strided_batched_path(*args, int(path), _stream(stream)))
+
+
+def sgemm_plan_describe(batch, m, n, k, alpha,
+                        A, sA_batch, sA_row, sA_col,
+                        B, sB_batch, sB_row, sB_col,
+                        accumulate,
+                        C, sC_batch, sC_row, sC_col,
+                        path=PATH_AUTO, num_cus=256) -> dict:
+    """The plan the library would launch (no device access when num_cus > 0)."""
+    info = PlanInfo()
+    args = _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
+                      sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col)
+    _check(load().sgemm_plan_describe(*args, int(path), int(num_cus), ctypes.byref(info)))
+    return info.as_dict()
+
+
+def sgemm_status_string(status: int) -> str:
+    return load().sgemm_status_string(int(status)).decode()
+
+
+def sgemm_last_error() -> str:
+    return load().sgemm_last_error().decode()

@@ -1,0 +1,250 @@
+// plan.cpp -- validation, layout classification and tile choice.
+//
+// Semantics follow StaleyNET "GPU Implementation", section "The matrix
+// product": C <- alpha*A*B (optionally + C) over a batch, every operand
+// described by strides, a transposed operand being the same memory with its
+// row and column strides exchanged.  The safety rule of the same page
+// (section "Safety": check every size a kernel depends on, then launch) is
+// what validate() and the buffer-range checks below implement.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+
+namespace sgemm {
+
+namespace {
+
+bool mul64(int64_t x, int64_t y, int64_t &r) { return !__builtin_mul_overflow(x, y, &r); }
+bool add64(int64_t x, int64_t y, int64_t &r) { return !__builtin_add_overflow(x, y, &r); }
+
+// Largest element offset of a [e0, e1, e2] view with strides s*, or -1 on
+// overflow.  Extents are >= 1 here.
+int64_t last_offset(int64_t e0, int64_t s0, int64_t e1, int64_t s1, int64_t e2, int64_t s2) {
+    int64_t a, b, c, t, r;
+    if (!mul64(e0 - 1, s0, a) || !mul64(e1 - 1, s1, b) || !mul64(e2 - 1, s2, c)) return -1;
+    if (!add64(a, b, t) || !add64(t, c, r)) return -1;
+    return r;
+}
+
+bool ranges_overlap(uintptr_t p, int64_t last_p, uintptr_t q, int64_t last_q) {
+    uintptr_t p_end = p + 4u * (uintptr_t)(last_p + 1);
+    uintptr_t q_end = q + 4u * (uintptr_t)(last_q + 1);
+    return p < q_end && q < p_end;
+}
+
+
+// Width (in floats) of the global loads along an operand's fast axis.
+int vector_width(uintptr_t base, int64_t fast_stride, int64_t fast_extent,
+                 int64_t slow_stride, int64_t batch_stride, int64_t batch) {
+    if (fast_stride != 1) return 1;
+    for (int v : {4, 2}) {
+        if (fast_extent % v) continue;
+        if (base % (uintptr_t)(4 * v)) continue;
+        if (slow_stride % v) continue;
+        if (batch > 1 && batch_stride % v) continue;
+        return v;
+    }
+    return 1;
+}
+
+// Which axis of a rows x cols operand is contiguous: returns true if the
+// column axis (cols) is the fast one.
+bool cols_fast(int64_t rows, int64_t s_row, int64_t cols, int64_t s_col) {
+    bool c1 = (s_col == 1), r1 = (s_row == 1);
+    if (c1 && r1) return cols >= rows;
+    if (c1) return true;
+    if (r1) return false;
+    if (cols == 1) return false;
+    if (rows == 1) return true;
+    return s_col <= s_row;
+}
+
+// Bytes a workgroup may address from its base, for the 32-bit buffer range.
+constexpr int64_t kBufferLimit = (int64_t(1) << 31) - 64;
+
+bool fits_buffer(int64_t span_rows, int64_t s_rows, int64_t span_cols, int64_t s_cols) {
+    int64_t off = last_offset(1, 0, std::max<int64_t>(span_rows, 1), s_rows,
+                              std::max<int64_t>(span_cols, 1), s_cols);
+    if (off < 0) return false;
+    int64_t bytes;
+    if (!mul64(off + 4, 4, bytes)) return false;
+    return bytes < kBufferLimit;
+}
+
+}  // namespace
+
+int validate(const GemmArgs &a, std::string &why) {
+    if (a.batch < 0 || a.m < 0 || a.n < 0 || a.k < 0) {
+        why = "negative size (batch, m, n, k must be >= 0)";
+        return kErrSize;
+    }
+    const int64_t strides[9] = {a.sA_batch, a.sA_row, a.sA_col, a.sB_batch, a.sB_row,
+                                a.sB_col, a.sC_batch, a.sC_row, a.sC_col};
+    static const char *names[9] = {"sA_batch", "sA_row", "sA_col", "sB_batch", "sB_row",
+                                   "sB_col", "sC_batch", "sC_row", "sC_col"};
+    for (int i = 0; i < 9; ++i)
+        if (strides[i] < 0) {
+            why = std::string("negative stride ") + names[i];
+            return kErrStride;
+        }
+    int64_t bm, work;
+    if (!mul64(a.batch, a.m, bm) || !mul64(bm, a.n, work)) {
+        why = "batch*m*n overflows int64";
+        return kErrUnsupported;
+    }
+    if (work == 0) return kOk;
+    if (!a.C) {
+        why = "C is NULL";
+        return kErrNull;
+    }
+    if (a.k > 0 && (!a.A || !a.B)) {
+        why = a.A ? "B is NULL" : "A is NULL";
+        return kErrNull;
+    }
+    int64_t lastC = last_offset(a.batch, a.sC_batch, a.m, a.sC_row, a.n, a.sC_col);
+    int64_t lastA = 0, lastB = 0;
+    if (a.k > 0) {
+        lastA = last_offset(a.batch, a.sA_batch, a.m, a.sA_row, a.k, a.sA_col);
+        lastB = last_offset(a.batch, a.sB_batch, a.k, a.sB_row, a.n, a.sB_col);
+    }
+    int64_t bytes;
+    if (lastC < 0 || lastA < 0 || lastB < 0 || !mul64(std::max({lastA, lastB, lastC}) + 1, 4, bytes)) {
+        why = "an operand's extent times its strides overflows int64";
+        return kErrUnsupported;
+    }
+    // C must address every output at its own element: sorted by stride, each
+    // axis of extent > 1 has to step past everything the smaller axes reach.
+    struct Axis { int64_t extent, stride; } ax[3] = {
+        {a.batch, a.sC_batch}, {a.m, a.sC_row}, {a.n, a.sC_col}};
+    std::sort(ax, ax + 3, [](const Axis &x, const Axis &y) { return x.stride < y.stride; });
+    int64_t reach = 0;
+    for (const Axis &x : ax) {
+        if (x.extent <= 1) continue;
+        if (x.stride <= reach) {
+            why = "C's strides map two outputs to the same element";
+            return kErrAlias;
+        }
+        reach += (x.extent - 1) * x.stride;
+    }
+    if (a.k > 0 && (ranges_overlap(a.C, lastC, a.A, lastA) || ranges_overlap(a.C, lastC, a.B, lastB))) {
+        why = "C's address range overlaps A or B";
+        return kErrAlias;
+    }
+    return kOk;
+}
+
+namespace {
+
+// Relative per-CU throughput of a tile when the matrix cores are fed by it
+// (larger tiles reuse each loaded value for more products).
+double tile_rate(const TileCfg &t) {
+    int area = t.bm * t.bn;
+    if (area >= 128 * 128) return 1.0;
+    if (area >= 128 * 64) return 0.85;
+    if (area >= 64 * 64) return 0.6;
+    return 0.3;
+}
+
+bool tile_fits(const Plan &p, const TileCfg &t) {
+    // Buffer offsets are 32-bit from a per-workgroup base: the workgroup's
+    // slice of each operand has to lie within 2 GiB of that base.
+    int64_t kspan = p.k;
+    return fits_buffer(t.bm, p.sA_m, kspan, p.sA_k) && fits_buffer(kspan, p.sB_k, t.bn, p.sB_n) &&
+           fits_buffer(t.bm, p.sC_m, t.bn, p.sC_n);
+}
+
+double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
+    int64_t tm = (p.m + t.bm - 1) / t.bm, tn = (p.n + t.bn - 1) / t.bn;
+    double tiles = double(p.batch) * double(tm) * double(tn);
+    double ksteps = std::max<double>(1.0, double((p.k + t.bk - 1) / t.bk));
+    double per_tile = double(t.bm) * t.bn * (ksteps * t.bk + 16.0 * (p.accumulate ? 2 : 1));
+    double rounds = std::ceil(tiles / double(std::max(num_cus, 1)));
+    return rounds * per_tile / tile_rate(t);
+}
+
+}  // namespace
+
+int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::string &why) {
+    int st = validate(a, why);
+    if (st != kOk) return st;
+    p = Plan();
+    p.batch = a.batch; p.m = a.m; p.n = a.n; p.k = a.k;
+    p.alpha = a.alpha; p.accumulate = a.accumulate ? 1 : 0;
+    if (a.batch == 0 || a.m == 0 || a.n == 0) {
+        p.empty = true;
+        p.kernel_name = "none";
+        return kOk;
+    }
+    // Kernel terms: A is m x k with strides (m, k), B is k x n with (k, n).
+    p.A = a.A; p.sA_b = a.sA_batch; p.sA_m = a.sA_row; p.sA_k = a.sA_col;
+    p.B = a.B; p.sB_b = a.sB_batch; p.sB_k = a.sB_row; p.sB_n = a.sB_col;
+    p.C = a.C; p.sC_b = a.sC_batch; p.sC_m = a.sC_row; p.sC_n = a.sC_col;
+    // Outputs are written row segments at a time; a column-major C is served
+    // as C^T = B^T A^T (kael book ch. 09, section "cuBLAS": the same bytes
+    // read in the other order are the transpose), which only exchanges roles
+    // and strides.
+    bool c_nfast = (p.n == 1 || p.sC_n == 1);
+    bool c_mfast = (p.m == 1 || p.sC_m == 1);
+    if (!c_nfast && c_mfast && p.m > 1) {
+        p.transposed = true;
+        std::swap(p.m, p.n);
+        uintptr_t A0 = p.A;
+        int64_t a_b = p.sA_b, a_m = p.sA_m, a_k = p.sA_k;
+        p.A = p.B; p.sA_b = p.sB_b; p.sA_m = p.sB_n; p.sA_k = p.sB_k;
+        p.B = A0; p.sB_b = a_b; p.sB_k = a_k; p.sB_n = a_m;
+        std::swap(p.sC_m, p.sC_n);
+    }
+    // Broadcast strides of extent-1 axes never matter; zero them so that
+    // alignment checks see only strides that are used.
+    if (p.batch == 1) { p.sA_b = 0; p.sB_b = 0; p.sC_b = 0; }
+
+    p.a_kfast = cols_fast(p.m, p.sA_m, p.k, p.sA_k);
+    p.b_kfast = !cols_fast(p.k, p.sB_k, p.n, p.sB_n);
+    p.vec_a = p.a_kfast ? vector_width(p.A, p.sA_k, p.k, p.sA_m, p.sA_b, p.batch)
+                        : vector_width(p.A, p.sA_m, p.m, p.sA_k, p.sA_b, p.batch);
+    p.vec_b = p.b_kfast ? vector_width(p.B, p.sB_k, p.k, p.sB_n, p.sB_b, p.batch)
+                        : vector_width(p.B, p.sB_n, p.n, p.sB_k, p.sB_b, p.batch);
+
+    const int64_t i32max = (int64_t(1) << 31) - 1;
+    bool small_enough = p.m <= i32max && p.n <= i32max && p.k <= i32max && p.batch <= i32max;
+
+    int best = -1;
+    if (small_enough && family != Family::Generic) {
+        double best_cost = 0;
+        for (int t = 0; t < kNumTiles; ++t) {
+            if (family == Family::Mfma && t == kWaveTile) continue;
+            if (family == Family::Wave && t != kWaveTile) continue;
+            if (!tile_fits(p, kTiles[t])) continue;
+            int64_t wgs = p.batch * ((p.m + kTiles[t].bm - 1) / kTiles[t].bm) *
+                          ((p.n + kTiles[t].bn - 1) / kTiles[t].bn);
+            if (wgs > i32max) continue;
+            double c = tile_cost(p, kTiles[t], num_cus);
+            if (best < 0 || c < best_cost) { best = t; best_cost = c; }
+        }
+    }
+    if (best >= 0) {
+        const TileCfg &t = kTiles[best];
+        p.family = (best == kWaveTile) ? Family::Wave : Family::Mfma;
+        p.tile = best;
+        p.tiles_m = (p.m + t.bm - 1) / t.bm;
+        p.tiles_n = (p.n + t.bn - 1) / t.bn;
+        p.workgroups = p.batch * p.tiles_m * p.tiles_n;
+        p.kernel_name = std::string(p.family == Family::Wave ? "wave_" : "mfma_") + t.name +
+                        (p.a_kfast ? "_ak" : "_am") + (p.b_kfast ? "_bk" : "_bn") +
+                        (p.accumulate ? "_acc" : "");
+    } else {
+        p.family = Family::Generic;
+        p.tile = -1;
+        p.vec_a = p.vec_b = 1;
+        p.tiles_m = (p.m + 63) / 64;
+        p.tiles_n = (p.n + 63) / 64;
+        int64_t tiles = p.batch * p.tiles_m * p.tiles_n;
+        p.workgroups = std::min<int64_t>(tiles, 65536);
+        p.kernel_name = std::string("generic_t64x64") + (p.accumulate ? "_acc" : "");
+    }
+    return kOk;
+}
+
+}  // namespace sgemm

@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI: symbols, validation and planning.
+
+These run without a GPU: the library is loaded, every symbol the header
+declares must be exported, every invalid-argument path must return its
+status before any HIP call, and sgemm_plan_describe (given a CU count) never
+touches a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import strided_fp32_gemm_amd as sg
+from strided_fp32_gemm_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm_strided.h")
+
+# Fake, suitably aligned device addresses: the planner reads alignment only.
+PA, PB, PC = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sgemm_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sg.load()
+    names = declared_functions()
+    assert names == sorted(sg.EXPORTS)
+    for name in names:
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr), name
+
+
+def test_status_strings():
+    for code, name in sg._binding.STATUS.items():
+        assert sg.sgemm_status_string(code).startswith(name)
+    assert sg.sgemm_status_string(12345) == "unknown sgemm status"
+
+
+def plan(batch, m, n, k, sa, sb, sc, acc=0, path=0, ptrs=(PA, PB, PC), alpha=1.0):
+    return sg.sgemm_plan_describe(batch, m, n, k, alpha, ptrs[0], *sa, ptrs[1], *sb, acc,
+                                  ptrs[2], *sc, path=path, num_cus=256)
+
+
+def status_of(fn):
+    with pytest.raises(sg.SgemmError) as e:
+        fn()
+    return e.value.status
+
+
+def test_validation_errors_never_reach_the_device():
+    rm = lambda r, c: (r * c, c, 1)  # noqa: E731
+    # negative sizes
+    assert status_of(lambda: sg.sgemm_strided_batched(1, -1, 4, 4, 1.0, PA, *rm(4, 4), PB, *rm(4, 4),
+                                                     0, PC, *rm(4, 4))) == -1
+    # negative stride
+    assert status_of(lambda: sg.sgemm_strided_batched(1, 4, 4, 4, 1.0, PA, 16, -4, 1, PB, *rm(4, 4),
+                                                     0, PC, *rm(4, 4))) == -2
+    # null C with work; null A with k > 0
+    assert status_of(lambda: sg.sgemm_strided_batched(1, 4, 4, 4, 1.0, PA, *rm(4, 4), PB, *rm(4, 4),
+                                                     0, 0, *rm(4, 4))) == -3
+    assert status_of(lambda: sg.sgemm_strided_batched(1, 4, 4, 4, 1.0, 0, *rm(4, 4), PB, *rm(4, 4),
+                                                     0, PC, *rm(4, 4))) == -3
+    # C rows overlap each other (row stride smaller than the row length)
+    assert status_of(lambda: sg.sgemm_strided_batched(1, 4, 4, 4, 1.0, PA, *rm(4, 4), PB, *rm(4, 4),
+                                                     0, PC, 16, 3, 1)) == -4
+    # batch stride 0 on C with batch > 1
+    assert status_of(lambda: sg.sgemm_strided_batched(2, 4, 4, 4, 1.0, PA, *rm(4, 4), PB, *rm(4, 4),
+                                                     0, PC, 0, 4, 1)) == -4
+    # C overlaps A
+    assert status_of(lambda: sg.sgemm_strided_batched(1, 4, 4, 4, 1.0, PA, *rm(4, 4), PB, *rm(4, 4),
+                                                     0, PA + 8, *rm(4, 4))) == -4
+    # extent * stride overflows int64
+    assert status_of(lambda: sg.sgemm_strided_batched(1, 4, 4, 4, 1.0, PA, *rm(4, 4), PB, *rm(4, 4),
+                                                     0, PC, 0, 1 << 62, 1)) == -5
+    # unknown path
+    assert status_of(lambda: sg.sgemm_strided_batched_path(1, 4, 4, 4, 1.0, PA, *rm(4, 4), PB,
+                                                          *rm(4, 4), 0, PC, *rm(4, 4), path=9)) == -7
+    assert "negative stride sA_row" in sg.sgemm_last_error() or sg.sgemm_last_error()
+
+
+def test_empty_products_are_accepted_without_a_device():
+    # batch, m or n == 0: OK, nothing enqueued, pointers may be NULL.
+    sg.sgemm_strided_batched(0, 4, 4, 4, 1.0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    sg.sgemm_strided_batched(3, 0, 4, 4, 1.0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    sg.sgemm_strided_batched(3, 4, 0, 4, 1.0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0)
+    p = plan(3, 4, 0, 4, (0, 0, 0), (0, 0, 0), (0, 0, 0), ptrs=(0, 0, 0))
+    assert p["launches"] == 0 and p["workgroups"] == 0
+
+
+def test_k_zero_needs_no_operands():
+    p = plan(2, 5, 7, 0, (0, 0, 0), (0, 0, 0), (35, 7, 1), ptrs=(0, 0, PC))
+    assert p["launches"] == 1
+
+
+def _cfg_plan(name):
+    prob = wl.workload(name) if name != "square4096_acc" else None
+    if prob is None:
+        s2 = 4096 * 4096
+        return plan(4, 4096, 4096, 4096, (s2, 1, 4096), (s2, 4096, 1), (s2, 4096, 1), acc=1, alpha=0.5)
+    return plan(prob.batch, prob.m, prob.n, prob.k, prob.A.strides, prob.B.strides, prob.C.strides,
+                acc=int(prob.accumulate), alpha=prob.alpha)
+
+
+@pytest.mark.parametrize("name,path,a_kfast,b_kfast,vec_b", [
+    ("square64", "wave", 1, 0, 4),
+    ("linear_xWt", "mfma", 1, 1, 4),
+    ("attn_qk", "mfma", 1, 1, 4),
+    ("attn_pv", "mfma", 1, 0, 4),
+    ("spectrogram", "mfma", 1, 0, 2),
+    ("square4096_acc", "mfma", 0, 0, 4),
+])
+def test_workload_plans(name, path, a_kfast, b_kfast, vec_b):
+    """Each workload reaches the matrix-core family with the loader its
+    layout calls for (the four transpose cases map to k-fast or m/n-fast
+    loaders; the spectrogram basis rows of 514 floats allow 8-byte loads)."""
+    p = _cfg_plan(name)
+    assert p["path_name"] == path, p
+    assert (p["a_kfast"], p["b_kfast"], p["vec_b"]) == (a_kfast, b_kfast, vec_b), p
+    assert p["vec_a"] == 4
+    assert p["transposed"] == 0
+
+
+def test_column_major_output_is_solved_transposed():
+    # C stored column-major (row stride 1): computed as C^T = B^T A^T.
+    p = plan(1, 3000, 2000, 640, (0, 640, 1), (0, 2000, 1), (0, 1, 3000))
+    assert p["transposed"] == 1 and p["path_name"] == "mfma"
+
+
+def test_offsets_beyond_32_bits_use_the_generic_path():
+    huge = 1 << 25  # row stride of 2^25 floats: even 32 rows span > 2^31 bytes
+    p = plan(1, 256, 256, 64, (0, huge, 1), (0, 256, 1), (0, 256, 1))
+    assert p["path_name"] == "generic"
+    forced = plan(1, 256, 256, 64, (0, huge, 1), (0, 256, 1), (0, 256, 1), path=sg.PATH_MFMA)
+    assert forced["path_name"] == "generic"
+
+
+def test_forced_families():
+    args = (1, 100, 90, 70, (0, 70, 1), (0, 90, 1), (0, 90, 1))
+    assert plan(*args, path=sg.PATH_WAVE)["path_name"] == "wave"
+    assert plan(*args, path=sg.PATH_MFMA)["path_name"] == "mfma"
+    assert plan(*args, path=sg.PATH_GENERIC)["path_name"] == "generic"
+
+
+def test_vector_width_follows_alignment():
+    # Misaligned base pointer (4 bytes past 16-byte alignment) forces scalar loads.
+    p = plan(1, 128, 128, 128, (0, 128, 1), (0, 128, 1), (0, 128, 1), ptrs=(PA + 4, PB, PC))
+    assert p["vec_a"] == 1 and p["vec_b"] == 4
+    # Fast extent not a multiple of 4 but of 2: 8-byte loads.
+    p = plan(1, 128, 130, 128, (0, 128, 1), (0, 130, 1), (0, 130, 1))
+    assert p["vec_b"] == 2
+    # Neither stride 1: element loads along the smaller stride.
+    p = plan(1, 64, 64, 64, (0, 128, 2), (0, 64, 1), (0, 64, 1))
+    assert p["vec_a"] == 1
+
+
+def test_tile_map_example_shape_is_planned():
+    """kael ch. 09 "Matmul" worked example: rows 5, inner 3, columns 9 is a
+    single clipped tile for every family here."""
+    from helpers import load_golden
+    g = load_golden("kael_tile_map.txt")
+    rows, inner, cols = int(g["rows"]), int(g["inner"]), int(g["columns"])
+    for path in (sg.PATH_WAVE, sg.PATH_MFMA, sg.PATH_GENERIC):
+        p = plan(1, rows, cols, inner, (0, inner, 1), (0, cols, 1), (0, cols, 1), path=path)
+        assert p["workgroups"] == 1
+    # The pages' own 4 x 4 decomposition of that shape: 2 x 3 tiles.
+    assert (-(-rows // 4), -(-cols // 4)) == (int(g["tile_rows"]), int(g["tile_columns"]))

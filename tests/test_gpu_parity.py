@@ -1,0 +1,318 @@
+"""GPU parity: the HIP library against the CPU oracle on the same host bytes.
+
+Every case goes through the C ABI (via the ctypes binding) and is compared
+element by element with the oracle:
+  * bitwise where the result is unique -- all-ones operands (C = k*alpha),
+    and integer operands whose partial sums are all exact (brute force over
+    every m, n, k in 1..8);
+  * otherwise within the acceptance bound
+        max |C_gpu - C_ref| / (k * max|A| * max|B|) <= 1e-6
+    (maxima over all logical elements of the call).
+Each kernel family (matrix-core tiles, one-wavefront tiles, generic) is
+forced in turn, and the five full-size workloads run in the configuration the
+benchmark times, checked on sampled outputs plus properties that hold at any
+size (determinism, untouched gaps, no read of C without accumulation).
+
+A missing GPU is a failure here, not a skip.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import strided_fp32_gemm_amd as sg
+from strided_fp32_gemm_amd import workloads as wl
+from helpers import view
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-6
+LAYOUTS = [(a, b) for a in ("row", "col") for b in ("row", "col")]
+FAMILIES = [sg.PATH_AUTO, sg.PATH_MFMA, sg.PATH_WAVE, sg.PATH_GENERIC]
+FAM_IDS = ["auto", "mfma", "wave", "generic"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "no GPU visible: GPU parity cannot pass without one"
+    sg.load()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+def gpu_call(p, path=sg.PATH_AUTO, C0=None, stream=None):
+    """Run problem p through the C ABI; returns the whole C storage."""
+    dA, dB = dev(p.A.storage), dev(p.B.storage)
+    dC = dev(p.C.storage if C0 is None else C0)
+    s = stream or torch.cuda.current_stream()
+    sg.sgemm_strided_batched_path(*p.call_args(dA, dB, dC), path=path, stream=s)
+    torch.cuda.synchronize()
+    return dC.cpu().numpy()
+
+
+def oracle_call(p, C0=None):
+    C = (p.C.storage if C0 is None else C0).copy()
+    oracle.ref_sgemm(*p.call_args(p.A.storage, p.B.storage, C))
+    return C
+
+
+def out(p, C):
+    return np.array(view(C, p.batch, p.m, p.n, p.C.strides))
+
+
+def err_ratio(p, got, ref):
+    """max |got - ref| / (k * max|A| * max|B|) over the logical outputs."""
+    if p.k == 0 or p.batch * p.m * p.n == 0:
+        return 0.0 if np.array_equal(got, ref) else np.inf
+    amax = np.abs(view(p.A.storage, p.batch, p.m, p.k, p.A.strides)).max()
+    bmax = np.abs(view(p.B.storage, p.batch, p.k, p.n, p.B.strides)).max()
+    denom = p.k * float(amax) * float(bmax)
+    diff = np.abs(got.astype(np.float64) - ref.astype(np.float64)).max()
+    if denom == 0.0:
+        return 0.0 if diff == 0.0 else np.inf
+    return diff / denom
+
+
+# --------------------------------------------------------------- bitwise pins
+
+@pytest.mark.parametrize("path", FAMILIES, ids=FAM_IDS)
+def test_all_ones_bitwise(path):
+    """A = B = 1 gives k*alpha (+ C_old) exactly, in every transpose case."""
+    for a_major, b_major in LAYOUTS:
+        for k in (1, 7, 64, 960, 4096):
+            for alpha in (1.0, 0.5):
+                for acc in (False, True):
+                    p = wl.random_problem(k, 2, 37, 45, k, a_major=a_major, b_major=b_major,
+                                          alpha=alpha, accumulate=acc, dist="ones")
+                    got, ref = out(p, gpu_call(p, path)), out(p, oracle_call(p))
+                    assert np.array_equal(got, ref), (a_major, b_major, k, alpha, acc)
+
+
+def _packed_cases(a_major, b_major, batch, variant, sizes):
+    """All (m, n, k) in sizes^3 packed into shared storages at 16-byte
+    aligned offsets; integer data in [-3, 3]."""
+    rng = np.random.default_rng([int(a_major == "row"), int(b_major == "row"), batch, variant])
+    cases, offs = [], [0, 0, 0]
+    for m in sizes:
+        for n in sizes:
+            for k in sizes:
+                acc = (m + n + k + batch + variant) % 2 == 0
+                alpha = 0.5 if (m * n * k + variant) % 2 else 1.0
+                per_a, sa = wl.layout_strides(m, k, a_major)
+                per_b, sb = wl.layout_strides(k, n, b_major)
+                per_c, sc = wl.layout_strides(m, n, "row")
+                cases.append((m, n, k, acc, alpha, sa, sb, sc, tuple(offs)))
+                for i, per in enumerate((per_a, per_b, per_c)):
+                    offs[i] += -(-per * batch // 4) * 4
+    A = rng.integers(-3, 4, offs[0]).astype(np.float32)
+    B = rng.integers(-3, 4, offs[1]).astype(np.float32)
+    C = rng.integers(-3, 4, offs[2]).astype(np.float32)
+    return cases, A, B, C
+
+
+@pytest.mark.parametrize("path", FAMILIES, ids=FAM_IDS)
+def test_exact_bruteforce_bitwise(path):
+    """Every m, n, k in 1..8, all four transpose cases, batch 1 and 3,
+    accumulate on and off, alpha 1 and 0.5, integer data: the exact result
+    is unique, so the GPU must match the oracle bit for bit."""
+    sizes = range(1, 9)
+    for a_major, b_major in LAYOUTS:
+        for batch in (1, 3):
+            for variant in (0, 1):
+                cases, A, B, C = _packed_cases(a_major, b_major, batch, variant, sizes)
+                dA, dB, dC = dev(A), dev(B), dev(C)
+                ref = C.copy()
+                s = torch.cuda.current_stream()
+                for (m, n, k, acc, alpha, sa, sb, sc, (oa, ob, oc)) in cases:
+                    sg.sgemm_strided_batched_path(
+                        batch, m, n, k, alpha, dA.data_ptr() + 4 * oa, *sa,
+                        dB.data_ptr() + 4 * ob, *sb, acc, dC.data_ptr() + 4 * oc, *sc,
+                        path=path, stream=s)
+                    oracle.ref_sgemm(batch, m, n, k, alpha, A[oa:], *sa, B[ob:], *sb, acc,
+                                     ref[oc:], *sc)
+                torch.cuda.synchronize()
+                got = dC.cpu().numpy()
+                if not np.array_equal(got, ref):
+                    for (m, n, k, acc, alpha, sa, sb, sc, (oa, ob, oc)) in cases:
+                        g = view(got[oc:], batch, m, n, sc)
+                        r = view(ref[oc:], batch, m, n, sc)
+                        assert np.array_equal(g, r), (a_major, b_major, batch, m, n, k, acc, alpha)
+
+
+# ------------------------------------------------------------ tolerance cases
+
+AWKWARD = [(17, 33, 9), (5, 129, 31), (1, 1, 1), (4, 4, 4), (5, 3, 9), (8, 16, 7),
+           (33, 20, 65), (64, 1, 64), (1, 64, 1), (127, 129, 128), (129, 127, 257),
+           (3, 514, 70), (200, 9, 300)]
+
+
+@pytest.mark.parametrize("path", FAMILIES, ids=FAM_IDS)
+def test_awkward_shapes(path):
+    """The pages' awkward sizes (StaleyNET "Testing the kernels": 17 x 33 x 9,
+    5 x 129 x 31; kael ch. 09 "How it is tested": 1x1x1 ... 1x64x1, as rows
+    x inner x columns) plus tile-boundary sizes, every transpose case, with
+    padding between lines and accumulation."""
+    for idx, (m, k, n) in enumerate(AWKWARD):
+        for a_major, b_major in LAYOUTS:
+            p = wl.random_problem(300 + idx, 2, m, n, k, a_major=a_major, b_major=b_major,
+                                  alpha=0.75, accumulate=bool(idx % 2), pad=3)
+            got, ref = out(p, gpu_call(p, path)), out(p, oracle_call(p))
+            e = err_ratio(p, got, ref)
+            assert e <= TOL, (m, n, k, a_major, b_major, e)
+
+
+@pytest.mark.parametrize("mnk", [(128, 128, 32), (129, 127, 33), (255, 257, 96),
+                                 (256, 128, 512), (384, 514, 200), (96, 640, 1000)])
+@pytest.mark.parametrize("path", [sg.PATH_AUTO, sg.PATH_MFMA], ids=["auto", "mfma"])
+def test_tile_boundaries(mnk, path):
+    """Sizes at, just below and just above the matrix-core tile edges, with
+    several tiles and a ragged tail, in all four transpose cases."""
+    m, n, k = mnk
+    for a_major, b_major in LAYOUTS:
+        p = wl.random_problem(m * 7 + n, 3, m, n, k, a_major=a_major, b_major=b_major,
+                              dist="normal", alpha=-0.5, accumulate=True)
+        got, ref = out(p, gpu_call(p, path)), out(p, oracle_call(p))
+        assert err_ratio(p, got, ref) <= TOL, (mnk, a_major, b_major)
+
+
+def test_column_major_output():
+    """C stored column-major is served as C^T = B^T A^T."""
+    for a_major, b_major in LAYOUTS:
+        p = wl.random_problem(41, 2, 150, 90, 77, a_major=a_major, b_major=b_major,
+                              c_major="col", accumulate=True, alpha=1.5)
+        got, ref = out(p, gpu_call(p)), out(p, oracle_call(p))
+        assert err_ratio(p, got, ref) <= TOL, (a_major, b_major)
+
+
+def test_broadcast_batch_stride_zero():
+    p = wl.random_problem(42, 5, 70, 130, 96, b_broadcast=True, dist="normal")
+    got, ref = out(p, gpu_call(p)), out(p, oracle_call(p))
+    assert err_ratio(p, got, ref) <= TOL
+
+
+def test_general_strides_and_misalignment():
+    """Neither stride of A is 1, and B starts one float past 16-byte
+    alignment: the loaders fall back to element and 4-byte loads."""
+    rng = np.random.default_rng(43)
+    m, n, k, batch = 70, 90, 50, 2
+    A = rng.uniform(-1, 1, batch * m * k * 2).astype(np.float32)
+    B = rng.uniform(-1, 1, batch * k * n + 1).astype(np.float32)
+    sa, sb, sc = (m * k * 2, 2 * k, 2), (k * n, n, 1), (m * n, n, 1)
+    dA, dB = dev(A), dev(B)
+    dC = torch.zeros(batch * m * n, device="cuda")
+    info = sg.sgemm_plan_describe(batch, m, n, k, 1.0, dA.data_ptr(), *sa, dB.data_ptr() + 4, *sb,
+                                  0, dC.data_ptr(), *sc)
+    assert info["path_name"] in ("mfma", "wave") and info["vec_a"] == 1 and info["vec_b"] == 1
+    sg.sgemm_strided_batched(batch, m, n, k, 1.0, dA.data_ptr(), *sa, dB.data_ptr() + 4, *sb,
+                             0, dC.data_ptr(), *sc, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = np.zeros(batch * m * n, np.float32)
+    oracle.ref_sgemm(batch, m, n, k, 1.0, A, *sa, B[1:], *sb, 0, ref, *sc)
+    p = wl.Problem("strided", batch, m, n, k, 1.0, False, wl.Operand(A, sa), wl.Operand(B[1:], sb),
+                   wl.Operand(ref, sc))
+    assert err_ratio(p, dC.cpu().numpy(), ref) <= TOL
+
+
+@pytest.mark.parametrize("path", FAMILIES, ids=FAM_IDS)
+def test_k_zero_and_empty(path):
+    for acc in (False, True):
+        p = wl.random_problem(44, 2, 33, 17, 0, accumulate=acc, alpha=3.0)
+        got, ref = out(p, gpu_call(p, path)), out(p, oracle_call(p))
+        assert np.array_equal(got, ref), acc
+    p = wl.random_problem(45, 0, 33, 17, 5)
+    gpu_call(p, path)
+
+
+@pytest.mark.parametrize("path", FAMILIES, ids=FAM_IDS)
+def test_canaries_nan_and_gaps(path):
+    """With accumulate = 0, a NaN-filled C is never read; the gaps between C's
+    rows and matrices keep their NaN sentinel; a NaN in A[0, 2, 1] poisons row
+    2 of batch 0 only."""
+    p = wl.random_problem(46, 2, 45, 70, 40, pad=5, dist="normal")
+    C0 = np.full_like(p.C.storage, np.nan)
+    got = gpu_call(p, path, C0=C0)
+    ref = oracle_call(p, C0=C0)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert not np.isnan(out(p, got)).any()
+    assert err_ratio(p, out(p, got), out(p, ref)) <= TOL
+    A = p.A.storage.copy()
+    sa = p.A.strides
+    A[2 * sa[1] + 1 * sa[2]] = np.nan
+    q = wl.Problem("nan", p.batch, p.m, p.n, p.k, 1.0, False, wl.Operand(A, sa), p.B, p.C)
+    g = out(q, gpu_call(q, path))
+    mask = np.zeros(g.shape, bool)
+    mask[0, 2, :] = True
+    assert np.array_equal(np.isnan(g), mask)
+
+
+def test_determinism_repeated_calls():
+    p = wl.random_problem(47, 4, 300, 260, 500, a_major="col", b_major="col", dist="normal")
+    first = gpu_call(p)
+    for _ in range(3):
+        assert np.array_equal(first, gpu_call(p))
+
+
+def test_torch_wrapper_and_side_stream():
+    """sgemm() on torch views: W.t() passes exchanged strides, a 2-D operand
+    broadcasts over the batch, and work runs on a caller-chosen stream."""
+    g = torch.Generator().manual_seed(48)
+    x = torch.randn(3, 100, 64, generator=g)
+    W = torch.randn(80, 64, generator=g)
+    y = torch.zeros(3, 100, 80)
+    xd, Wd, yd = x.cuda(), W.cuda(), y.cuda()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        sg.sgemm(xd, Wd.t(), yd, alpha=2.0)
+    s.synchronize()
+    ref = np.zeros(3 * 100 * 80, np.float32)
+    oracle.ref_sgemm(3, 100, 80, 64, 2.0, x.numpy().ravel(), 6400, 64, 1,
+                     W.numpy().ravel(), 0, 1, 64, 0, ref, 8000, 80, 1)
+    denom = 64 * float(x.abs().max()) * float(W.abs().max())
+    assert np.abs(yd.cpu().numpy().ravel() - ref).max() / denom <= TOL
+
+
+# --------------------------------------------------- full-size workloads
+
+def _sample_indices(p, rng, count=3000):
+    b = rng.integers(0, p.batch, count)
+    i = rng.integers(0, p.m, count)
+    j = rng.integers(0, p.n, count)
+    edges = []
+    for bb in {0, p.batch - 1}:
+        for ii in {0, p.m - 1}:
+            for jj in {0, p.n - 1, max(p.n - 2, 0)}:
+                edges.append((bb, ii, jj))
+    idx = np.concatenate([np.stack([b, i, j], 1), np.array(edges)], 0)
+    return idx.astype(np.int64)
+
+
+@pytest.mark.parametrize("name", wl.WORKLOADS)
+def test_workload_full_size(name):
+    """Each workload at its full size, in the launch configuration the
+    benchmark times (planner's choice, torch's current stream): sampled
+    outputs (plus every corner and the last two columns) against the oracle
+    one by one, bitwise determinism across two calls, and for the smallest
+    workload the whole output."""
+    p = wl.workload(name)
+    info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
+    assert info["path_name"] in ("mfma", "wave"), info
+    dA, dB = dev(p.A.storage), dev(p.B.storage)
+    dC = dev(p.C.storage)
+    s = torch.cuda.current_stream()
+    sg.sgemm_strided_batched(*p.call_args(dA, dB, dC), stream=s)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    if p.m * p.n * p.k * p.batch <= 1 << 20:
+        ref = oracle_call(p)
+        assert err_ratio(p, out(p, got), out(p, ref)) <= TOL
+    idx = _sample_indices(p, np.random.default_rng(49))
+    refv = oracle.ref_entries(*p.call_args(p.A.storage, p.B.storage, p.C.storage), idx=idx)
+    gv = view(got, p.batch, p.m, p.n, p.C.strides)[idx[:, 0], idx[:, 1], idx[:, 2]]
+    e = err_ratio(p, gv, refv)
+    assert e <= TOL, (name, e)
+    dC2 = dev(p.C.storage)
+    sg.sgemm_strided_batched(*p.call_args(dA, dB, dC2), stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(dC, dC2)
