@@ -40,7 +40,8 @@ if ROOT not in sys.path:
 PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
 DEFAULT_WORKLOAD = "square4096_acc"
-KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/kernels.hip", "strided_fp32_gemm_amd/csrc/plan.hpp",
+KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/mfma_kernel.hpp", "strided_fp32_gemm_amd/csrc/kernels.hip",
+                  "strided_fp32_gemm_amd/csrc/plan.hpp",
                   "strided_fp32_gemm_amd/csrc/plan.cpp"]
 
 
@@ -187,6 +188,9 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the CPU oracle baseline (0 skips it)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the product, run 3 plain device copies of this many MiB "
+                         "(calibrates the HBM byte counters; prints nothing else)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -200,6 +204,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": n * 4, "copies": 3}))
+        return 0
     from strided_fp32_gemm_amd import workloads as wl
     names = list(wl.WORKLOADS) if args.workload == "all" else [args.workload]
     for name in names:

@@ -21,7 +21,7 @@ struct MfmaArgs {
     long long sC_b, sC_m, sC_n;
     int m, n, k;
     int tiles_m, tiles_n;
-    int vec_a, vec_b;
+    int accumulate;
     float alpha;
 };
 
@@ -38,6 +38,25 @@ struct GenericArgs {
     float alpha;
     int accumulate;
 };
+
+// Launchers of the MFMA kernel, indexed [tile][A k-fast][B k-fast]
+// [A 16-byte loads][B 16-byte loads].  Each tile's row is filled by its own
+// translation unit (mfma_t<tile>.hip) so the instantiations compile in
+// parallel.
+using MfmaLaunch = void (*)(const MfmaArgs &, unsigned, hipStream_t);
+struct MfmaTable {
+    MfmaLaunch f[kNumTiles][2][2][2][2];
+};
+void fill_tile_0(MfmaTable &);
+void fill_tile_1(MfmaTable &);
+void fill_tile_2(MfmaTable &);
+void fill_tile_3(MfmaTable &);
+void fill_tile_4(MfmaTable &);
+void fill_tile_5(MfmaTable &);
+void fill_tile_6(MfmaTable &);
+void fill_tile_7(MfmaTable &);
+void fill_tile_8(MfmaTable &);
+void fill_tile_9(MfmaTable &);
 
 // Enqueues the plan on `stream`.  Returns kOk, or kErrHip with `why` set when
 // the runtime rejects the launch.

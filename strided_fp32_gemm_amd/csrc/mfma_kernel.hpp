@@ -1,0 +1,356 @@
+// mfma_kernel.hpp -- the LDS-tiled fp32 matrix-core kernel for gfx950.
+//
+// C[b,i,j] <- alpha * sum_p A[b,i,p] B[b,p,j] (+ C[b,i,j]); operands are
+// addressed through (batch, row, col) element strides (StaleyNET "GPU
+// Implementation", section "The matrix product").
+//
+// One workgroup owns a BM x BN output tile.  Each k step copies a BM x BK
+// slice of A and a BK x BN slice of B from global memory into LDS; the
+// wavefronts then run fp32 matrix-core instructions (v_mfma_f32_32x32x2_f32
+// or v_mfma_f32_16x16x4_f32) on 32 x 32 or 16 x 16 blocks accumulated in
+// registers.  It is the shared-memory tiled
+// and register-blocked design the pages describe (StaleyNET "The matrix
+// product": tiles staged in fast shared memory, many outputs per thread so
+// each value read feeds several products) mapped onto CDNA4's 64-wide
+// wavefronts, LDS and matrix cores.
+//
+//  - Global loads run along each operand's contiguous ("fast") axis,
+//    whichever it is, so all four transpose cases read whole cache lines.
+//    (The tiled kernel of "PyTorch demystified 3", section "Opt. 6 - Tiled
+//    matmul kernel", loads both operands one way, which strides the
+//    transposed ones.)  The LDS copy keeps the global orientation, padded so
+//    fragment reads are free of bank conflicts.
+//  - The load width is a template parameter: 16-byte loads (contiguous,
+//    16-byte aligned, extent a multiple of 4) or element loads (any stride,
+//    any alignment).  Straight-line load code lets the compiler keep every
+//    load of the next k slice in flight while the matrix cores work.
+//  - LDS is double buffered (one barrier per k step) and the fragments of
+//    the next 8-deep k group are read from LDS while the current group's
+//    matrix-core instructions run.
+//  - Loads and stores go through buffer resources.  A lane outside the
+//    matrix gets an offset beyond the resource's range, so the hardware
+//    returns zero for its load and drops its store: no branch and no access
+//    outside the operands.
+//  - Workgroup ids are remapped so that neighbouring tiles (which share A
+//    rows and B columns) run on the same XCD and share its L2.
+//
+// Every output element is summed by one lane in an order fixed by the tile
+// configuration, so results are reproducible bit for bit.  No atomics.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace sgemm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Raw buffer resources: stride 0, num_records = 2^31 bytes.  Offsets at or
+// beyond kOutOfRange fail the hardware range check (loads read 0, stores are
+// dropped).  Word 3 holds the gfx9-family data-format bits.
+constexpr unsigned kOutOfRange = 0x80000000u;
+constexpr int kRecordBytes = int(0x80000000u);
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, kRecordBytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ f32x4 load4(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
+}
+
+__device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
+}
+
+__device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, int(off), 0, 0);
+}
+
+// An R x F tile (F along the operand's contiguous axis) held as one f32x4
+// per slot; NT threads cover its R*F/4 slots in rounds, the last round
+// possibly partial.  In LDS the tile is stored [R][F + PAD].
+template <int R, int F, int PAD, int NT, bool V4>
+struct TileLoader {
+    static constexpr int kSlotsPerRow = F / 4;
+    static constexpr int kTotal = R * F / 4;
+    static constexpr int kSlots = (kTotal + NT - 1) / NT;
+    static_assert(F % 4 == 0, "tile rows must split into 4-float slots");
+    f32x4 v[kSlots];
+
+    static __device__ __forceinline__ bool active(int q, int tid) {
+        return (kTotal % NT == 0) || q + 1 < kSlots || tid + q * NT < kTotal;
+    }
+
+    // Tile row r is global row r + r_off (valid below r_lim); tile column f
+    // is global column f + f_off (valid below f_lim).  Element offsets are
+    // row * s_r + col * s_f from the resource base.  With V4, s_f == 1 and
+    // f_lim is a multiple of 4 (the planner checks both).
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int tid, unsigned r_off,
+                                         unsigned r_lim, unsigned f_off, unsigned f_lim,
+                                         unsigned s_r, unsigned s_f) {
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) {
+            if (!active(q, tid)) continue;
+            const int s = tid + q * NT;
+            const unsigned rg = unsigned(s / kSlotsPerRow) + r_off;
+            const unsigned fg = unsigned(s % kSlotsPerRow) * 4u + f_off;
+            const bool rv = rg < r_lim;
+            const unsigned row_off = rg * s_r;
+            if constexpr (V4) {
+                v[q] = load4(rs, (rv && fg < f_lim) ? (row_off + fg) * 4u : kOutOfRange);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned fe = fg + unsigned(e);
+                    v[q][e] = load1(rs, (rv && fe < f_lim) ? (row_off + fe * s_f) * 4u : kOutOfRange);
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(float *lds, int tid) const {
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) {
+            if (!active(q, tid)) continue;
+            const int s = tid + q * NT;
+            const int r = s / kSlotsPerRow, f = (s % kSlotsPerRow) * 4;
+            *reinterpret_cast<f32x4 *>(lds + r * (F + PAD) + f) = v[q];
+        }
+    }
+};
+
+// Workgroup -> (batch, tile row, tile column).  The hardware hands out
+// workgroup ids round-robin over the 8 XCDs; the remap gives each XCD a
+// contiguous range of tile ids, and tiles are ordered in groups of 8 tile
+// rows so that consecutive ids share B columns and nearby A rows.
+__device__ __forceinline__ void map_tile(int wg, int total, int tiles_m, int tiles_n, int &b,
+                                         int &tm, int &tn) {
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        wg = (wg & 7) * per + (wg >> 3);
+    }
+    const int per_batch = tiles_m * tiles_n;
+    b = wg / per_batch;
+    const int t = wg - b * per_batch;
+    constexpr int kGroup = 8;
+    const int group = t / (kGroup * tiles_n);
+    const int first = group * kGroup;
+    const int gsz = min(tiles_m - first, kGroup);
+    const int in = t - group * kGroup * tiles_n;
+    tm = first + in % gsz;
+    tn = in / gsz;
+}
+
+// Matrix-core block of MF x MF outputs.
+//  MF = 32: v_mfma_f32_32x32x2_f32.  Lanes 0-31 feed the k = 0 operand and
+//    lanes 32-63 the k = 1 operand; accumulator register r of lane l holds
+//    row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+//  MF = 16: v_mfma_f32_16x16x4_f32.  Lane quarter l/16 feeds k = l/16;
+//    register r of lane l holds row 4*(l/16) + r, column l%16.
+// k order inside a BK slice: in a group of KG = 4 * (64/MF) consecutive k,
+// instruction q (0..3) gives lane group h = l/MF the element k = KG*g + 4h + q,
+// so a lane reading a k-contiguous tile fetches its 4 values of a group with
+// one 16-byte LDS read.  A and B use the same order, so every product
+// A[i,p]*B[p,j] is formed exactly once.
+template <int MF>
+struct Mfma;
+
+template <>
+struct Mfma<32> {
+    typedef f32x16 acc_t;
+    static constexpr int kRegs = 16;
+    static __device__ __forceinline__ acc_t op(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
+};
+
+template <>
+struct Mfma<16> {
+    typedef f32x4 acc_t;
+    static constexpr int kRegs = 4;
+    static __device__ __forceinline__ acc_t op(float a, float b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int r, int lh) { return 4 * lh + r; }
+};
+
+template <int T, bool AK, bool BKF, bool AV4, bool BV4>
+__global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma(MfmaArgs p) {
+    constexpr TileCfg cfg = kTiles[T];
+    constexpr int BM = cfg.bm, BN = cfg.bn, BK = cfg.bk, MF = cfg.mf;
+    constexpr int NT = cfg.wgm * cfg.wgn * 64;
+    constexpr int WM = BM / cfg.wgm, WN = BN / cfg.wgn;
+    constexpr int TM = WM / MF, TN = WN / MF;
+    constexpr int KG = 4 * (64 / MF);
+    constexpr int G = BK / KG;
+    using M = Mfma<MF>;
+    using acc_t = typename M::acc_t;
+    static_assert(WM % MF == 0 && WN % MF == 0 && BK % KG == 0, "tile shape");
+
+    // LDS tiles: A as [BM][BK+pad] (k fast) or [BK][BM+pad] (m fast);
+    //            B as [BN][BK+pad] (k fast) or [BK][BN+pad] (n fast).
+    constexpr int A_R = AK ? BM : BK, A_F = AK ? BK : BM, A_PAD = cfg.pad(AK);
+    constexpr int B_R = BKF ? BN : BK, B_F = BKF ? BK : BN, B_PAD = cfg.pad(BKF);
+    constexpr int A_LD = A_F + A_PAD, B_LD = B_F + B_PAD;
+    constexpr int A_SIZE = A_R * A_LD, B_SIZE = B_R * B_LD;
+    static_assert(2 * 4 * (A_SIZE + B_SIZE) == cfg.lds_bytes(AK, BKF), "LDS carve-up");
+    __shared__ __attribute__((aligned(16))) float smem[2 * (A_SIZE + B_SIZE)];
+
+    const int tid = threadIdx.x;
+    int b, tm, tn;
+    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, b, tm, tn);
+    const int i0 = tm * BM, j0 = tn * BN;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(p.A + (long long)b * p.sA_b + (long long)i0 * p.sA_m);
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(p.B + (long long)b * p.sB_b + (long long)j0 * p.sB_n);
+
+    const unsigned m_left = unsigned(p.m - i0), n_left = unsigned(p.n - j0);
+    const unsigned K = unsigned(p.k);
+    const unsigned sAm = unsigned(p.sA_m), sAk = unsigned(p.sA_k);
+    const unsigned sBk = unsigned(p.sB_k), sBn = unsigned(p.sB_n);
+
+    TileLoader<A_R, A_F, A_PAD, NT, AV4> la;
+    TileLoader<B_R, B_F, B_PAD, NT, BV4> lb;
+    auto load_slice = [&](unsigned k0) {
+        if constexpr (AK) la.load(rA, tid, 0u, m_left, k0, K, sAm, sAk);
+        else              la.load(rA, tid, k0, K, 0u, m_left, sAk, sAm);
+        if constexpr (BKF) lb.load(rB, tid, 0u, n_left, k0, K, sBn, sBk);
+        else               lb.load(rB, tid, k0, K, 0u, n_left, sBk, sBn);
+    };
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / cfg.wgn, wn = wave % cfg.wgn;
+    const int lr = lane % MF, lh = lane / MF;
+
+    // Fragments of k group g: af[a][q] = A[row lr of block a][KG*g + 4*lh + q].
+    auto read_frags = [&](const float *As, const float *Bs, int g, f32x4 (&af)[TM],
+                          f32x4 (&bf)[TN]) {
+        const int kq = KG * g + 4 * lh;
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int mr = wm * WM + a * MF + lr;
+            if constexpr (AK) {
+                af[a] = *reinterpret_cast<const f32x4 *>(As + mr * A_LD + kq);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) af[a][q] = As[(kq + q) * A_LD + mr];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < TN; ++c) {
+            const int nc = wn * WN + c * MF + lr;
+            if constexpr (BKF) {
+                bf[c] = *reinterpret_cast<const f32x4 *>(Bs + nc * B_LD + kq);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bf[c][q] = Bs[(kq + q) * B_LD + nc];
+            }
+        }
+    };
+
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int c = 0; c < TN; ++c) acc[a][c] = acc_t{};
+
+    const int KT = (p.k + BK - 1) / BK;
+    if (KT > 0) {
+        load_slice(0u);
+        la.store(smem, tid);
+        lb.store(smem + A_SIZE, tid);
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+            const float *As = smem + (kt & 1) * (A_SIZE + B_SIZE);
+            const float *Bs = As + A_SIZE;
+            const bool more = kt + 1 < KT;
+            if (more) load_slice(unsigned(kt + 1) * BK);
+            f32x4 af[2][TM], bf[2][TN];
+            read_frags(As, Bs, 0, af[0], bf[0]);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (g + 1 < G) read_frags(As, Bs, g + 1, af[(g + 1) & 1], bf[(g + 1) & 1]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int a = 0; a < TM; ++a)
+#pragma unroll
+                        for (int c = 0; c < TN; ++c)
+                            acc[a][c] = M::op(af[g & 1][a][q], bf[g & 1][c][q], acc[a][c]);
+            }
+            if (more) {
+                float *nA = smem + ((kt + 1) & 1) * (A_SIZE + B_SIZE);
+                la.store(nA, tid);
+                lb.store(nA + A_SIZE, tid);
+            }
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: C = alpha*acc, or C_old + alpha*acc as one fused
+    // multiply-add when accumulating.  The MF lanes of a lane group cover MF
+    // consecutive columns of one row.
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(p.C + (long long)b * p.sC_b + (long long)i0 * p.sC_m + (long long)j0 * p.sC_n);
+    const unsigned sCm = unsigned(p.sC_m), sCn = unsigned(p.sC_n);
+    const float alpha = p.alpha;
+    const bool accumulate = p.accumulate != 0;
+    constexpr int R = M::kRegs;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+#pragma unroll
+        for (int c = 0; c < TN; ++c) {
+            const unsigned col = unsigned(wn * WN + c * MF + lr);
+            unsigned off[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const unsigned row = unsigned(wm * WM + a * MF + M::row(r, lh));
+                off[r] = (row < m_left && col < n_left) ? (row * sCm + col * sCn) * 4u : kOutOfRange;
+            }
+            if (accumulate) {
+                float old[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) old[r] = load1(rC, off[r]);
+#pragma unroll
+                for (int r = 0; r < R; ++r) store1(rC, off[r], __builtin_fmaf(alpha, acc[a][c][r], old[r]));
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) store1(rC, off[r], alpha * acc[a][c][r]);
+            }
+        }
+    }
+}
+
+// Launch-table rows for one tile: every (A fast axis, B fast axis, A load
+// width, B load width) combination.
+template <int T, bool AK, bool BKF, bool AV4, bool BV4>
+void launch_mfma(const MfmaArgs &a, unsigned grid, hipStream_t s) {
+    constexpr int nt = kTiles[T].wgm * kTiles[T].wgn * 64;
+    hipLaunchKernelGGL((sgemm_mfma<T, AK, BKF, AV4, BV4>), dim3(grid), dim3(nt), 0, s, a);
+}
+
+template <int T, bool AK, bool BKF>
+void fill_layout(MfmaTable &tab) {
+    tab.f[T][AK][BKF][0][0] = launch_mfma<T, AK, BKF, false, false>;
+    tab.f[T][AK][BKF][0][1] = launch_mfma<T, AK, BKF, false, true>;
+    tab.f[T][AK][BKF][1][0] = launch_mfma<T, AK, BKF, true, false>;
+    tab.f[T][AK][BKF][1][1] = launch_mfma<T, AK, BKF, true, true>;
+}
+
+template <int T>
+void fill_tile(MfmaTable &tab) {
+    fill_layout<T, false, false>(tab);
+    fill_layout<T, false, true>(tab);
+    fill_layout<T, true, false>(tab);
+    fill_layout<T, true, true>(tab);
+}
+
+}  // namespace sgemm

@@ -11,6 +11,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 namespace sgemm {
 
@@ -35,18 +37,18 @@ bool ranges_overlap(uintptr_t p, int64_t last_p, uintptr_t q, int64_t last_q) {
 }
 
 
-// Width (in floats) of the global loads along an operand's fast axis.
+// Width (in floats) of the global loads along an operand's fast axis: 4
+// (16-byte loads) when the fast axis is contiguous, its extent a multiple of
+// 4 and every tile base 16-byte aligned; otherwise 1 (element loads, any
+// stride and alignment).
 int vector_width(uintptr_t base, int64_t fast_stride, int64_t fast_extent,
                  int64_t slow_stride, int64_t batch_stride, int64_t batch) {
     if (fast_stride != 1) return 1;
-    for (int v : {4, 2}) {
-        if (fast_extent % v) continue;
-        if (base % (uintptr_t)(4 * v)) continue;
-        if (slow_stride % v) continue;
-        if (batch > 1 && batch_stride % v) continue;
-        return v;
-    }
-    return 1;
+    if (fast_extent % 4) return 1;
+    if (base % 16) return 1;
+    if (slow_stride % 4) return 1;
+    if (batch > 1 && batch_stride % 4) return 1;
+    return 4;
 }
 
 // Which axis of a rows x cols operand is contiguous: returns true if the
@@ -137,16 +139,6 @@ int validate(const GemmArgs &a, std::string &why) {
 
 namespace {
 
-// Relative per-CU throughput of a tile when the matrix cores are fed by it
-// (larger tiles reuse each loaded value for more products).
-double tile_rate(const TileCfg &t) {
-    int area = t.bm * t.bn;
-    if (area >= 128 * 128) return 1.0;
-    if (area >= 128 * 64) return 0.85;
-    if (area >= 64 * 64) return 0.6;
-    return 0.3;
-}
-
 bool tile_fits(const Plan &p, const TileCfg &t) {
     // Buffer offsets are 32-bit from a per-workgroup base: the workgroup's
     // slice of each operand has to lie within 2 GiB of that base.
@@ -155,13 +147,26 @@ bool tile_fits(const Plan &p, const TileCfg &t) {
            fits_buffer(t.bm, p.sC_m, t.bn, p.sC_n);
 }
 
+// Estimated cycles of the whole launch with tile t.  Tiles are spread over
+// the CUs; up to `occ` of them run concurrently on one CU (bounded by LDS and
+// by how many each CU receives).  One round of `occ` tiles costs their
+// matrix-core work at the tile's sustained rate, plus the epilogue traffic of
+// C (read and written when accumulating) at ~10 bytes per cycle per CU, plus
+// a fixed start-up latency.  Constants were fitted to tile sweeps on MI355X.
 double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
+    const double kLdsBytes = 160.0 * 1024.0, kStoreBytesPerCycle = 10.0, kStartCycles = 1000.0;
+    const double kFlopPerCuCycle = 256.0;
     int64_t tm = (p.m + t.bm - 1) / t.bm, tn = (p.n + t.bn - 1) / t.bn;
     double tiles = double(p.batch) * double(tm) * double(tn);
-    double ksteps = std::max<double>(1.0, double((p.k + t.bk - 1) / t.bk));
-    double per_tile = double(t.bm) * t.bn * (ksteps * t.bk + 16.0 * (p.accumulate ? 2 : 1));
-    double rounds = std::ceil(tiles / double(std::max(num_cus, 1)));
-    return rounds * per_tile / tile_rate(t);
+    double cus = double(std::max(num_cus, 1));
+    double fit = std::max(1.0, std::min(8.0, std::floor(kLdsBytes / t.lds_bytes(p.a_kfast, p.b_kfast))));
+    double per_cu = std::ceil(tiles / cus);
+    double occ = std::min(fit, per_cu);
+    double rounds = std::ceil(tiles / (cus * occ));
+    double kpad = double((p.k + t.bk - 1) / t.bk) * t.bk;
+    double compute = occ * t.bm * t.bn * 2.0 * kpad / kFlopPerCuCycle / t.rate;
+    double epilogue = occ * t.bm * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
+    return rounds * (compute + epilogue + kStartCycles);
 }
 
 }  // namespace
@@ -210,10 +215,21 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
     const int64_t i32max = (int64_t(1) << 31) - 1;
     bool small_enough = p.m <= i32max && p.n <= i32max && p.k <= i32max && p.batch <= i32max;
 
+    // SGEMM_FORCE_TILE=<tile name> restricts the choice to that tile when it
+    // can serve the call (for tuning sweeps); otherwise it is ignored.
+    int forced = -1;
+    if (const char *env = std::getenv("SGEMM_FORCE_TILE")) {
+        for (int t = 0; t < kNumTiles; ++t)
+            if (std::strcmp(env, kTiles[t].name) == 0) forced = t;
+    }
+    if (forced >= 0 && !(small_enough && family == Family::Auto && tile_fits(p, kTiles[forced])))
+        forced = -1;
+
     int best = -1;
     if (small_enough && family != Family::Generic) {
         double best_cost = 0;
         for (int t = 0; t < kNumTiles; ++t) {
+            if (forced >= 0 && t != forced) continue;
             if (family == Family::Mfma && t == kWaveTile) continue;
             if (family == Family::Wave && t != kWaveTile) continue;
             if (!tile_fits(p, kTiles[t])) continue;

@@ -23,33 +23,46 @@ enum class Family : int { Auto = 0, Mfma = 1, Wave = 2, Generic = 3 };
 
 // One LDS-tiled MFMA configuration.  Tiles are BM x BN outputs with BK-deep
 // k steps; WGM x WGN wavefronts each own a (BM/WGM) x (BN/WGN) sub-tile made
-// of 32 x 32 matrix-core blocks.
+// of MF x MF matrix-core blocks (MF = 32: v_mfma_f32_32x32x2_f32, MF = 16:
+// v_mfma_f32_16x16x4_f32).
 struct TileCfg {
     int bm, bn, bk;
     int wgm, wgn;
+    int mf;
     const char *name;
+    // Fraction of the matrix-core peak a CU sustains on this tile when k is
+    // long and the CU is full (measured on MI355X, 4 x 4096^3).
+    double rate;
     constexpr int waves() const { return wgm * wgn; }
+    // Padding of an LDS tile row: 4 floats on a k-fast tile; on an m- or
+    // n-fast tile 8 (32-wide blocks) or 4 (16-wide blocks), which spreads the
+    // lane groups that read different k rows over distinct banks.
+    constexpr int pad(bool kfast) const { return kfast ? 4 : (mf == 32 ? 8 : 4); }
     // LDS bytes of the kernel's carve-up: two buffers of the A and B tiles,
-    // each stored [slow][fast + pad], pad 4 on a k-fast tile and 8 on an
-    // m- or n-fast tile.
+    // each stored [slow][fast + pad].
     constexpr int lds_bytes(bool a_kfast, bool b_kfast) const {
-        return 2 * 4 * ((a_kfast ? bm * (bk + 4) : bk * (bm + 8)) +
-                        (b_kfast ? bn * (bk + 4) : bk * (bn + 8)));
+        return 2 * 4 * ((a_kfast ? bm * (bk + pad(true)) : bk * (bm + pad(false))) +
+                        (b_kfast ? bn * (bk + pad(true)) : bk * (bn + pad(false))));
     }
 };
 
 // The MFMA tile table.  Kernel instantiations are generated from the same
-// indices, so the order is part of the contract between planner and
-// kernels.  Index kWaveTile is the one-wavefront tile of the WAVE family.
-constexpr int kNumTiles = 6;
+// indices (one translation unit per tile), so the order is part of the
+// contract between planner and kernels.  Index kWaveTile is the
+// one-wavefront tile of the WAVE family.
+constexpr int kNumTiles = 10;
 constexpr int kWaveTile = 5;
 inline constexpr TileCfg kTiles[kNumTiles] = {
-    {128, 128, 32, 2, 2, "t128x128"},
-    {128, 64, 32, 2, 2, "t128x64"},
-    {64, 128, 32, 2, 2, "t64x128"},
-    {64, 64, 32, 2, 2, "t64x64"},
-    {256, 128, 32, 2, 2, "t256x128"},
-    {32, 32, 32, 1, 1, "wave32x32"},
+    {128, 128, 32, 2, 2, 32, "t128x128", 0.83},
+    {128, 64, 32, 2, 2, 32, "t128x64", 0.80},
+    {64, 128, 32, 2, 2, 32, "t64x128", 0.81},
+    {64, 64, 32, 2, 2, 32, "t64x64", 0.77},
+    {256, 128, 32, 2, 2, 32, "t256x128", 0.74},
+    {32, 32, 32, 1, 1, 32, "wave32x32", 0.64},
+    {128, 160, 32, 4, 1, 32, "t128x160", 0.81},
+    {128, 80, 32, 4, 1, 16, "t128x80m16", 0.76},
+    {64, 176, 32, 4, 1, 16, "t64x176m16", 0.71},
+    {64, 64, 32, 2, 2, 16, "t64x64m16", 0.82},
 };
 
 // Everything a launch needs, in kernel terms: A is m x k, B is k x n, C is

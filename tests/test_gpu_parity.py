@@ -177,6 +177,30 @@ def test_tile_boundaries(mnk, path):
         assert err_ratio(p, got, ref) <= TOL, (mnk, a_major, b_major)
 
 
+TILE_NAMES = ["t128x128", "t128x64", "t64x128", "t64x64", "t256x128", "wave32x32",
+              "t128x160", "t128x80m16", "t64x176m16", "t64x64m16"]
+
+
+@pytest.mark.parametrize("tile", TILE_NAMES)
+def test_every_tile(tile, monkeypatch):
+    """Each matrix-core tile configuration, forced, on ragged multi-tile
+    shapes in all four transpose cases, with 16-byte loads (aligned shape)
+    and element loads (padded lines), accumulating and not."""
+    monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+    shapes = [(2, 300, 260, 96, 0), (2, 150, 190, 70, 3), (1, 33, 520, 40, 1)]
+    for batch, m, n, k, pad in shapes:
+        for a_major, b_major in LAYOUTS:
+            for acc in (False, True):
+                p = wl.random_problem(m + n + k + pad, batch, m, n, k, a_major=a_major,
+                                      b_major=b_major, dist="normal", alpha=0.625,
+                                      accumulate=acc, pad=pad)
+                info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
+                assert tile in info["kernel"], info
+                got, ref = out(p, gpu_call(p)), out(p, oracle_call(p))
+                e = err_ratio(p, got, ref)
+                assert e <= TOL, (tile, m, n, k, pad, a_major, b_major, acc, e)
+
+
 def test_column_major_output():
     """C stored column-major is served as C^T = B^T A^T."""
     for a_major, b_major in LAYOUTS:
