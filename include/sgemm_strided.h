@@ -64,7 +64,7 @@ enum sgemm_status {
 enum sgemm_path {
     SGEMM_PATH_AUTO = 0,    /* planner's choice (what sgemm_strided_batched uses) */
     SGEMM_PATH_MFMA = 1,    /* LDS-tiled fp32 MFMA kernel, per-layout coalesced loaders */
-    SGEMM_PATH_WAVE = 2,    /* one wavefront per small output tile: tiny and skinny shapes */
+    SGEMM_PATH_WAVE = 2,    /* one wavefront per tile, operands straight to registers: short k, few tiles */
     SGEMM_PATH_GENERIC = 3  /* any strides, 64-bit addressing, fp32 FMA */
 };
 

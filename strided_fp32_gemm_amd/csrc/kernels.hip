@@ -2,9 +2,10 @@
 //
 // C[b,i,j] <- alpha * sum_p A[b,i,p] B[b,p,j] (+ C[b,i,j]); operands are
 // addressed through (batch, row, col) element strides (StaleyNET "GPU
-// Implementation", section "The matrix product").  The matrix-core kernel
-// lives in mfma_kernel.hpp; this file holds the generic kernel, which serves
-// layouts whose offsets exceed the 32-bit buffer range, and launch_plan().
+// Implementation", section "The matrix product").  The matrix-core kernels
+// live in mfma_kernel.hpp (LDS-tiled) and wave_kernel.hpp (direct
+// wavefront); this file holds the generic kernel, which serves layouts whose
+// offsets exceed the 32-bit buffer range, and launch_plan().
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -90,8 +91,20 @@ const MfmaTable &table() {
         fill_tile_6(tab);
         fill_tile_7(tab);
         fill_tile_8(tab);
-        fill_tile_9(tab);
-        static_assert(kNumTiles == 10, "launch table covers every tile");
+        static_assert(kNumTiles == 9, "launch table covers every tile");
+        return tab;
+    }();
+    return t;
+}
+
+const WaveTable &wave_table() {
+    static const WaveTable t = [] {
+        WaveTable tab{};
+        fill_wave_0(tab);
+        fill_wave_1(tab);
+        fill_wave_2(tab);
+        fill_wave_3(tab);
+        static_assert(kNumWaveTiles == 4, "launch table covers every wave tile");
         return tab;
     }();
     return t;
@@ -125,9 +138,14 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         a.m = int(p.m); a.n = int(p.n); a.k = int(p.k);
         a.tiles_m = int(p.tiles_m); a.tiles_n = int(p.tiles_n);
         a.accumulate = p.accumulate;
+        a.c_vec4 = p.c_vec4 ? 1 : 0;
         a.alpha = p.alpha;
-        table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4](
-            a, unsigned(p.workgroups), stream);
+        if (p.family == Family::Wave)
+            wave_table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4](
+                a, unsigned(p.workgroups), stream);
+        else
+            table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4](
+                a, unsigned(p.workgroups), stream);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {

@@ -22,6 +22,7 @@ struct MfmaArgs {
     int m, n, k;
     int tiles_m, tiles_n;
     int accumulate;
+    int c_vec4;   // C rows take 16-byte stores (n-contiguous, aligned, n % 4 == 0)
     float alpha;
 };
 
@@ -39,13 +40,16 @@ struct GenericArgs {
     int accumulate;
 };
 
-// Launchers of the MFMA kernel, indexed [tile][A k-fast][B k-fast]
-// [A 16-byte loads][B 16-byte loads].  Each tile's row is filled by its own
-// translation unit (mfma_t<tile>.hip) so the instantiations compile in
+// Launchers indexed [tile][A k-fast][B k-fast][A 16-byte loads]
+// [B 16-byte loads].  Each tile's row is filled by its own translation unit
+// (mfma_t<tile>.hip, wave_w<tile>.hip) so the instantiations compile in
 // parallel.
 using MfmaLaunch = void (*)(const MfmaArgs &, unsigned, hipStream_t);
 struct MfmaTable {
     MfmaLaunch f[kNumTiles][2][2][2][2];
+};
+struct WaveTable {
+    MfmaLaunch f[kNumWaveTiles][2][2][2][2];
 };
 void fill_tile_0(MfmaTable &);
 void fill_tile_1(MfmaTable &);
@@ -56,7 +60,10 @@ void fill_tile_5(MfmaTable &);
 void fill_tile_6(MfmaTable &);
 void fill_tile_7(MfmaTable &);
 void fill_tile_8(MfmaTable &);
-void fill_tile_9(MfmaTable &);
+void fill_wave_0(WaveTable &);
+void fill_wave_1(WaveTable &);
+void fill_wave_2(WaveTable &);
+void fill_wave_3(WaveTable &);
 
 // Enqueues the plan on `stream`.  Returns kOk, or kErrHip with `why` set when
 // the runtime rejects the launch.

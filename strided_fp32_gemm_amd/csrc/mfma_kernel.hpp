@@ -47,6 +47,7 @@ namespace sgemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resources: stride 0, num_records = 2^31 bytes.  Offsets at or
 // beyond kOutOfRange fail the hardware range check (loads read 0, stores are
@@ -69,6 +70,10 @@ __device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, unsigned off) {
 
 __device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, int(off), 0, 0);
+}
+
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, unsigned off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, int(off), 0, 0);
 }
 
 // An R x F tile (F along the operand's contiguous axis) held as one f32x4
@@ -199,8 +204,12 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
     constexpr int B_R = BKF ? BN : BK, B_F = BKF ? BK : BN, B_PAD = cfg.pad(BKF);
     constexpr int A_LD = A_F + A_PAD, B_LD = B_F + B_PAD;
     constexpr int A_SIZE = A_R * A_LD, B_SIZE = B_R * B_LD;
-    static_assert(2 * 4 * (A_SIZE + B_SIZE) == cfg.lds_bytes(AK, BKF), "LDS carve-up");
-    __shared__ __attribute__((aligned(16))) float smem[2 * (A_SIZE + B_SIZE)];
+    static_assert(4 * (A_SIZE + B_SIZE) == cfg.buffer_lds_bytes(AK, BKF), "LDS carve-up");
+    constexpr int E_LD = WN + 4;  // staged-epilogue row pitch
+    // Dynamic LDS of cfg.lds_bytes(AK, BKF, slices) bytes: one A/B buffer
+    // when the k extent is a single slice, two otherwise, and at least the
+    // staged epilogue's footprint.
+    extern __shared__ __attribute__((aligned(16))) float smem[];
 
     const int tid = threadIdx.x;
     int b, tm, tn;
@@ -217,13 +226,20 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
     const unsigned sAm = unsigned(p.sA_m), sAk = unsigned(p.sA_k);
     const unsigned sBk = unsigned(p.sB_k), sBn = unsigned(p.sB_n);
 
-    TileLoader<A_R, A_F, A_PAD, NT, AV4> la;
-    TileLoader<B_R, B_F, B_PAD, NT, BV4> lb;
-    auto load_slice = [&](unsigned k0) {
+    using LoaderA = TileLoader<A_R, A_F, A_PAD, NT, AV4>;
+    using LoaderB = TileLoader<B_R, B_F, B_PAD, NT, BV4>;
+    // Issue the global loads of the k slice starting at k0.  Slices past the
+    // end of k fail the range check and read zeros without touching memory.
+    auto issue = [&](LoaderA &la, LoaderB &lb, unsigned k0) {
         if constexpr (AK) la.load(rA, tid, 0u, m_left, k0, K, sAm, sAk);
         else              la.load(rA, tid, k0, K, 0u, m_left, sAk, sAm);
         if constexpr (BKF) lb.load(rB, tid, 0u, n_left, k0, K, sBn, sBk);
         else               lb.load(rB, tid, k0, K, 0u, n_left, sBk, sBn);
+    };
+    auto put = [&](const LoaderA &la, const LoaderB &lb, int buf) {
+        float *base = smem + buf * (A_SIZE + B_SIZE);
+        la.store(base, tid);
+        lb.store(base + A_SIZE, tid);
     };
 
     const int lane = tid & 63, wave = tid >> 6;
@@ -262,48 +278,114 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
 #pragma unroll
         for (int c = 0; c < TN; ++c) acc[a][c] = acc_t{};
 
+    // One k slice from LDS buffer `buf`: fragments of group g+1 are read
+    // while the matrix-core instructions of group g run.
+    auto multiply = [&](int buf) {
+        const float *As = smem + buf * (A_SIZE + B_SIZE);
+        const float *Bs = As + A_SIZE;
+        f32x4 af[2][TM], bf[2][TN];
+        read_frags(As, Bs, 0, af[0], bf[0]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (g + 1 < G) read_frags(As, Bs, g + 1, af[(g + 1) & 1], bf[(g + 1) & 1]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int c = 0; c < TN; ++c)
+                        acc[a][c] = M::op(af[g & 1][a][q], bf[g & 1][c][q], acc[a][c]);
+        }
+    };
+
     const int KT = (p.k + BK - 1) / BK;
     if (KT > 0) {
-        load_slice(0u);
-        la.store(smem, tid);
-        lb.store(smem + A_SIZE, tid);
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            const float *As = smem + (kt & 1) * (A_SIZE + B_SIZE);
-            const float *Bs = As + A_SIZE;
-            const bool more = kt + 1 < KT;
-            if (more) load_slice(unsigned(kt + 1) * BK);
-            f32x4 af[2][TM], bf[2][TN];
-            read_frags(As, Bs, 0, af[0], bf[0]);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                if (g + 1 < G) read_frags(As, Bs, g + 1, af[(g + 1) & 1], bf[(g + 1) & 1]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int a = 0; a < TM; ++a)
-#pragma unroll
-                        for (int c = 0; c < TN; ++c)
-                            acc[a][c] = M::op(af[g & 1][a][q], bf[g & 1][c][q], acc[a][c]);
-            }
-            if (more) {
-                float *nA = smem + ((kt + 1) & 1) * (A_SIZE + B_SIZE);
-                la.store(nA, tid);
-                lb.store(nA + A_SIZE, tid);
-            }
+        LoaderA la0;
+        LoaderB lb0;
+        if constexpr (cfg.pf == 1) {
+            // Global -> registers one slice ahead, registers -> LDS at the end
+            // of each step, one barrier per step.
+            issue(la0, lb0, 0u);
+            put(la0, lb0, 0);
             __syncthreads();
+            for (int kt = 0; kt < KT; ++kt) {
+                const bool more = kt + 1 < KT;
+                if (more) issue(la0, lb0, unsigned(kt + 1) * BK);
+                multiply(kt & 1);
+                if (more) put(la0, lb0, (kt + 1) & 1);
+                __syncthreads();
+            }
+        } else {
+            // Two register sets: while slice kt is multiplied, slice kt+1 is
+            // landing in one set and slice kt+2 is being requested into the
+            // other, so two slices of loads are in flight per workgroup.  The
+            // loop is unrolled by two so the sets alternate statically.
+            LoaderA la1;
+            LoaderB lb1;
+            issue(la0, lb0, 0u);
+            issue(la1, lb1, unsigned(BK));
+            put(la0, lb0, 0);
+            __syncthreads();
+            auto step = [&](int kt, LoaderA &la_next, LoaderB &lb_next, LoaderA &la_free,
+                            LoaderB &lb_free) {
+                issue(la_free, lb_free, unsigned(kt + 2) * BK);
+                multiply(kt & 1);
+                if (kt + 1 < KT) put(la_next, lb_next, (kt + 1) & 1);
+                __syncthreads();
+            };
+            for (int kt = 0; kt < KT; kt += 2) {
+                step(kt, la1, lb1, la0, lb0);
+                if (kt + 1 < KT) step(kt + 1, la0, lb0, la1, lb1);
+            }
         }
     }
 
     // Epilogue: C = alpha*acc, or C_old + alpha*acc as one fused
-    // multiply-add when accumulating.  The MF lanes of a lane group cover MF
-    // consecutive columns of one row.
+    // multiply-add when accumulating.
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(p.C + (long long)b * p.sC_b + (long long)i0 * p.sC_m + (long long)j0 * p.sC_n);
     const unsigned sCm = unsigned(p.sC_m), sCn = unsigned(p.sC_n);
     const float alpha = p.alpha;
     const bool accumulate = p.accumulate != 0;
     constexpr int R = M::kRegs;
+    if (p.c_vec4) {
+        // Staged: each wavefront writes its WM x WN sub-tile to its own LDS
+        // region (the main loop's buffers are free after its last barrier),
+        // then stores whole rows with 16-byte stores, WN/4 lanes per row.
+        float *stage = smem + wave * (WM * E_LD);
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int c = 0; c < TN; ++c)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    stage[(a * MF + M::row(r, lh)) * E_LD + c * MF + lr] = acc[a][c][r];
+        __syncthreads();
+        constexpr int kQuads = WM * WN / 4;
+        constexpr int kPerRow = WN / 4;
+        static_assert(kQuads % 64 == 0, "wave sub-tile must split into 64-lane rounds");
+#pragma unroll
+        for (int i = 0; i < kQuads / 64; ++i) {
+            const int quad = lane + 64 * i;
+            const int row = quad / kPerRow, c4 = (quad % kPerRow) * 4;
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + row * E_LD + c4);
+            const unsigned grow = unsigned(wm * WM + row), gcol = unsigned(wn * WN + c4);
+            const unsigned off = (grow < m_left && gcol < n_left) ? (grow * sCm + gcol) * 4u : kOutOfRange;
+            f32x4 o;
+            if (accumulate) {
+                const f32x4 old = load4(rC, off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(alpha, v[e], old[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = alpha * v[e];
+            }
+            store4(rC, off, o);
+        }
+        return;
+    }
+    // Direct: every lane stores its accumulators; the MF lanes of a lane
+    // group cover MF consecutive columns of one row.
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
 #pragma unroll
@@ -333,8 +415,16 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
 // width, B load width) combination.
 template <int T, bool AK, bool BKF, bool AV4, bool BV4>
 void launch_mfma(const MfmaArgs &a, unsigned grid, hipStream_t s) {
-    constexpr int nt = kTiles[T].wgm * kTiles[T].wgn * 64;
-    hipLaunchKernelGGL((sgemm_mfma<T, AK, BKF, AV4, BV4>), dim3(grid), dim3(nt), 0, s, a);
+    constexpr TileCfg cfg = kTiles[T];
+    constexpr int nt = cfg.wgm * cfg.wgn * 64;
+    const long long slices = (a.k + cfg.bk - 1) / cfg.bk;
+    const int lds = cfg.lds_bytes(AK, BKF, slices);
+    // Allow this kernel the largest dynamic LDS any of its launches asks for.
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&sgemm_mfma<T, AK, BKF, AV4, BV4>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes(AK, BKF, 2));
+    (void)attr;
+    hipLaunchKernelGGL((sgemm_mfma<T, AK, BKF, AV4, BV4>), dim3(grid), dim3(nt), lds, s, a);
 }
 
 template <int T, bool AK, bool BKF>

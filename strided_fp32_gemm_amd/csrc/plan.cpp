@@ -139,34 +139,57 @@ int validate(const GemmArgs &a, std::string &why) {
 
 namespace {
 
-bool tile_fits(const Plan &p, const TileCfg &t) {
+bool tile_fits(const Plan &p, int bm, int bn) {
     // Buffer offsets are 32-bit from a per-workgroup base: the workgroup's
-    // slice of each operand has to lie within 2 GiB of that base.
+    // slice of each operand has to lie within 2 GiB of that base.  (A fetch
+    // may run up to two k slices past the end; those lanes are out of range
+    // and their offsets are never formed from valid rows.)
     int64_t kspan = p.k;
-    return fits_buffer(t.bm, p.sA_m, kspan, p.sA_k) && fits_buffer(kspan, p.sB_k, t.bn, p.sB_n) &&
-           fits_buffer(t.bm, p.sC_m, t.bn, p.sC_n);
+    return fits_buffer(bm, p.sA_m, kspan, p.sA_k) && fits_buffer(kspan, p.sB_k, bn, p.sB_n) &&
+           fits_buffer(bm, p.sC_m, bn, p.sC_n);
 }
 
-// Estimated cycles of the whole launch with tile t.  Tiles are spread over
-// the CUs; up to `occ` of them run concurrently on one CU (bounded by LDS and
-// by how many each CU receives).  One round of `occ` tiles costs their
-// matrix-core work at the tile's sustained rate, plus the epilogue traffic of
-// C (read and written when accumulating) at ~10 bytes per cycle per CU, plus
-// a fixed start-up latency.  Constants were fitted to tile sweeps on MI355X.
-double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
-    const double kLdsBytes = 160.0 * 1024.0, kStoreBytesPerCycle = 10.0, kStartCycles = 1000.0;
-    const double kFlopPerCuCycle = 256.0;
-    int64_t tm = (p.m + t.bm - 1) / t.bm, tn = (p.n + t.bn - 1) / t.bn;
+// Estimated cycles of a launch.  Tiles are spread over the CUs and up to
+// `occ` of them run concurrently on one CU (bounded by LDS or registers, and
+// by how many each CU receives).  A round of `occ` tiles costs the larger of
+// its matrix-core work at the tile's sustained rate and its operand reads
+// through L2 (~64 bytes per cycle per CU), plus the epilogue traffic of C
+// (read and written when accumulating, ~10 bytes per cycle per CU), plus
+// memory latency the round cannot hide.  Constants were fitted to tile
+// sweeps of the benchmark workloads on MI355X.
+struct CostShape {
+    int bm, bn, kstep;   // tile and k granularity
+    double occ_limit;    // tiles one CU can hold
+    double rate;
+    double latency;      // cycles per round
+};
+
+double launch_cost(const Plan &p, const CostShape &c, int num_cus) {
+    const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 10.0;
+    int64_t tm = (p.m + c.bm - 1) / c.bm, tn = (p.n + c.bn - 1) / c.bn;
     double tiles = double(p.batch) * double(tm) * double(tn);
     double cus = double(std::max(num_cus, 1));
-    double fit = std::max(1.0, std::min(8.0, std::floor(kLdsBytes / t.lds_bytes(p.a_kfast, p.b_kfast))));
-    double per_cu = std::ceil(tiles / cus);
-    double occ = std::min(fit, per_cu);
+    double occ = std::max(1.0, std::min(c.occ_limit, std::ceil(tiles / cus)));
     double rounds = std::ceil(tiles / (cus * occ));
-    double kpad = double((p.k + t.bk - 1) / t.bk) * t.bk;
-    double compute = occ * t.bm * t.bn * 2.0 * kpad / kFlopPerCuCycle / t.rate;
-    double epilogue = occ * t.bm * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
-    return rounds * (compute + epilogue + kStartCycles);
+    double kpad = double((p.k + c.kstep - 1) / c.kstep) * c.kstep;
+    double compute = occ * c.bm * c.bn * 2.0 * kpad / kFlopPerCuCycle / c.rate;
+    double operands = occ * double(c.bm + c.bn) * kpad * 4.0 / kOperandBytesPerCycle;
+    double epilogue = occ * c.bm * c.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
+    return rounds * (std::max(compute, operands) + epilogue + c.latency);
+}
+
+double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
+    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 830.0;
+    long long slices = (p.k + t.bk - 1) / t.bk;
+    double fit = std::max(1.0, std::min(8.0, std::floor(kLdsBytes / t.lds_bytes(p.a_kfast, p.b_kfast, slices))));
+    CostShape c{t.bm, t.bn, t.bk, fit, t.rate, kSliceLatency * std::min<double>(double(slices), 2.0)};
+    return launch_cost(p, c, num_cus);
+}
+
+double wave_cost(const Plan &p, const WaveCfg &t, int num_cus) {
+    const double kLatency = 2170.0;
+    CostShape c{t.bm, t.bn, 16, 4.0 * t.waves_per_simd, t.rate, kLatency};
+    return launch_cost(p, c, num_cus);
 }
 
 }  // namespace
@@ -212,42 +235,56 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
     p.vec_b = p.b_kfast ? vector_width(p.B, p.sB_k, p.k, p.sB_n, p.sB_b, p.batch)
                         : vector_width(p.B, p.sB_n, p.n, p.sB_k, p.sB_b, p.batch);
 
+    p.c_vec4 = p.sC_n == 1 && p.n % 4 == 0 && p.C % 16 == 0 && p.sC_m % 4 == 0 &&
+               (p.batch == 1 || p.sC_b % 4 == 0);
+
     const int64_t i32max = (int64_t(1) << 31) - 1;
     bool small_enough = p.m <= i32max && p.n <= i32max && p.k <= i32max && p.batch <= i32max;
 
-    // SGEMM_FORCE_TILE=<tile name> restricts the choice to that tile when it
-    // can serve the call (for tuning sweeps); otherwise it is ignored.
-    int forced = -1;
-    if (const char *env = std::getenv("SGEMM_FORCE_TILE")) {
+    // SGEMM_FORCE_TILE=<tile name> restricts the choice to that tile (of
+    // either family) when it can serve the call (for tuning sweeps);
+    // otherwise it is ignored.
+    const char *force = std::getenv("SGEMM_FORCE_TILE");
+    auto allowed = [&](const char *name) { return !force || std::strcmp(force, name) == 0; };
+    bool force_known = false;
+    if (force) {
         for (int t = 0; t < kNumTiles; ++t)
-            if (std::strcmp(env, kTiles[t].name) == 0) forced = t;
+            if (std::strcmp(force, kTiles[t].name) == 0 && tile_fits(p, kTiles[t].bm, kTiles[t].bn))
+                force_known = true;
+        for (int t = 0; t < kNumWaveTiles; ++t)
+            if (std::strcmp(force, kWaveTiles[t].name) == 0 && tile_fits(p, kWaveTiles[t].bm, kWaveTiles[t].bn))
+                force_known = true;
+        if (!force_known || family != Family::Auto) force = nullptr;
     }
-    if (forced >= 0 && !(small_enough && family == Family::Auto && tile_fits(p, kTiles[forced])))
-        forced = -1;
 
     int best = -1;
+    bool best_wave = false;
+    double best_cost = 0;
+    auto consider = [&](int t, bool wave, int bm, int bn, double cost) {
+        int64_t wgs = p.batch * ((p.m + bm - 1) / bm) * ((p.n + bn - 1) / bn);
+        if (wgs > i32max || !tile_fits(p, bm, bn)) return;
+        if (best < 0 || cost < best_cost) { best = t; best_wave = wave; best_cost = cost; }
+    };
     if (small_enough && family != Family::Generic) {
-        double best_cost = 0;
-        for (int t = 0; t < kNumTiles; ++t) {
-            if (forced >= 0 && t != forced) continue;
-            if (family == Family::Mfma && t == kWaveTile) continue;
-            if (family == Family::Wave && t != kWaveTile) continue;
-            if (!tile_fits(p, kTiles[t])) continue;
-            int64_t wgs = p.batch * ((p.m + kTiles[t].bm - 1) / kTiles[t].bm) *
-                          ((p.n + kTiles[t].bn - 1) / kTiles[t].bn);
-            if (wgs > i32max) continue;
-            double c = tile_cost(p, kTiles[t], num_cus);
-            if (best < 0 || c < best_cost) { best = t; best_cost = c; }
-        }
+        if (family != Family::Wave)
+            for (int t = 0; t < kNumTiles; ++t)
+                if (allowed(kTiles[t].name))
+                    consider(t, false, kTiles[t].bm, kTiles[t].bn, tile_cost(p, kTiles[t], num_cus));
+        if (family != Family::Mfma)
+            for (int t = 0; t < kNumWaveTiles; ++t)
+                if (allowed(kWaveTiles[t].name))
+                    consider(t, true, kWaveTiles[t].bm, kWaveTiles[t].bn, wave_cost(p, kWaveTiles[t], num_cus));
     }
     if (best >= 0) {
-        const TileCfg &t = kTiles[best];
-        p.family = (best == kWaveTile) ? Family::Wave : Family::Mfma;
+        int bm = best_wave ? kWaveTiles[best].bm : kTiles[best].bm;
+        int bn = best_wave ? kWaveTiles[best].bn : kTiles[best].bn;
+        const char *name = best_wave ? kWaveTiles[best].name : kTiles[best].name;
+        p.family = best_wave ? Family::Wave : Family::Mfma;
         p.tile = best;
-        p.tiles_m = (p.m + t.bm - 1) / t.bm;
-        p.tiles_n = (p.n + t.bn - 1) / t.bn;
+        p.tiles_m = (p.m + bm - 1) / bm;
+        p.tiles_n = (p.n + bn - 1) / bn;
         p.workgroups = p.batch * p.tiles_m * p.tiles_n;
-        p.kernel_name = std::string(p.family == Family::Wave ? "wave_" : "mfma_") + t.name +
+        p.kernel_name = std::string(best_wave ? "wave_" : "mfma_") + name +
                         (p.a_kfast ? "_ak" : "_am") + (p.b_kfast ? "_bk" : "_bn") +
                         (p.accumulate ? "_acc" : "");
     } else {

@@ -29,41 +29,67 @@ struct TileCfg {
     int bm, bn, bk;
     int wgm, wgn;
     int mf;
+    int pf;   // k slices of A and B in flight ahead of the one being multiplied (1 or 2)
     const char *name;
-    // Fraction of the matrix-core peak a CU sustains on this tile when k is
-    // long and the CU is full (measured on MI355X, 4 x 4096^3).
+    // Fraction of the matrix-core peak a CU sustains on this tile when it
+    // is full (fitted to tile sweeps on MI355X).
     double rate;
     constexpr int waves() const { return wgm * wgn; }
     // Padding of an LDS tile row: 4 floats on a k-fast tile; on an m- or
     // n-fast tile 8 (32-wide blocks) or 4 (16-wide blocks), which spreads the
     // lane groups that read different k rows over distinct banks.
     constexpr int pad(bool kfast) const { return kfast ? 4 : (mf == 32 ? 8 : 4); }
-    // LDS bytes of the kernel's carve-up: two buffers of the A and B tiles,
-    // each stored [slow][fast + pad].
-    constexpr int lds_bytes(bool a_kfast, bool b_kfast) const {
-        return 2 * 4 * ((a_kfast ? bm * (bk + pad(true)) : bk * (bm + pad(false))) +
-                        (b_kfast ? bn * (bk + pad(true)) : bk * (bn + pad(false))));
+    // LDS bytes of one buffer of the A and B tiles, each stored
+    // [slow][fast + pad]; the main loop double-buffers them unless the whole
+    // k extent fits one slice.
+    constexpr int buffer_lds_bytes(bool a_kfast, bool b_kfast) const {
+        return 4 * ((a_kfast ? bm * (bk + pad(true)) : bk * (bm + pad(false))) +
+                    (b_kfast ? bn * (bk + pad(true)) : bk * (bn + pad(false))));
+    }
+    // LDS bytes of the staged epilogue: every wavefront's (bm/wgm) x (bn/wgn)
+    // sub-tile of C, rows padded by 4 floats.
+    constexpr int epilogue_lds_bytes() const { return 4 * waves() * (bm / wgm) * (bn / wgn + 4); }
+    // LDS a launch allocates for k-slice count `slices` (dynamic shared memory).
+    constexpr int lds_bytes(bool a_kfast, bool b_kfast, long long slices) const {
+        int loop = buffer_lds_bytes(a_kfast, b_kfast) * (slices > 1 ? 2 : 1);
+        return loop > epilogue_lds_bytes() ? loop : epilogue_lds_bytes();
     }
 };
 
-// The MFMA tile table.  Kernel instantiations are generated from the same
-// indices (one translation unit per tile), so the order is part of the
-// contract between planner and kernels.  Index kWaveTile is the
-// one-wavefront tile of the WAVE family.
-constexpr int kNumTiles = 10;
-constexpr int kWaveTile = 5;
+// The LDS-tiled (MFMA family) tile table.  Kernel instantiations are
+// generated from the same indices (one translation unit per tile), so the
+// order is part of the contract between planner and kernels.
+constexpr int kNumTiles = 9;
 inline constexpr TileCfg kTiles[kNumTiles] = {
-    {128, 128, 32, 2, 2, 32, "t128x128", 0.83},
-    {128, 64, 32, 2, 2, 32, "t128x64", 0.80},
-    {64, 128, 32, 2, 2, 32, "t64x128", 0.81},
-    {64, 64, 32, 2, 2, 32, "t64x64", 0.77},
-    {256, 128, 32, 2, 2, 32, "t256x128", 0.74},
-    {32, 32, 32, 1, 1, 32, "wave32x32", 0.64},
-    {128, 160, 32, 4, 1, 32, "t128x160", 0.81},
-    {128, 80, 32, 4, 1, 16, "t128x80m16", 0.76},
-    {64, 176, 32, 4, 1, 16, "t64x176m16", 0.71},
-    {64, 64, 32, 2, 2, 16, "t64x64m16", 0.82},
+    {128, 128, 32, 2, 2, 32, 2, "t128x128", 0.82},
+    {128, 64, 32, 2, 2, 32, 2, "t128x64", 0.86},
+    {64, 128, 32, 2, 2, 32, 2, "t64x128", 0.88},
+    {64, 64, 32, 2, 2, 32, 2, "t64x64", 0.90},
+    {256, 128, 32, 2, 2, 32, 2, "t256x128", 0.78},
+    {128, 160, 32, 4, 1, 32, 2, "t128x160", 0.75},
+    {128, 80, 32, 4, 1, 16, 2, "t128x80m16", 0.71},
+    {64, 176, 32, 4, 1, 16, 2, "t64x176m16", 0.59},
+    {64, 64, 32, 2, 2, 16, 2, "t64x64m16", 0.94},
 };
+
+// One tile of the direct wavefront kernel (WAVE family): a single
+// wavefront owns bm x bn outputs in 16 x 16 matrix-core blocks and reads its
+// operands straight from global memory.
+struct WaveCfg {
+    int bm, bn;
+    int waves_per_simd;  // resident wavefronts per SIMD (register-limited, from the compiled code)
+    const char *name;
+    double rate;         // sustained fraction of peak on a full CU (fitted)
+};
+
+constexpr int kNumWaveTiles = 4;
+inline constexpr WaveCfg kWaveTiles[kNumWaveTiles] = {
+    {32, 32, 5, "w32x32", 0.58},
+    {32, 64, 3, "w32x64", 0.75},
+    {64, 32, 3, "w64x32", 0.75},
+    {64, 64, 2, "w64x64", 0.74},
+};
+
 
 // Everything a launch needs, in kernel terms: A is m x k, B is k x n, C is
 // m x n, each with a batch stride, and "fast" names the contiguous axis.
@@ -71,9 +97,10 @@ struct Plan {
     bool empty = false;        // batch*m*n == 0: nothing to enqueue
     bool transposed = false;   // solved as C^T = B^T A^T
     Family family = Family::Generic;
-    int tile = -1;             // index into kTiles (MFMA / WAVE)
+    int tile = -1;             // index into kTiles (MFMA) or kWaveTiles (WAVE)
     bool a_kfast = true, b_kfast = false;
     int vec_a = 1, vec_b = 1;
+    bool c_vec4 = false;       // C rows take 16-byte stores
     int64_t batch = 0, m = 0, n = 0, k = 0;
     float alpha = 1.0f;
     int accumulate = 0;

@@ -1,0 +1,190 @@
+// wave_kernel.hpp -- the direct wavefront kernel for gfx950.
+//
+// C[b,i,j] <- alpha * sum_p A[b,i,p] B[b,p,j] (+ C[b,i,j]) (StaleyNET "GPU
+// Implementation", section "The matrix product").
+//
+// One wavefront per workgroup owns a WM x WN output tile made of 16 x 16
+// matrix-core blocks (v_mfma_f32_16x16x4_f32).  Operand fragments go straight
+// from global memory into the registers the matrix core reads: no LDS and no
+// barriers, so a SIMD can hold many such wavefronts and interleave their
+// memory latency.  This is the path for products whose k is short or whose
+// tiles are few (attention scores, skinny and tiny shapes), where a
+// workgroup-wide LDS pipeline spends most of its life waiting for one slice.
+//
+//  - Fragment of a 16-row block for k group g (16 consecutive k): lane l
+//    holds rows l%16 and k = 16g + 4*(l/16) + q, q = 0..3.  A k-contiguous
+//    operand delivers those 4 values with one 16-byte load; otherwise 4
+//    element loads, each of which reads 16 consecutive lanes' worth of the
+//    contiguous axis.
+//  - The matrix core is fed B's fragment as its first operand and A's as its
+//    second, so it produces C^T blocks: register r of lane l is
+//    C[row l%16][column 4*(l/16) + r].  Each lane therefore owns 4 adjacent
+//    columns of one row and writes them with a single 16-byte store.
+//  - Two fragment sets alternate: group g+1 is in flight while group g is
+//    multiplied.  Loads past the end of k fail the buffer range check and
+//    read zeros, so the load sequence is the same in every iteration.
+//
+// Summation order per output is fixed (k groups in order), so results are
+// reproducible bit for bit.  No atomics.
+#pragma once
+
+#include "mfma_kernel.hpp"
+
+namespace sgemm {
+
+template <int W, bool AK, bool BKF, bool AV4, bool BV4>
+__global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
+    constexpr WaveCfg cfg = kWaveTiles[W];
+    constexpr int WM = cfg.bm, WN = cfg.bn;
+    constexpr int TM = WM / 16, TN = WN / 16;
+    static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile shape");
+
+    const int lane = threadIdx.x;
+    const int lr = lane & 15, lh = lane >> 4;
+    int b, tm, tn;
+    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, b, tm, tn);
+    const int i0 = tm * WM, j0 = tn * WN;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(p.A + (long long)b * p.sA_b + (long long)i0 * p.sA_m);
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(p.B + (long long)b * p.sB_b + (long long)j0 * p.sB_n);
+    const unsigned m_left = unsigned(p.m - i0), n_left = unsigned(p.n - j0);
+    const unsigned K = unsigned(p.k);
+    const unsigned sAm = unsigned(p.sA_m), sAk = unsigned(p.sA_k);
+    const unsigned sBk = unsigned(p.sB_k), sBn = unsigned(p.sB_n);
+
+    // Per-lane row (of A) and column (of B) offsets, fixed for the tile.
+    unsigned a_row[TM], b_col[TN];
+    bool a_ok[TM], b_ok[TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        const unsigned row = unsigned(a * 16 + lr);
+        a_ok[a] = row < m_left;
+        a_row[a] = row * sAm;
+    }
+#pragma unroll
+    for (int c = 0; c < TN; ++c) {
+        const unsigned col = unsigned(c * 16 + lr);
+        b_ok[c] = col < n_left;
+        b_col[c] = col * sBn;
+    }
+
+    auto fetch = [&](unsigned g, f32x4 (&fa)[TM], f32x4 (&fb)[TN]) {
+        const unsigned kb = 16u * g + 4u * unsigned(lh);
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            if constexpr (AK && AV4) {
+                fa[a] = load4(rA, (a_ok[a] && kb < K) ? (a_row[a] + kb) * 4u : kOutOfRange);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const unsigned k = kb + unsigned(q);
+                    fa[a][q] = load1(rA, (a_ok[a] && k < K) ? (a_row[a] + k * sAk) * 4u : kOutOfRange);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < TN; ++c) {
+            if constexpr (BKF && BV4) {
+                fb[c] = load4(rB, (b_ok[c] && kb < K) ? (b_col[c] + kb) * 4u : kOutOfRange);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const unsigned k = kb + unsigned(q);
+                    fb[c][q] = load1(rB, (b_ok[c] && k < K) ? (b_col[c] + k * sBk) * 4u : kOutOfRange);
+                }
+            }
+        }
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int c = 0; c < TN; ++c) acc[a][c] = f32x4{};
+
+    auto multiply = [&](const f32x4 (&fa)[TM], const f32x4 (&fb)[TN]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int c = 0; c < TN; ++c)
+                    acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[c][q], fa[a][q], acc[a][c], 0, 0, 0);
+    };
+
+    const int NG = (p.k + 15) / 16;
+    if (NG > 0) {
+        f32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+        fetch(0u, fa0, fb0);
+        fetch(1u, fa1, fb1);
+        for (int g = 0; g < NG; g += 2) {
+            multiply(fa0, fb0);
+            fetch(unsigned(g + 2), fa0, fb0);
+            if (g + 1 < NG) multiply(fa1, fb1);
+            fetch(unsigned(g + 3), fa1, fb1);
+        }
+    }
+
+    // Epilogue: lane (lr, lh) of block (a, c) holds C[a*16 + lr][c*16 + 4*lh + r].
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(p.C + (long long)b * p.sC_b + (long long)i0 * p.sC_m + (long long)j0 * p.sC_n);
+    const unsigned sCm = unsigned(p.sC_m), sCn = unsigned(p.sC_n);
+    const float alpha = p.alpha;
+    const bool accumulate = p.accumulate != 0;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+        const unsigned row = unsigned(a * 16 + lr);
+        const bool rv = row < m_left;
+#pragma unroll
+        for (int c = 0; c < TN; ++c) {
+            const unsigned col = unsigned(c * 16 + 4 * lh);
+            const f32x4 v = acc[a][c];
+            if (p.c_vec4) {
+                const unsigned off = (rv && col < n_left) ? (row * sCm + col) * 4u : kOutOfRange;
+                f32x4 o;
+                if (accumulate) {
+                    const f32x4 old = load4(rC, off);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(alpha, v[e], old[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = alpha * v[e];
+                }
+                store4(rC, off, o);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned ce = col + unsigned(e);
+                    const unsigned off = (rv && ce < n_left) ? (row * sCm + ce * sCn) * 4u : kOutOfRange;
+                    const float o = accumulate ? __builtin_fmaf(alpha, v[e], load1(rC, off)) : alpha * v[e];
+                    store1(rC, off, o);
+                }
+            }
+        }
+    }
+}
+
+template <int W, bool AK, bool BKF, bool AV4, bool BV4>
+void launch_wave(const MfmaArgs &a, unsigned grid, hipStream_t s) {
+    hipLaunchKernelGGL((sgemm_wave<W, AK, BKF, AV4, BV4>), dim3(grid), dim3(64), 0, s, a);
+}
+
+template <int W, bool AK, bool BKF>
+void fill_wave_layout(WaveTable &tab) {
+    tab.f[W][AK][BKF][0][0] = launch_wave<W, AK, BKF, false, false>;
+    tab.f[W][AK][BKF][0][1] = launch_wave<W, AK, BKF, false, true>;
+    tab.f[W][AK][BKF][1][0] = launch_wave<W, AK, BKF, true, false>;
+    tab.f[W][AK][BKF][1][1] = launch_wave<W, AK, BKF, true, true>;
+}
+
+template <int W>
+void fill_wave(WaveTable &tab) {
+    fill_wave_layout<W, false, false>(tab);
+    fill_wave_layout<W, false, true>(tab);
+    fill_wave_layout<W, true, false>(tab);
+    fill_wave_layout<W, true, true>(tab);
+}
+
+}  // namespace sgemm

@@ -177,8 +177,8 @@ def test_tile_boundaries(mnk, path):
         assert err_ratio(p, got, ref) <= TOL, (mnk, a_major, b_major)
 
 
-TILE_NAMES = ["t128x128", "t128x64", "t64x128", "t64x64", "t256x128", "wave32x32",
-              "t128x160", "t128x80m16", "t64x176m16", "t64x64m16"]
+TILE_NAMES = ["t128x128", "t128x64", "t64x128", "t64x64", "t256x128", "t128x160", "t128x80m16",
+              "t64x176m16", "t64x64m16", "w32x32", "w32x64", "w64x32", "w64x64"]
 
 
 @pytest.mark.parametrize("tile", TILE_NAMES)
@@ -187,7 +187,8 @@ def test_every_tile(tile, monkeypatch):
     shapes in all four transpose cases, with 16-byte loads (aligned shape)
     and element loads (padded lines), accumulating and not."""
     monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
-    shapes = [(2, 300, 260, 96, 0), (2, 150, 190, 70, 3), (1, 33, 520, 40, 1)]
+    shapes = [(2, 300, 260, 96, 0), (2, 150, 190, 70, 3), (1, 33, 520, 40, 1), (3, 70, 100, 200, 0),
+              (2, 64, 96, 64, 0)]
     for batch, m, n, k, pad in shapes:
         for a_major, b_major in LAYOUTS:
             for acc in (False, True):
