@@ -91,7 +91,10 @@ const MfmaTable &table() {
         fill_tile_6(tab);
         fill_tile_7(tab);
         fill_tile_8(tab);
-        static_assert(kNumTiles == 9, "launch table covers every tile");
+        fill_tile_9(tab);
+        fill_tile_10(tab);
+        fill_tile_11(tab);
+        static_assert(kNumTiles == 12, "launch table covers every tile");
         return tab;
     }();
     return t;

@@ -60,6 +60,9 @@ void fill_tile_5(MfmaTable &);
 void fill_tile_6(MfmaTable &);
 void fill_tile_7(MfmaTable &);
 void fill_tile_8(MfmaTable &);
+void fill_tile_9(MfmaTable &);
+void fill_tile_10(MfmaTable &);
+void fill_tile_11(MfmaTable &);
 void fill_wave_0(WaveTable &);
 void fill_wave_1(WaveTable &);
 void fill_wave_2(WaveTable &);

@@ -165,7 +165,7 @@ struct CostShape {
 };
 
 double launch_cost(const Plan &p, const CostShape &c, int num_cus) {
-    const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 10.0;
+    const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 10.8;
     int64_t tm = (p.m + c.bm - 1) / c.bm, tn = (p.n + c.bn - 1) / c.bn;
     double tiles = double(p.batch) * double(tm) * double(tn);
     double cus = double(std::max(num_cus, 1));
@@ -179,7 +179,7 @@ double launch_cost(const Plan &p, const CostShape &c, int num_cus) {
 }
 
 double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
-    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 830.0;
+    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 890.0;
     long long slices = (p.k + t.bk - 1) / t.bk;
     double fit = std::max(1.0, std::min(8.0, std::floor(kLdsBytes / t.lds_bytes(p.a_kfast, p.b_kfast, slices))));
     CostShape c{t.bm, t.bn, t.bk, fit, t.rate, kSliceLatency * std::min<double>(double(slices), 2.0)};
@@ -187,7 +187,7 @@ double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
 }
 
 double wave_cost(const Plan &p, const WaveCfg &t, int num_cus) {
-    const double kLatency = 2170.0;
+    const double kLatency = 3900.0;
     CostShape c{t.bm, t.bn, 16, 4.0 * t.waves_per_simd, t.rate, kLatency};
     return launch_cost(p, c, num_cus);
 }

@@ -59,17 +59,20 @@ struct TileCfg {
 // The LDS-tiled (MFMA family) tile table.  Kernel instantiations are
 // generated from the same indices (one translation unit per tile), so the
 // order is part of the contract between planner and kernels.
-constexpr int kNumTiles = 9;
+constexpr int kNumTiles = 12;
 inline constexpr TileCfg kTiles[kNumTiles] = {
-    {128, 128, 32, 2, 2, 32, 2, "t128x128", 0.82},
-    {128, 64, 32, 2, 2, 32, 2, "t128x64", 0.86},
-    {64, 128, 32, 2, 2, 32, 2, "t64x128", 0.88},
-    {64, 64, 32, 2, 2, 32, 2, "t64x64", 0.90},
-    {256, 128, 32, 2, 2, 32, 2, "t256x128", 0.78},
-    {128, 160, 32, 4, 1, 32, 2, "t128x160", 0.75},
+    {128, 128, 32, 2, 2, 32, 2, "t128x128", 0.83},
+    {128, 64, 32, 2, 2, 32, 2, "t128x64", 0.80},
+    {64, 128, 32, 2, 2, 32, 2, "t64x128", 0.84},
+    {64, 64, 32, 2, 2, 32, 2, "t64x64", 0.88},
+    {256, 128, 32, 2, 2, 32, 2, "t256x128", 0.77},
+    {128, 160, 32, 4, 1, 32, 2, "t128x160", 0.74},
     {128, 80, 32, 4, 1, 16, 2, "t128x80m16", 0.71},
     {64, 176, 32, 4, 1, 16, 2, "t64x176m16", 0.59},
-    {64, 64, 32, 2, 2, 16, 2, "t64x64m16", 0.94},
+    {64, 64, 32, 2, 2, 16, 2, "t64x64m16", 0.97},
+    {128, 128, 32, 2, 2, 16, 2, "t128x128m16", 0.83},
+    {128, 64, 32, 2, 2, 16, 2, "t128x64m16", 0.86},
+    {64, 128, 32, 2, 2, 16, 2, "t64x128m16", 0.96},
 };
 
 // One tile of the direct wavefront kernel (WAVE family): a single
@@ -84,10 +87,10 @@ struct WaveCfg {
 
 constexpr int kNumWaveTiles = 4;
 inline constexpr WaveCfg kWaveTiles[kNumWaveTiles] = {
-    {32, 32, 5, "w32x32", 0.58},
-    {32, 64, 3, "w32x64", 0.75},
-    {64, 32, 3, "w64x32", 0.75},
-    {64, 64, 2, "w64x64", 0.74},
+    {32, 32, 5, "w32x32", 0.55},
+    {32, 64, 3, "w32x64", 0.60},
+    {64, 32, 3, "w64x32", 0.60},
+    {64, 64, 2, "w64x64", 0.65},
 };
 
 
