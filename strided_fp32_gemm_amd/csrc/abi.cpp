@@ -129,7 +129,11 @@ int sgemm_plan_describe(int64_t batch, int64_t m, int64_t n, int64_t k, float al
     std::memset(info, 0, sizeof *info);
     info->path = plan.empty ? SGEMM_PATH_AUTO : static_cast<int>(plan.family);
     info->transposed = plan.transposed ? 1 : 0;
-    if (plan.tile >= 0 && plan.family == sgemm::Family::Wave) {
+    if (plan.tile >= 0 && plan.persist) {
+        const sgemm::PersistCfg &t = sgemm::kPersistTiles[plan.tile];
+        info->tile_m = t.bm; info->tile_n = t.bn; info->tile_k = t.kmax;
+        info->waves = t.waves();
+    } else if (plan.tile >= 0 && plan.family == sgemm::Family::Wave) {
         const sgemm::WaveCfg &t = sgemm::kWaveTiles[plan.tile];
         info->tile_m = t.bm; info->tile_n = t.bn; info->tile_k = 16;
         info->waves = 1;

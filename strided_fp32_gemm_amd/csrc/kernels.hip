@@ -113,6 +113,16 @@ const WaveTable &wave_table() {
     return t;
 }
 
+const PersistTable &persist_table() {
+    static const PersistTable t = [] {
+        PersistTable tab{};
+        fill_persist_0(tab);
+        static_assert(kNumPersistTiles == 1, "launch table covers every persistent tile");
+        return tab;
+    }();
+    return t;
+}
+
 }  // namespace
 
 int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
@@ -140,10 +150,15 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         a.sC_b = p.sC_b; a.sC_m = p.sC_m; a.sC_n = p.sC_n;
         a.m = int(p.m); a.n = int(p.n); a.k = int(p.k);
         a.tiles_m = int(p.tiles_m); a.tiles_n = int(p.tiles_n);
+        a.total_tiles = int(p.batch * p.tiles_m * p.tiles_n);
+        a.map = make_tile_map(p.batch, p.tiles_m, p.tiles_n);
         a.accumulate = p.accumulate;
         a.c_vec4 = p.c_vec4 ? 1 : 0;
         a.alpha = p.alpha;
-        if (p.family == Family::Wave)
+        if (p.persist)
+            persist_table().f[p.tile][p.a_kfast][p.b_kfast][p.accumulate != 0](
+                a, unsigned(p.workgroups), stream);
+        else if (p.family == Family::Wave)
             wave_table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4](
                 a, unsigned(p.workgroups), stream);
         else

@@ -21,6 +21,8 @@ struct MfmaArgs {
     long long sC_b, sC_m, sC_n;
     int m, n, k;
     int tiles_m, tiles_n;
+    int total_tiles;   // batch * tiles_m * tiles_n (the persistent kernel's loop bound)
+    TileMap map;       // tile id -> (batch, tile row, tile column)
     int accumulate;
     int c_vec4;   // C rows take 16-byte stores (n-contiguous, aligned, n % 4 == 0)
     float alpha;
@@ -51,6 +53,10 @@ struct MfmaTable {
 struct WaveTable {
     MfmaLaunch f[kNumWaveTiles][2][2][2][2];
 };
+// Persistent kernel: [tile][A k-fast][B k-fast][accumulate] (16-byte loads only).
+struct PersistTable {
+    MfmaLaunch f[kNumPersistTiles][2][2][2];
+};
 void fill_tile_0(MfmaTable &);
 void fill_tile_1(MfmaTable &);
 void fill_tile_2(MfmaTable &);
@@ -67,6 +73,7 @@ void fill_wave_0(WaveTable &);
 void fill_wave_1(WaveTable &);
 void fill_wave_2(WaveTable &);
 void fill_wave_3(WaveTable &);
+void fill_persist_0(PersistTable &);
 
 // Enqueues the plan on `stream`.  Returns kOk, or kErrHip with `why` set when
 // the runtime rejects the launch.

@@ -46,6 +46,7 @@
 namespace sgemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -129,28 +130,6 @@ struct TileLoader {
     }
 };
 
-// Workgroup -> (batch, tile row, tile column).  The hardware hands out
-// workgroup ids round-robin over the 8 XCDs; the remap gives each XCD a
-// contiguous range of tile ids, and tiles are ordered in groups of 8 tile
-// rows so that consecutive ids share B columns and nearby A rows.
-__device__ __forceinline__ void map_tile(int wg, int total, int tiles_m, int tiles_n, int &b,
-                                         int &tm, int &tn) {
-    if ((total & 7) == 0) {
-        const int per = total >> 3;
-        wg = (wg & 7) * per + (wg >> 3);
-    }
-    const int per_batch = tiles_m * tiles_n;
-    b = wg / per_batch;
-    const int t = wg - b * per_batch;
-    constexpr int kGroup = 8;
-    const int group = t / (kGroup * tiles_n);
-    const int first = group * kGroup;
-    const int gsz = min(tiles_m - first, kGroup);
-    const int in = t - group * kGroup * tiles_n;
-    tm = first + in % gsz;
-    tn = in / gsz;
-}
-
 // Matrix-core block of MF x MF outputs.
 //  MF = 32: v_mfma_f32_32x32x2_f32.  Lanes 0-31 feed the k = 0 operand and
 //    lanes 32-63 the k = 1 operand; accumulator register r of lane l holds
@@ -213,7 +192,7 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
 
     const int tid = threadIdx.x;
     int b, tm, tn;
-    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, b, tm, tn);
+    tile_coords(p.map, blockIdx.x, b, tm, tn);
     const int i0 = tm * BM, j0 = tn * BN;
 
     const __amdgpu_buffer_rsrc_t rA =
@@ -246,28 +225,74 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
     const int wm = wave / cfg.wgn, wn = wave % cfg.wgn;
     const int lr = lane % MF, lh = lane / MF;
 
-    // Fragments of k group g: af[a][q] = A[row lr of block a][KG*g + 4*lh + q].
+    // Which tile row / column block a (c) holds at local index i.  Blocks of
+    // an operand whose LDS tile is k-fast are contiguous (block a = rows
+    // 16a .. 16a+15).  For an m- (n-) fast tile of 16-wide blocks with 2 or 4
+    // blocks per wavefront the blocks interleave: block a holds rows TM*i + a,
+    // so the TM values a lane needs for one k sit side by side in LDS and
+    // come in one 8- or 16-byte read instead of TM single-float reads.
+    constexpr bool A_IL = !AK && MF == 16 && (TM == 2 || TM == 4);
+    constexpr bool B_IL = !BKF && MF == 16 && (TN == 2 || TN == 4);
+    auto arow_w = [&](int a, int i) { return A_IL ? TM * i + a : a * MF + i; };  // within the wavefront's rows
+    auto bcol_w = [&](int c, int j) { return B_IL ? TN * j + c : c * MF + j; };
+    auto arow = [&](int a, int i) { return wm * WM + arow_w(a, i); };
+    auto bcol = [&](int c, int j) { return wn * WN + bcol_w(c, j); };
+
+    // Fragments of k group g: af[a][q] = A[arow(a, lr)][KG*g + 4*lh + q],
+    // bf[c][q] = B[KG*g + 4*lh + q][bcol(c, lr)].
     auto read_frags = [&](const float *As, const float *Bs, int g, f32x4 (&af)[TM],
                           f32x4 (&bf)[TN]) {
         const int kq = KG * g + 4 * lh;
+        if constexpr (A_IL) {
 #pragma unroll
-        for (int a = 0; a < TM; ++a) {
-            const int mr = wm * WM + a * MF + lr;
-            if constexpr (AK) {
-                af[a] = *reinterpret_cast<const f32x4 *>(As + mr * A_LD + kq);
-            } else {
+            for (int q = 0; q < 4; ++q) {
+                const float *src = As + (kq + q) * A_LD + arow(0, lr);
+                if constexpr (TM == 4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(src);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) af[a][q] = As[(kq + q) * A_LD + mr];
+                    for (int a = 0; a < 4; ++a) af[a][q] = v[a];
+                } else {
+                    const f32x2 v = *reinterpret_cast<const f32x2 *>(src);
+                    af[0][q] = v[0];
+                    af[1][q] = v[1];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int a = 0; a < TM; ++a) {
+                const int mr = arow(a, lr);
+                if constexpr (AK) {
+                    af[a] = *reinterpret_cast<const f32x4 *>(As + mr * A_LD + kq);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) af[a][q] = As[(kq + q) * A_LD + mr];
+                }
             }
         }
+        if constexpr (B_IL) {
 #pragma unroll
-        for (int c = 0; c < TN; ++c) {
-            const int nc = wn * WN + c * MF + lr;
-            if constexpr (BKF) {
-                bf[c] = *reinterpret_cast<const f32x4 *>(Bs + nc * B_LD + kq);
-            } else {
+            for (int q = 0; q < 4; ++q) {
+                const float *src = Bs + (kq + q) * B_LD + bcol(0, lr);
+                if constexpr (TN == 4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(src);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) bf[c][q] = Bs[(kq + q) * B_LD + nc];
+                    for (int c = 0; c < 4; ++c) bf[c][q] = v[c];
+                } else {
+                    const f32x2 v = *reinterpret_cast<const f32x2 *>(src);
+                    bf[0][q] = v[0];
+                    bf[1][q] = v[1];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < TN; ++c) {
+                const int nc = bcol(c, lr);
+                if constexpr (BKF) {
+                    bf[c] = *reinterpret_cast<const f32x4 *>(Bs + nc * B_LD + kq);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) bf[c][q] = Bs[(kq + q) * B_LD + nc];
+                }
             }
         }
     };
@@ -279,8 +304,9 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
         for (int c = 0; c < TN; ++c) acc[a][c] = acc_t{};
 
     // One k slice from LDS buffer `buf`: fragments of group g+1 are read
-    // while the matrix-core instructions of group g run.
-    auto multiply = [&](int buf) {
+    // while the matrix-core instructions of group g run, and hook(g) slots
+    // other work of the step in after group g's products.
+    auto multiply = [&](int buf, auto &&hook) {
         const float *As = smem + buf * (A_SIZE + B_SIZE);
         const float *Bs = As + A_SIZE;
         f32x4 af[2][TM], bf[2][TN];
@@ -295,6 +321,8 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
 #pragma unroll
                     for (int c = 0; c < TN; ++c)
                         acc[a][c] = M::op(af[g & 1][a][q], bf[g & 1][c][q], acc[a][c]);
+            hook(g);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -302,40 +330,46 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
     if (KT > 0) {
         LoaderA la0;
         LoaderB lb0;
-        if constexpr (cfg.pf == 1) {
-            // Global -> registers one slice ahead, registers -> LDS at the end
-            // of each step, one barrier per step.
-            issue(la0, lb0, 0u);
-            put(la0, lb0, 0);
-            __syncthreads();
-            for (int kt = 0; kt < KT; ++kt) {
-                const bool more = kt + 1 < KT;
-                if (more) issue(la0, lb0, unsigned(kt + 1) * BK);
-                multiply(kt & 1);
-                if (more) put(la0, lb0, (kt + 1) & 1);
-                __syncthreads();
-            }
-        } else {
+        {
             // Two register sets: while slice kt is multiplied, slice kt+1 is
             // landing in one set and slice kt+2 is being requested into the
             // other, so two slices of loads are in flight per workgroup.  The
-            // loop is unrolled by two so the sets alternate statically.
+            // loop runs pairs of steps so the sets alternate statically, and
+            // nothing in its body is conditional: a step only conditional on
+            // the slice count would give the accumulators two incoming paths
+            // at the loop's end, and the compiler reconciles those with
+            // register copies on every iteration.  Requests past the end of k
+            // read zeros, and moving them to the idle buffer is harmless (the
+            // loop only runs when k has at least two slices, so both buffers
+            // exist).  An odd last slice, already in buffer 0, is multiplied
+            // after the loop; with a single slice that is the only step and
+            // buffer 1 is never touched.
             LoaderA la1;
             LoaderB lb1;
             issue(la0, lb0, 0u);
             issue(la1, lb1, unsigned(BK));
             put(la0, lb0, 0);
             __syncthreads();
-            auto step = [&](int kt, LoaderA &la_next, LoaderB &lb_next, LoaderA &la_free,
+            // A step requests slice kt+2 after the first k group's products
+            // and moves slice kt+1 (requested a step ago) into the other
+            // buffer after the last group's: that buffer was last read for
+            // slice kt-1, before the previous barrier.
+            auto step = [&](int kt, int buf, LoaderA &la_next, LoaderB &lb_next, LoaderA &la_free,
                             LoaderB &lb_free) {
-                issue(la_free, lb_free, unsigned(kt + 2) * BK);
-                multiply(kt & 1);
-                if (kt + 1 < KT) put(la_next, lb_next, (kt + 1) & 1);
+                multiply(buf, [&](int g) {
+                    if (g == 0) issue(la_free, lb_free, unsigned(kt + 2) * BK);
+                    if (g == G - 1) put(la_next, lb_next, buf ^ 1);
+                });
                 __syncthreads();
             };
-            for (int kt = 0; kt < KT; kt += 2) {
-                step(kt, la1, lb1, la0, lb0);
-                if (kt + 1 < KT) step(kt + 1, la0, lb0, la1, lb1);
+            int kt = 0;
+            for (; kt + 1 < KT; kt += 2) {
+                step(kt, 0, la1, lb1, la0, lb0);
+                step(kt + 1, 1, la0, lb0, la1, lb1);
+            }
+            if (kt < KT) {
+                multiply(0, [](int) {});
+                __syncthreads();
             }
         }
     }
@@ -353,13 +387,23 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
         // region (the main loop's buffers are free after its last barrier),
         // then stores whole rows with 16-byte stores, WN/4 lanes per row.
         float *stage = smem + wave * (WM * E_LD);
+        if constexpr (B_IL && TN == 4) {
+            // The 4 blocks of a row hold 4 adjacent columns: one 16-byte write.
 #pragma unroll
-        for (int a = 0; a < TM; ++a)
-#pragma unroll
-            for (int c = 0; c < TN; ++c)
+            for (int a = 0; a < TM; ++a)
 #pragma unroll
                 for (int r = 0; r < R; ++r)
-                    stage[(a * MF + M::row(r, lh)) * E_LD + c * MF + lr] = acc[a][c][r];
+                    *reinterpret_cast<f32x4 *>(stage + arow_w(a, M::row(r, lh)) * E_LD + bcol_w(0, lr)) =
+                        f32x4{acc[a][0][r], acc[a][1][r], acc[a][2][r], acc[a][3][r]};
+        } else {
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int c = 0; c < TN; ++c)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        stage[arow_w(a, M::row(r, lh)) * E_LD + bcol_w(c, lr)] = acc[a][c][r];
+        }
         __syncthreads();
         constexpr int kQuads = WM * WN / 4;
         constexpr int kPerRow = WN / 4;
@@ -390,11 +434,11 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
     for (int a = 0; a < TM; ++a) {
 #pragma unroll
         for (int c = 0; c < TN; ++c) {
-            const unsigned col = unsigned(wn * WN + c * MF + lr);
+            const unsigned col = unsigned(bcol(c, lr));
             unsigned off[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const unsigned row = unsigned(wm * WM + a * MF + M::row(r, lh));
+                const unsigned row = unsigned(arow(a, M::row(r, lh)));
                 off[r] = (row < m_left && col < n_left) ? (row * sCm + col * sCn) * 4u : kOutOfRange;
             }
             if (accumulate) {

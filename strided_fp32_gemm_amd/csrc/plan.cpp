@@ -165,7 +165,7 @@ struct CostShape {
 };
 
 double launch_cost(const Plan &p, const CostShape &c, int num_cus) {
-    const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 10.8;
+    const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 11.0;
     int64_t tm = (p.m + c.bm - 1) / c.bm, tn = (p.n + c.bn - 1) / c.bn;
     double tiles = double(p.batch) * double(tm) * double(tn);
     double cus = double(std::max(num_cus, 1));
@@ -179,7 +179,7 @@ double launch_cost(const Plan &p, const CostShape &c, int num_cus) {
 }
 
 double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
-    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 890.0;
+    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 368.0;
     long long slices = (p.k + t.bk - 1) / t.bk;
     double fit = std::max(1.0, std::min(8.0, std::floor(kLdsBytes / t.lds_bytes(p.a_kfast, p.b_kfast, slices))));
     CostShape c{t.bm, t.bn, t.bk, fit, t.rate, kSliceLatency * std::min<double>(double(slices), 2.0)};
@@ -187,9 +187,49 @@ double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
 }
 
 double wave_cost(const Plan &p, const WaveCfg &t, int num_cus) {
-    const double kLatency = 3900.0;
+    const double kLatency = 2720.0;
     CostShape c{t.bm, t.bn, 16, 4.0 * t.waves_per_simd, t.rate, kLatency};
     return launch_cost(p, c, num_cus);
+}
+
+// Workgroups of a persistent launch: as many as the CUs hold at once (LDS
+// bound, two slabs each), at most one per tile.  When the tile count is a
+// multiple of 8 the grid is too, so that every workgroup's tiles stay on the
+// XCD its id maps to.  SGEMM_PERSIST_WGS=<n> caps the grid (tuning sweeps,
+// and tests that need many tiles per workgroup on small shapes).
+int64_t persist_grid(const Plan &p, const PersistCfg &t, int num_cus, int64_t tiles) {
+    const int lds = 2 * t.slab_bytes(p.a_kfast, p.b_kfast);
+    int64_t per_cu = std::max(1, std::min(8, int(160 * 1024 / lds)));
+    int64_t grid = std::min<int64_t>(tiles, int64_t(std::max(num_cus, 1)) * per_cu);
+    if (const char *cap = std::getenv("SGEMM_PERSIST_WGS")) {
+        long long v = std::atoll(cap);
+        if (v > 0) grid = std::min<int64_t>(grid, v);
+    }
+    if (tiles % 8 == 0 && grid >= 8) grid -= grid % 8;
+    return grid;
+}
+
+// Persistent launch: each CU holds grid/num_cus workgroups, and a workgroup's
+// tiles follow one another with the next operands already loaded, so per
+// tile the CU pays the larger of its matrix-core work, operand reads and C
+// traffic rather than their sum; the pipeline's fill is paid once.
+double persist_cost(const Plan &p, const PersistCfg &t, int num_cus, int64_t grid) {
+    const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 11.0;
+    const double kFill = 5350.0;
+    int64_t tm = (p.m + t.bm - 1) / t.bm, tn = (p.n + t.bn - 1) / t.bn;
+    double tiles = double(p.batch) * double(tm) * double(tn);
+    double cus = double(std::max(num_cus, 1));
+    double occ = std::max(1.0, std::ceil(double(grid) / cus));
+    double iters = std::ceil(tiles / double(grid));
+    double kpad = double((p.k + 15) / 16) * 16.0;
+    double compute = occ * t.bm * t.bn * 2.0 * kpad / kFlopPerCuCycle / t.rate;
+    double operands = occ * double(t.bm + t.bn) * kpad * 4.0 / kOperandBytesPerCycle;
+    double epilogue = occ * t.bm * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
+    return iters * std::max({compute, operands, epilogue}) + kFill;
+}
+
+bool persist_serves(const Plan &p, const PersistCfg &t) {
+    return p.vec_a == 4 && p.vec_b == 4 && p.c_vec4 && p.k >= 1 && p.k <= t.kmax;
 }
 
 }  // namespace
@@ -254,37 +294,53 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         for (int t = 0; t < kNumWaveTiles; ++t)
             if (std::strcmp(force, kWaveTiles[t].name) == 0 && tile_fits(p, kWaveTiles[t].bm, kWaveTiles[t].bn))
                 force_known = true;
+        for (int t = 0; t < kNumPersistTiles; ++t)
+            if (std::strcmp(force, kPersistTiles[t].name) == 0 && persist_serves(p, kPersistTiles[t]) &&
+                tile_fits(p, kPersistTiles[t].bm, kPersistTiles[t].bn))
+                force_known = true;
         if (!force_known || family != Family::Auto) force = nullptr;
     }
 
     int best = -1;
-    bool best_wave = false;
+    bool best_wave = false, best_persist = false;
     double best_cost = 0;
-    auto consider = [&](int t, bool wave, int bm, int bn, double cost) {
+    auto consider = [&](int t, bool wave, bool persist, int bm, int bn, double cost) {
         int64_t wgs = p.batch * ((p.m + bm - 1) / bm) * ((p.n + bn - 1) / bn);
         if (wgs > i32max || !tile_fits(p, bm, bn)) return;
-        if (best < 0 || cost < best_cost) { best = t; best_wave = wave; best_cost = cost; }
+        if (best < 0 || cost < best_cost) {
+            best = t; best_wave = wave; best_persist = persist; best_cost = cost;
+        }
     };
     if (small_enough && family != Family::Generic) {
-        if (family != Family::Wave)
+        if (family != Family::Wave) {
             for (int t = 0; t < kNumTiles; ++t)
                 if (allowed(kTiles[t].name))
-                    consider(t, false, kTiles[t].bm, kTiles[t].bn, tile_cost(p, kTiles[t], num_cus));
+                    consider(t, false, false, kTiles[t].bm, kTiles[t].bn, tile_cost(p, kTiles[t], num_cus));
+            for (int t = 0; t < kNumPersistTiles; ++t) {
+                const PersistCfg &c = kPersistTiles[t];
+                if (!allowed(c.name) || !persist_serves(p, c)) continue;
+                int64_t tiles = p.batch * ((p.m + c.bm - 1) / c.bm) * ((p.n + c.bn - 1) / c.bn);
+                consider(t, false, true, c.bm, c.bn, persist_cost(p, c, num_cus, persist_grid(p, c, num_cus, tiles)));
+            }
+        }
         if (family != Family::Mfma)
             for (int t = 0; t < kNumWaveTiles; ++t)
                 if (allowed(kWaveTiles[t].name))
-                    consider(t, true, kWaveTiles[t].bm, kWaveTiles[t].bn, wave_cost(p, kWaveTiles[t], num_cus));
+                    consider(t, true, false, kWaveTiles[t].bm, kWaveTiles[t].bn, wave_cost(p, kWaveTiles[t], num_cus));
     }
     if (best >= 0) {
-        int bm = best_wave ? kWaveTiles[best].bm : kTiles[best].bm;
-        int bn = best_wave ? kWaveTiles[best].bn : kTiles[best].bn;
-        const char *name = best_wave ? kWaveTiles[best].name : kTiles[best].name;
+        int bm = best_wave ? kWaveTiles[best].bm : best_persist ? kPersistTiles[best].bm : kTiles[best].bm;
+        int bn = best_wave ? kWaveTiles[best].bn : best_persist ? kPersistTiles[best].bn : kTiles[best].bn;
+        const char *name = best_wave ? kWaveTiles[best].name
+                                     : best_persist ? kPersistTiles[best].name : kTiles[best].name;
         p.family = best_wave ? Family::Wave : Family::Mfma;
         p.tile = best;
+        p.persist = best_persist;
         p.tiles_m = (p.m + bm - 1) / bm;
         p.tiles_n = (p.n + bn - 1) / bn;
         p.workgroups = p.batch * p.tiles_m * p.tiles_n;
-        p.kernel_name = std::string(best_wave ? "wave_" : "mfma_") + name +
+        if (best_persist) p.workgroups = persist_grid(p, kPersistTiles[best], num_cus, p.workgroups);
+        p.kernel_name = std::string(best_wave ? "wave_" : best_persist ? "persist_" : "mfma_") + name +
                         (p.a_kfast ? "_ak" : "_am") + (p.b_kfast ? "_bk" : "_bn") +
                         (p.accumulate ? "_acc" : "");
     } else {

@@ -29,7 +29,6 @@ struct TileCfg {
     int bm, bn, bk;
     int wgm, wgn;
     int mf;
-    int pf;   // k slices of A and B in flight ahead of the one being multiplied (1 or 2)
     const char *name;
     // Fraction of the matrix-core peak a CU sustains on this tile when it
     // is full (fitted to tile sweeps on MI355X).
@@ -61,18 +60,18 @@ struct TileCfg {
 // order is part of the contract between planner and kernels.
 constexpr int kNumTiles = 12;
 inline constexpr TileCfg kTiles[kNumTiles] = {
-    {128, 128, 32, 2, 2, 32, 2, "t128x128", 0.83},
-    {128, 64, 32, 2, 2, 32, 2, "t128x64", 0.80},
-    {64, 128, 32, 2, 2, 32, 2, "t64x128", 0.84},
-    {64, 64, 32, 2, 2, 32, 2, "t64x64", 0.88},
-    {256, 128, 32, 2, 2, 32, 2, "t256x128", 0.77},
-    {128, 160, 32, 4, 1, 32, 2, "t128x160", 0.74},
-    {128, 80, 32, 4, 1, 16, 2, "t128x80m16", 0.71},
-    {64, 176, 32, 4, 1, 16, 2, "t64x176m16", 0.59},
-    {64, 64, 32, 2, 2, 16, 2, "t64x64m16", 0.97},
-    {128, 128, 32, 2, 2, 16, 2, "t128x128m16", 0.83},
-    {128, 64, 32, 2, 2, 16, 2, "t128x64m16", 0.86},
-    {64, 128, 32, 2, 2, 16, 2, "t64x128m16", 0.96},
+    {128, 128, 32, 2, 2, 32, "t128x128", 0.87},
+    {128, 64, 32, 2, 2, 32, "t128x64", 0.89},
+    {64, 128, 32, 2, 2, 32, "t64x128", 0.89},
+    {64, 64, 32, 2, 2, 32, "t64x64", 0.94},
+    {256, 128, 32, 2, 2, 32, "t256x128", 0.78},
+    {128, 160, 32, 4, 1, 32, "t128x160", 0.74},
+    {128, 80, 32, 4, 1, 16, "t128x80m16", 0.77},
+    {64, 176, 32, 4, 1, 16, "t64x176m16", 0.75},
+    {64, 64, 32, 2, 2, 16, "t64x64m16", 0.95},
+    {128, 128, 32, 2, 2, 16, "t128x128m16", 0.95},
+    {128, 64, 32, 2, 2, 16, "t128x64m16", 0.88},
+    {64, 128, 32, 2, 2, 16, "t64x128m16", 0.88},
 };
 
 // One tile of the direct wavefront kernel (WAVE family): a single
@@ -87,12 +86,94 @@ struct WaveCfg {
 
 constexpr int kNumWaveTiles = 4;
 inline constexpr WaveCfg kWaveTiles[kNumWaveTiles] = {
-    {32, 32, 5, "w32x32", 0.55},
-    {32, 64, 3, "w32x64", 0.60},
-    {64, 32, 3, "w64x32", 0.60},
-    {64, 64, 2, "w64x64", 0.65},
+    {32, 32, 5, "w32x32", 0.58},
+    {32, 64, 3, "w32x64", 0.75},
+    {64, 32, 3, "w64x32", 0.76},
+    {64, 64, 2, "w64x64", 0.77},
 };
 
+// One tile of the persistent short-k kernel (MFMA family): a fixed grid of
+// wgm x wgn-wavefront workgroups loops over bm x bn output tiles whose whole
+// k extent (k <= kmax) sits in one LDS slab; two slabs alternate.  Served
+// only with 16-byte loads of both operands and 16-byte C rows.
+struct PersistCfg {
+    int bm, bn, kmax;
+    int wgm, wgn;
+    const char *name;
+    double rate;   // sustained fraction of the matrix-core peak (fitted)
+    constexpr int waves() const { return wgm * wgn; }
+    // LDS bytes of one slab: A and B stored [slow][fast + 4].
+    constexpr int slab_bytes(bool a_kfast, bool b_kfast) const {
+        return 4 * ((a_kfast ? bm * (kmax + 4) : kmax * (bm + 4)) +
+                    (b_kfast ? bn * (kmax + 4) : kmax * (bn + 4)));
+    }
+};
+
+constexpr int kNumPersistTiles = 1;
+inline constexpr PersistCfg kPersistTiles[kNumPersistTiles] = {
+    {64, 64, 64, 2, 2, "p64x64k64", 0.59},
+};
+
+// Division by a launch constant as a multiply and a shift (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// for 1 <= d < 2^31 take l = ceil(log2 d) and m = ceil(2^(31+l) / d), which
+// lies in [2^31, 2^32).  For 0 <= n < 2^31, n*m / 2^(31+l) exceeds n/d by
+// less than n / 2^(31+l) < 2^-l <= 1/d, which never reaches the next
+// integer, so (n*m) >> (31+l) == floor(n/d).  On the GPU this is a 64-bit
+// scalar product and a shift instead of a ~40-instruction division.
+struct Divisor {
+    uint32_t d, m, s;
+};
+
+constexpr Divisor make_divisor(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t num = uint64_t(1) << (31 + l);
+    return Divisor{d, uint32_t((num + d - 1) / d), 31 + l};
+}
+
+constexpr uint32_t divide(uint32_t n, Divisor v) { return uint32_t((uint64_t(n) * v.m) >> v.s); }
+
+// Order in which a launch visits its batch * tiles_m * tiles_n output tiles.
+// Workgroup ids reach the 8 XCDs round-robin; when the tile count is a
+// multiple of 8, id w is remapped to (w % 8) * (count / 8) + w / 8, so that
+// each XCD (and its L2) works through one contiguous range.  Within a batch
+// entry, tiles go in groups of kGroupRows tile rows, column by column inside
+// a group, so neighbouring ids share B columns and nearby A rows.
+constexpr int kGroupRows = 8;
+
+struct TileMap {
+    int tiles_m, tiles_n;
+    int per_xcd;          // count / 8 if count % 8 == 0, else 0 (no remap)
+    Divisor per_batch;    // tiles_m * tiles_n
+    Divisor group;        // kGroupRows * tiles_n
+    Divisor last_rows;    // tile rows of the last group (tiles_m % kGroupRows, or kGroupRows)
+};
+
+constexpr TileMap make_tile_map(int64_t batch, int64_t tiles_m, int64_t tiles_n) {
+    const int64_t count = batch * tiles_m * tiles_n;
+    const int64_t rem = tiles_m % kGroupRows;
+    return TileMap{int(tiles_m), int(tiles_n), count % 8 == 0 ? int(count / 8) : 0,
+                   make_divisor(uint32_t(tiles_m * tiles_n)), make_divisor(uint32_t(kGroupRows * tiles_n)),
+                   make_divisor(uint32_t(rem ? rem : kGroupRows))};
+}
+
+// Tile id w (0 <= w < count) -> batch entry b, tile row tm, tile column tn.
+constexpr void tile_coords(const TileMap &map, int w, int &b, int &tm, int &tn) {
+    if (map.per_xcd) w = (w & 7) * map.per_xcd + (w >> 3);
+    const uint32_t uw = uint32_t(w);
+    const uint32_t ub = divide(uw, map.per_batch);
+    const uint32_t t = uw - ub * map.per_batch.d;
+    const uint32_t group = divide(t, map.group);
+    const uint32_t in = t - group * map.group.d;
+    const int first = int(group) * kGroupRows;
+    const bool full = first + kGroupRows <= map.tiles_m;
+    const uint32_t col = full ? in / uint32_t(kGroupRows) : divide(in, map.last_rows);
+    const uint32_t row = in - col * (full ? uint32_t(kGroupRows) : map.last_rows.d);
+    b = int(ub);
+    tm = first + int(row);
+    tn = int(col);
+}
 
 // Everything a launch needs, in kernel terms: A is m x k, B is k x n, C is
 // m x n, each with a batch stride, and "fast" names the contiguous axis.
@@ -100,7 +181,8 @@ struct Plan {
     bool empty = false;        // batch*m*n == 0: nothing to enqueue
     bool transposed = false;   // solved as C^T = B^T A^T
     Family family = Family::Generic;
-    int tile = -1;             // index into kTiles (MFMA) or kWaveTiles (WAVE)
+    int tile = -1;             // index into kTiles / kPersistTiles (MFMA) or kWaveTiles (WAVE)
+    bool persist = false;      // MFMA family, persistent short-k kernel (tile indexes kPersistTiles)
     bool a_kfast = true, b_kfast = false;
     int vec_a = 1, vec_b = 1;
     bool c_vec4 = false;       // C rows take 16-byte stores
@@ -111,7 +193,7 @@ struct Plan {
     int64_t sA_b = 0, sA_m = 0, sA_k = 0;
     int64_t sB_b = 0, sB_k = 0, sB_n = 0;
     int64_t sC_b = 0, sC_m = 0, sC_n = 0;
-    int64_t tiles_m = 0, tiles_n = 0, workgroups = 0;
+    int64_t tiles_m = 0, tiles_n = 0, workgroups = 0;  // workgroups < tiles for the persistent kernel
     std::string kernel_name;
 };
 

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
     const int lane = threadIdx.x;
     const int lr = lane & 15, lh = lane >> 4;
     int b, tm, tn;
-    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, b, tm, tn);
+    tile_coords(p.map, blockIdx.x, b, tm, tn);
     const int i0 = tm * WM, j0 = tn * WN;
 
     const __amdgpu_buffer_rsrc_t rA =
@@ -114,17 +114,23 @@ __global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
                     acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[c][q], fa[a][q], acc[a][c], 0, 0, 0);
     };
 
+    // Pairs of groups per iteration with nothing conditional inside (a
+    // multiply conditional on the group count would give the accumulators
+    // two incoming paths and cost register copies every iteration); an odd
+    // last group is multiplied after the loop.
     const int NG = (p.k + 15) / 16;
     if (NG > 0) {
         f32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
         fetch(0u, fa0, fb0);
         fetch(1u, fa1, fb1);
-        for (int g = 0; g < NG; g += 2) {
+        int g = 0;
+        for (; g + 1 < NG; g += 2) {
             multiply(fa0, fb0);
             fetch(unsigned(g + 2), fa0, fb0);
-            if (g + 1 < NG) multiply(fa1, fb1);
+            multiply(fa1, fb1);
             fetch(unsigned(g + 3), fa1, fb1);
         }
+        if (g < NG) multiply(fa0, fb0);
     }
 
     // Epilogue: lane (lr, lh) of block (a, c) holds C[a*16 + lr][c*16 + 4*lh + r].

@@ -169,3 +169,27 @@ def test_tile_map_example_shape_is_planned():
         assert p["workgroups"] == 1
     # The pages' own 4 x 4 decomposition of that shape: 2 x 3 tiles.
     assert (-(-rows // 4), -(-cols // 4)) == (int(g["tile_rows"]), int(g["tile_columns"]))
+
+
+def test_persistent_tile_serves_short_k_only(monkeypatch):
+    """The persistent short-k kernel takes the attention-score shape (k = 64,
+    16-byte loads and stores) with one workgroup per LDS-resident pair of
+    slabs on each CU, and is never used where it cannot serve: k above its
+    slab depth, element loads, or C rows without 16-byte stores."""
+    qk = _cfg_plan("attn_qk")
+    assert qk["kernel"].startswith("persist_p64x64k64"), qk
+    assert qk["tile_k"] == 64 and qk["workgroups"] == 2 * 256
+    monkeypatch.setenv("SGEMM_FORCE_TILE", "p64x64k64")
+    ok = plan(120, 512, 512, 64, (512 * 64, 64, 1), (512 * 64, 1, 64), (512 * 512, 512, 1))
+    assert ok["kernel"].startswith("persist_"), ok
+    deep = plan(120, 512, 512, 68, (512 * 68, 68, 1), (512 * 68, 1, 68), (512 * 512, 512, 1))
+    assert not deep["kernel"].startswith("persist_"), deep
+    ragged = plan(120, 512, 512, 62, (512 * 62, 62, 1), (512 * 62, 1, 62), (512 * 512, 512, 1))
+    assert not ragged["kernel"].startswith("persist_"), ragged
+    odd_c = plan(120, 512, 510, 64, (512 * 64, 64, 1), (510 * 64, 1, 64), (512 * 510, 510, 1))
+    assert not odd_c["kernel"].startswith("persist_"), odd_c
+    # A grid cap (for sweeps and tests) bounds the workgroups, never above the tiles.
+    monkeypatch.setenv("SGEMM_PERSIST_WGS", "7")
+    assert plan(120, 512, 512, 64, (512 * 64, 64, 1), (512 * 64, 1, 64), (512 * 512, 512, 1))["workgroups"] == 7
+    monkeypatch.setenv("SGEMM_PERSIST_WGS", "100000")
+    assert plan(1, 64, 128, 64, (0, 64, 1), (0, 1, 64), (0, 128, 1))["workgroups"] == 2

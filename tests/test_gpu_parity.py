@@ -203,6 +203,28 @@ def test_every_tile(tile, monkeypatch):
                 assert e <= TOL, (tile, m, n, k, pad, a_major, b_major, acc, e)
 
 
+@pytest.mark.parametrize("wgs", [None, "8", "7", "1"])
+def test_persistent_tile(wgs, monkeypatch):
+    """The persistent short-k kernel, forced, on ragged shapes with k <= 64
+    in all four transpose cases, accumulating and not; a capped grid makes
+    each workgroup loop over many tiles (odd and even counts)."""
+    monkeypatch.setenv("SGEMM_FORCE_TILE", "p64x64k64")
+    if wgs:
+        monkeypatch.setenv("SGEMM_PERSIST_WGS", wgs)
+    shapes = [(3, 300, 260, 64), (5, 132, 68, 40), (2, 64, 64, 4), (9, 128, 192, 60), (1, 4, 8, 12)]
+    for batch, m, n, k in shapes:
+        for a_major, b_major in LAYOUTS:
+            for acc in (False, True):
+                p = wl.random_problem(m * 7 + n + k, batch, m, n, k, a_major=a_major,
+                                      b_major=b_major, dist="normal", alpha=-1.25,
+                                      accumulate=acc)
+                info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
+                assert info["kernel"].startswith("persist_p64x64k64"), info
+                got, ref = out(p, gpu_call(p)), out(p, oracle_call(p))
+                e = err_ratio(p, got, ref)
+                assert e <= TOL, (wgs, m, n, k, a_major, b_major, acc, e)
+
+
 def test_column_major_output():
     """C stored column-major is served as C^T = B^T A^T."""
     for a_major, b_major in LAYOUTS:
