@@ -40,9 +40,9 @@ if ROOT not in sys.path:
 PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
 DEFAULT_WORKLOAD = "square4096_acc"
-KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/mfma_kernel.hpp", "strided_fp32_gemm_amd/csrc/kernels.hip",
-                  "strided_fp32_gemm_amd/csrc/plan.hpp",
-                  "strided_fp32_gemm_amd/csrc/plan.cpp"]
+KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/" + f for f in (
+    "mfma_kernel.hpp", "persist_kernel.hpp", "wave_kernel.hpp", "kernels.hpp", "kernels.hip",
+    "plan.hpp", "plan.cpp")]
 
 
 def kernel_sources_sha256() -> str:
