@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
 SOURCES = ["plan.cpp", "abi.cpp", "kernels.hip"] + [f"mfma_t{t}.hip" for t in range(12)] + \
-    [f"wave_w{t}.hip" for t in range(4)] + ["persist_p0.hip"]
+    [f"wave_w{t}.hip" for t in range(4)] + [f"persist_p{t}.hip" for t in range(3)]
 
 
 def _hipcc() -> str:

@@ -117,7 +117,9 @@ const PersistTable &persist_table() {
     static const PersistTable t = [] {
         PersistTable tab{};
         fill_persist_0(tab);
-        static_assert(kNumPersistTiles == 1, "launch table covers every persistent tile");
+        fill_persist_1(tab);
+        fill_persist_2(tab);
+        static_assert(kNumPersistTiles == 3, "launch table covers every persistent tile");
         return tab;
     }();
     return t;

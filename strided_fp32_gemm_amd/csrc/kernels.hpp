@@ -74,6 +74,8 @@ void fill_wave_1(WaveTable &);
 void fill_wave_2(WaveTable &);
 void fill_wave_3(WaveTable &);
 void fill_persist_0(PersistTable &);
+void fill_persist_1(PersistTable &);
+void fill_persist_2(PersistTable &);
 
 // Enqueues the plan on `stream`.  Returns kOk, or kErrHip with `why` set when
 // the runtime rejects the launch.

@@ -109,9 +109,11 @@ struct PersistCfg {
     }
 };
 
-constexpr int kNumPersistTiles = 1;
+constexpr int kNumPersistTiles = 3;
 inline constexpr PersistCfg kPersistTiles[kNumPersistTiles] = {
     {64, 64, 64, 2, 2, "p64x64k64", 0.59},
+    {128, 64, 64, 4, 2, "p128x64k64", 0.59},
+    {64, 128, 64, 2, 4, "p64x128k64", 0.59},
 };
 
 // Division by a launch constant as a multiply and a shift (Granlund and

@@ -32,8 +32,13 @@ import numpy as np
 
 ROOT_SEED = 2024
 
-# Workload names in the order they are spawned from the root seed.
-WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc")
+# Benchmark workloads.
+WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
+             "linear_bwd_dx", "linear_bwd_dw", "linear_xT")
+# Children of the root seed, in spawn order (the two halves of the linear
+# layer's backward pass share one draw of dy, W and x).
+SEED_NAMES = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
+              "linear_bwd", "linear_xT")
 
 
 @dataclasses.dataclass
@@ -84,8 +89,8 @@ class Problem:
 
 
 def _children(name: str):
-    idx = WORKLOADS.index(name)
-    return np.random.SeedSequence(ROOT_SEED).spawn(len(WORKLOADS))[idx]
+    idx = SEED_NAMES.index(name)
+    return np.random.SeedSequence(ROOT_SEED).spawn(len(SEED_NAMES))[idx]
 
 
 def _gens(name: str, count: int):
@@ -190,6 +195,48 @@ def square4096_acc(batch: int = 4, size: int = 4096) -> Problem:
                    Operand(A, (s2, 1, size)), Operand(B, (s2, size, 1)), Operand(C, (s2, size, 1)))
 
 
+def _linear_bwd_tensors():
+    gy, gw, gx = _gens("linear_bwd", 3)
+    dy = _f32(gy.normal(0.0, 1.0, (2048, 2560)))
+    W = _f32(gw.normal(0.0, 0.02, (2560, 960)))
+    x = _f32(gx.normal(0.0, 1.0, (2048, 960)))
+    return dy, W, x
+
+
+def linear_bwd_dx() -> Problem:
+    """Backward of the linear layer y = x W^T, input gradient: dx = dy W
+    (the left gradient dC B^T of "PyTorch demystified 3", Opt. 4, with B =
+    W^T).  dy [2048][2560] N(0,1) row-major (k-fast), W stored [2560][960]
+    N(0,0.02) read as stored (n-fast), dx [2048][960]."""
+    dy, W, _ = _linear_bwd_tensors()
+    dx = np.zeros(2048 * 960, np.float32)
+    return Problem("linear_bwd_dx", 1, 2048, 960, 2560, 1.0, False,
+                   Operand(dy, (0, 2560, 1)), Operand(W, (0, 960, 1)), Operand(dx, (0, 960, 1)))
+
+
+def linear_bwd_dw() -> Problem:
+    """Backward of the linear layer, weight gradient in W's own layout:
+    dW = dy^T x (the right gradient A^T dC of the same page, transposed to
+    match W [2560][960]).  dy read transposed (A[i][p] = dy[p][i], m-fast),
+    x [2048][960] N(0,1) row-major (n-fast), same dy as linear_bwd_dx."""
+    dy, _, x = _linear_bwd_tensors()
+    dW = np.zeros(2560 * 960, np.float32)
+    return Problem("linear_bwd_dw", 1, 2560, 960, 2048, 1.0, False,
+                   Operand(dy, (0, 1, 2560)), Operand(x, (0, 960, 1)), Operand(dW, (0, 960, 1)))
+
+
+def linear_xT() -> Problem:
+    """The fourth transpose case at the linear layer's size: y = x W^T with
+    the activations stored feature-major, x^T [960][2048] (A m-fast), and W
+    stored [2560][960] read transposed (B k-fast)."""
+    gx, gw = _gens("linear_xT", 2)
+    xT = _f32(gx.normal(0.0, 1.0, (960, 2048)))
+    W = _f32(gw.normal(0.0, 0.02, (2560, 960)))
+    y = np.zeros(2048 * 2560, np.float32)
+    return Problem("linear_xT", 1, 2048, 2560, 960, 1.0, False,
+                   Operand(xT, (0, 1, 2048)), Operand(W, (0, 1, 960)), Operand(y, (0, 2560, 1)))
+
+
 BUILDERS = {
     "square64": square64,
     "linear_xWt": linear_xWt,
@@ -197,6 +244,9 @@ BUILDERS = {
     "attn_pv": attn_pv,
     "spectrogram": spectrogram,
     "square4096_acc": square4096_acc,
+    "linear_bwd_dx": linear_bwd_dx,
+    "linear_bwd_dw": linear_bwd_dw,
+    "linear_xT": linear_xT,
 }
 
 

@@ -203,12 +203,13 @@ def test_every_tile(tile, monkeypatch):
                 assert e <= TOL, (tile, m, n, k, pad, a_major, b_major, acc, e)
 
 
+@pytest.mark.parametrize("tile", ["p64x64k64", "p128x64k64", "p64x128k64"])
 @pytest.mark.parametrize("wgs", [None, "8", "7", "1"])
-def test_persistent_tile(wgs, monkeypatch):
-    """The persistent short-k kernel, forced, on ragged shapes with k <= 64
+def test_persistent_tile(tile, wgs, monkeypatch):
+    """Each persistent short-k tile, forced, on ragged shapes with k <= 64
     in all four transpose cases, accumulating and not; a capped grid makes
     each workgroup loop over many tiles (odd and even counts)."""
-    monkeypatch.setenv("SGEMM_FORCE_TILE", "p64x64k64")
+    monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
     if wgs:
         monkeypatch.setenv("SGEMM_PERSIST_WGS", wgs)
     shapes = [(3, 300, 260, 64), (5, 132, 68, 40), (2, 64, 64, 4), (9, 128, 192, 60), (1, 4, 8, 12)]
@@ -219,10 +220,10 @@ def test_persistent_tile(wgs, monkeypatch):
                                       b_major=b_major, dist="normal", alpha=-1.25,
                                       accumulate=acc)
                 info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
-                assert info["kernel"].startswith("persist_p64x64k64"), info
+                assert info["kernel"].startswith("persist_" + tile), info
                 got, ref = out(p, gpu_call(p)), out(p, oracle_call(p))
                 e = err_ratio(p, got, ref)
-                assert e <= TOL, (wgs, m, n, k, a_major, b_major, acc, e)
+                assert e <= TOL, (tile, wgs, m, n, k, a_major, b_major, acc, e)
 
 
 def test_column_major_output():
