@@ -17,6 +17,11 @@ for b < batch, i < m, j < n
 
 with X[b,r,c] = X_storage[b*sX_batch + r*sX_row + c*sX_col], strides counted in
 elements.  Sums are formed in fp64 in ascending p and rounded to fp32 once.
+
+The general epilogue (``ref_sgemm_ex``) adds beta * C_old (not read when
+beta == 0), a per-row term r[b,i] and a per-column term c[b,j]; ``ref_sqnorms``
+and ``ref_sqdist`` are squared Euclidean norms and distances from their plain
+definitions.
 """
 from __future__ import annotations
 
@@ -67,6 +72,27 @@ def _bind(lib):
         _fptr, _i64, _i64, _i64,
         _i64, _i64ptr, _fptr,
     ]
+    ex_args = [
+        _i64, _i64, _i64, _i64, _f32,
+        _fptr, _i64, _i64, _i64,
+        _fptr, _i64, _i64, _i64,
+        _f32,
+        _fptr, _i64, _i64, _i64,
+        _fptr, _i64, _i64,
+        _fptr, _i64, _i64,
+    ]
+    lib.oracle_sgemm_ex.restype = _int
+    lib.oracle_sgemm_ex.argtypes = ex_args + [_int]
+    lib.oracle_sgemm_ex_entries.restype = _int
+    lib.oracle_sgemm_ex_entries.argtypes = ex_args + [_i64, _i64ptr, _fptr]
+    lib.oracle_sqnorms.restype = _int
+    lib.oracle_sqnorms.argtypes = [_i64, _i64, _i64, _fptr, _i64, _i64, _i64, _fptr, _i64, _i64]
+    lib.oracle_sqdist.restype = _int
+    lib.oracle_sqdist.argtypes = [_i64, _i64, _i64, _i64,
+                                  _fptr, _i64, _i64, _i64,
+                                  _fptr, _i64, _i64, _i64,
+                                  _fptr, _i64, _i64, _i64,
+                                  _i64, _i64ptr, _fptr]
     lib.oracle_num_threads.restype = _int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -170,6 +196,123 @@ def ref_entries(batch, m, n, k, alpha,
                                   idx.shape[0], idx.ctypes.data_as(_i64ptr), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_sgemm_entries: index outside the product")
+    return out
+
+
+def _opt_vector(v, name, batch, count, s_batch, s_item):
+    """A NULL pointer for None, else the checked storage of a batch of
+    vectors v[b*s_batch + i*s_item]."""
+    if v is None:
+        return None
+    v = _as_storage(v, name)
+    if batch and count:
+        _check_view(v, name, (batch, count), (s_batch, s_item))
+    return v
+
+
+def _ex_args(batch, m, n, k, alpha, A, sA, B, sB, beta, C, sC, row_add, sR, col_add, sL):
+    A = _as_storage(A, "A")
+    B = _as_storage(B, "B")
+    if min(batch, m, n, k) < 0:
+        raise ValueError("negative size")
+    if batch and m and k:
+        _check_view(A, "A", (batch, m, k), sA)
+    if batch and n and k:
+        _check_view(B, "B", (batch, k, n), sB)
+    _check_view(C, "C", (batch, m, n), sC)
+    row_add = _opt_vector(row_add, "row_add", batch, m, *sR)
+    col_add = _opt_vector(col_add, "col_add", batch, n, *sL)
+    nul = ctypes.cast(None, _fptr)
+    return [batch, m, n, k, float(alpha), _ptr(A), *sA, _ptr(B), *sB, float(beta), _ptr(C), *sC,
+            _ptr(row_add) if row_add is not None else nul, *sR,
+            _ptr(col_add) if col_add is not None else nul, *sL]
+
+
+def ref_sgemm_ex(batch, m, n, k, alpha, A, sA, B, sB, beta, C, sC,
+                 row_add=None, sR=(0, 0), col_add=None, sL=(0, 0), reverse=False, lib=None):
+    """C <- alpha*A*B + beta*C + row_add[b,i] + col_add[b,j] over host
+    storages (each s* a stride tuple: (batch, row, col) for the matrices,
+    (batch, index) for the vectors); writes C in place.  beta == 0 never
+    reads C; a vector given as None drops its term."""
+    lib = lib or _get_lib()
+    C = _as_storage(C, "C", writable=True)
+    args = _ex_args(batch, m, n, k, alpha, A, sA, B, sB, beta, C, sC, row_add, sR, col_add, sL)
+    rc = lib.oracle_sgemm_ex(*args, int(bool(reverse)))
+    if rc != 0:
+        raise RuntimeError(f"oracle_sgemm_ex returned {rc}")
+    return C
+
+
+def ref_sgemm_ex_entries(batch, m, n, k, alpha, A, sA, B, sB, beta, C, sC, idx,
+                         row_add=None, sR=(0, 0), col_add=None, sL=(0, 0), lib=None):
+    """Values ref_sgemm_ex would store at the (b,i,j) rows of `idx`; C is
+    only read (as C_old, when beta != 0)."""
+    lib = lib or _get_lib()
+    C = _as_storage(C, "C")
+    idx = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 3)
+    args = _ex_args(batch, m, n, k, alpha, A, sA, B, sB, beta, C, sC, row_add, sR, col_add, sL)
+    out = np.empty(idx.shape[0], dtype=np.float32)
+    rc = lib.oracle_sgemm_ex_entries(*args, idx.shape[0], idx.ctypes.data_as(_i64ptr), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_sgemm_ex_entries: index outside the product")
+    return out
+
+
+def ref_sqnorms(batch, count, length, X, sX, out, sO, lib=None):
+    """out[b*sO[0] + i*sO[1]] = sum_p X[b,i,p]^2 for X strides sX =
+    (batch, item, element); writes out in place."""
+    lib = lib or _get_lib()
+    X = _as_storage(X, "X")
+    out = _as_storage(out, "out", writable=True)
+    if min(batch, count, length) < 0:
+        raise ValueError("negative size")
+    if batch and count and length:
+        _check_view(X, "X", (batch, count, length), sX)
+    if batch and count:
+        _check_view(out, "out", (batch, count), sO)
+    rc = lib.oracle_sqnorms(batch, count, length, _ptr(X), *sX, _ptr(out), *sO)
+    if rc != 0:
+        raise RuntimeError(f"oracle_sqnorms returned {rc}")
+    return out
+
+
+def _sqdist_views(batch, m, n, k, X, sX, Y, sY):
+    X = _as_storage(X, "X")
+    Y = _as_storage(Y, "Y")
+    if min(batch, m, n, k) < 0:
+        raise ValueError("negative size")
+    if batch and m and k:
+        _check_view(X, "X", (batch, m, k), sX)
+    if batch and n and k:
+        _check_view(Y, "Y", (batch, n, k), sY)
+    return X, Y
+
+
+def ref_sqdist(batch, m, n, k, X, sX, Y, sY, D, sD, lib=None):
+    """D[b,i,j] = sum_p (X[b,i,p] - Y[b,j,p])^2 (rows of X against rows of
+    Y, both [batch][rows][k] views); writes D in place."""
+    lib = lib or _get_lib()
+    X, Y = _sqdist_views(batch, m, n, k, X, sX, Y, sY)
+    D = _as_storage(D, "D", writable=True)
+    _check_view(D, "D", (batch, m, n), sD)
+    rc = lib.oracle_sqdist(batch, m, n, k, _ptr(X), *sX, _ptr(Y), *sY, _ptr(D), *sD,
+                           0, ctypes.cast(None, _i64ptr), ctypes.cast(None, _fptr))
+    if rc != 0:
+        raise RuntimeError(f"oracle_sqdist returned {rc}")
+    return D
+
+
+def ref_sqdist_entries(batch, m, n, k, X, sX, Y, sY, idx, lib=None):
+    """Distances at the (b,i,j) rows of `idx` only."""
+    lib = lib or _get_lib()
+    X, Y = _sqdist_views(batch, m, n, k, X, sX, Y, sY)
+    idx = np.ascontiguousarray(idx, dtype=np.int64).reshape(-1, 3)
+    out = np.empty(idx.shape[0], dtype=np.float32)
+    nul = ctypes.cast(None, _fptr)
+    rc = lib.oracle_sqdist(batch, m, n, k, _ptr(X), *sX, _ptr(Y), *sY, nul, 0, 0, 0,
+                           idx.shape[0], idx.ctypes.data_as(_i64ptr), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_sqdist: index outside the table")
     return out
 
 

@@ -29,6 +29,10 @@
  * fp32 once.  Every output element is computed on its own, so the order in
  * which elements are visited cannot change any bit.
  *
+ * The general epilogue (any beta, a per-row and a per-column term) and the
+ * squared norms and distances follow the same rules: every term is formed in
+ * fp64 and the element is rounded to fp32 once.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
 #include <stdint.h>
@@ -44,11 +48,11 @@ static inline int64_t elem_offset(int64_t b, int64_t r, int64_t c,
     return b * s_batch + r * s_row + c * s_col;
 }
 
-/* One output element, straight from the definition. */
-static float one_element(int64_t b, int64_t i, int64_t j, int64_t k, float alpha,
-                         const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
-                         const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
-                         int accumulate, float c_old)
+/* sum_p A[b,i,p] * B[b,p,j] in fp64, ascending p (the products of two fp32
+ * values are exact in fp64). */
+static double dot_fp64(int64_t b, int64_t i, int64_t j, int64_t k,
+                       const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                       const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col)
 {
     double sum = 0.0;
     for (int64_t p = 0; p < k; ++p) {
@@ -56,24 +60,58 @@ static float one_element(int64_t b, int64_t i, int64_t j, int64_t k, float alpha
         double bv = (double)B[elem_offset(b, p, j, sB_batch, sB_row, sB_col)];
         sum += a * bv;
     }
-    double out = (double)alpha * sum;
-    if (accumulate)
-        out += (double)c_old;
+    return sum;
+}
+
+/*
+ * One output element, straight from the definition, with the epilogue in its
+ * general form:
+ *
+ *   C[b,i,j] <- alpha * sum_p A[b,i,p] B[b,p,j] + beta * C_old[b,i,j]
+ *               + row_add[b,i] + col_add[b,j]
+ *
+ * "Optionally plus C" is beta = 1, the plain product beta = 0.  The general
+ * beta and the two vector terms serve the matrix-and-bias fusion of "PyTorch
+ * demystified 3" ("Comparison with cuBLAS and outlook": a feed-forward layer's
+ * product and its bias add in one kernel) and the tokenizer distances that
+ * StaleyNET ("The matrix product") routes through the product.  beta == 0
+ * drops the C_old term without reading it (the stored C may hold anything,
+ * NaN included); a NULL row_add or col_add drops its term.  The vectors are
+ * addressed as row_add[b*sR_batch + i*sR_row] and col_add[b*sL_batch +
+ * j*sL_col].
+ */
+static float one_element(int64_t b, int64_t i, int64_t j, int64_t k, float alpha,
+                         const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                         const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                         float beta, const float *c_old,
+                         const float *row_add, int64_t sR_batch, int64_t sR_row,
+                         const float *col_add, int64_t sL_batch, int64_t sL_col)
+{
+    double total = dot_fp64(b, i, j, k, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row, sB_col);
+    double out = (double)alpha * total;
+    if (beta != 0.0f)
+        out += (double)beta * (double)*c_old;
+    if (row_add)
+        out += (double)row_add[b * sR_batch + i * sR_row];
+    if (col_add)
+        out += (double)col_add[b * sL_batch + j * sL_col];
     return (float)out;
 }
 
 /*
- * Full product.  Same argument order and meaning as the library entry point,
- * with host pointers.  `reverse` visits the (b, i, j) elements last-to-first
- * (the order-independence check of kael's host emulation); it must not change
- * any bit.  Returns 0, or -1 for a negative size.
+ * Full product with the general epilogue, host pointers.  `reverse` visits
+ * the (b, i, j) elements last-to-first (the order-independence check of
+ * kael's host emulation); it must not change any bit.  Returns 0, or -1 for a
+ * negative size.
  */
-int oracle_sgemm(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
-                 const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
-                 const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
-                 int accumulate,
-                 float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
-                 int reverse)
+int oracle_sgemm_ex(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                    const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                    const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                    float beta,
+                    float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                    const float *row_add, int64_t sR_batch, int64_t sR_row,
+                    const float *col_add, int64_t sL_batch, int64_t sL_col,
+                    int reverse)
 {
     if (batch < 0 || m < 0 || n < 0 || k < 0)
         return -1;
@@ -85,9 +123,8 @@ int oracle_sgemm(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
         for (int64_t jj = 0; jj < n; ++jj) {
             int64_t j = reverse ? n - 1 - jj : jj;
             float *c = C + elem_offset(b, i, j, sC_batch, sC_row, sC_col);
-            float c_old = accumulate ? *c : 0.0f;
-            *c = one_element(b, i, j, k, alpha, A, sA_batch, sA_row, sA_col,
-                             B, sB_batch, sB_row, sB_col, accumulate, c_old);
+            *c = one_element(b, i, j, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row,
+                             sB_col, beta, c, row_add, sR_batch, sR_row, col_add, sL_batch, sL_col);
         }
     }
     return 0;
@@ -95,17 +132,19 @@ int oracle_sgemm(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
 
 /*
  * Selected elements only: for each q < count, (b, i, j) = idx[3q .. 3q+2],
- * out[q] receives what oracle_sgemm would store at C[b, i, j].  C_old is read
- * from C when accumulating; C is never written.  This is how outputs of
- * products too large for the full oracle are checked one by one.
+ * out[q] receives what oracle_sgemm_ex would store at C[b, i, j].  C is only
+ * read (as C_old, and only when beta != 0), never written.  This is how
+ * outputs of products too large for the full oracle are checked one by one.
  * Returns 0, or -1 for an index outside [0,batch) x [0,m) x [0,n).
  */
-int oracle_sgemm_entries(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
-                         const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
-                         const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
-                         int accumulate,
-                         const float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
-                         int64_t count, const int64_t *idx, float *out)
+int oracle_sgemm_ex_entries(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                            const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                            const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                            float beta,
+                            const float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                            const float *row_add, int64_t sR_batch, int64_t sR_row,
+                            const float *col_add, int64_t sL_batch, int64_t sL_col,
+                            int64_t count, const int64_t *idx, float *out)
 {
     for (int64_t q = 0; q < count; ++q) {
         int64_t b = idx[3 * q], i = idx[3 * q + 1], j = idx[3 * q + 2];
@@ -115,9 +154,106 @@ int oracle_sgemm_entries(int64_t batch, int64_t m, int64_t n, int64_t k, float a
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t q = 0; q < count; ++q) {
         int64_t b = idx[3 * q], i = idx[3 * q + 1], j = idx[3 * q + 2];
-        float c_old = accumulate ? C[elem_offset(b, i, j, sC_batch, sC_row, sC_col)] : 0.0f;
-        out[q] = one_element(b, i, j, k, alpha, A, sA_batch, sA_row, sA_col,
-                             B, sB_batch, sB_row, sB_col, accumulate, c_old);
+        out[q] = one_element(b, i, j, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row,
+                             sB_col, beta, C + elem_offset(b, i, j, sC_batch, sC_row, sC_col),
+                             row_add, sR_batch, sR_row, col_add, sL_batch, sL_col);
+    }
+    return 0;
+}
+
+/* "Optionally plus C" as a flag: beta = 1 when accumulating, else 0. */
+static float accumulate_beta(int accumulate) { return accumulate ? 1.0f : 0.0f; }
+
+/* The product of the pages, C <- alpha*A*B (+ C): same argument order and
+ * meaning as the library entry point.  Returns 0, or -1 for a negative size. */
+int oracle_sgemm(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                 const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                 const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                 int accumulate,
+                 float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                 int reverse)
+{
+    return oracle_sgemm_ex(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row,
+                           sB_col, accumulate_beta(accumulate), C, sC_batch, sC_row, sC_col,
+                           NULL, 0, 0, NULL, 0, 0, reverse);
+}
+
+/* Selected elements of oracle_sgemm (see oracle_sgemm_ex_entries). */
+int oracle_sgemm_entries(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                         const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                         const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                         int accumulate,
+                         const float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                         int64_t count, const int64_t *idx, float *out)
+{
+    return oracle_sgemm_ex_entries(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
+                                   sB_row, sB_col, accumulate_beta(accumulate), C, sC_batch, sC_row,
+                                   sC_col, NULL, 0, 0, NULL, 0, 0, count, idx, out);
+}
+
+/*
+ * Squared Euclidean norms of a batch of vectors: out[b,i] = sum_p X[b,i,p]^2,
+ * with X[b,i,p] at b*sX_batch + i*sX_item + p*sX_elem and out[b,i] at
+ * b*sO_batch + i*sO_item.  Returns 0, or -1 for a negative size.
+ */
+int oracle_sqnorms(int64_t batch, int64_t count, int64_t len,
+                   const float *X, int64_t sX_batch, int64_t sX_item, int64_t sX_elem,
+                   float *out, int64_t sO_batch, int64_t sO_item)
+{
+    if (batch < 0 || count < 0 || len < 0)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < batch * count; ++t) {
+        int64_t bb = t / count, item = t % count;
+        double sq = 0.0;
+        for (int64_t e = 0; e < len; ++e) {
+            double x = (double)X[bb * sX_batch + item * sX_item + e * sX_elem];
+            sq += x * x;
+        }
+        out[bb * sO_batch + item * sO_item] = (float)sq;
+    }
+    return 0;
+}
+
+/*
+ * Squared Euclidean distances between the rows of X [batch][m][k] and the
+ * rows of Y [batch][n][k], straight from the definition:
+ * D[b,i,j] = sum_p (X[b,i,p] - Y[b,j,p])^2 (differences and squares in fp64).
+ * The tokenizer distances of StaleyNET ("The matrix product") are such a
+ * table of vectors against codebook entries.  With idx == NULL the whole
+ * table is written to D (strides sD_*); otherwise out[q] receives the
+ * element (b, i, j) = idx[3q .. 3q+2] and D is not touched.
+ * Returns 0, -1 for a negative size, -2 for an index outside the table.
+ */
+int oracle_sqdist(int64_t batch, int64_t m, int64_t n, int64_t k,
+                  const float *X, int64_t sX_batch, int64_t sX_row, int64_t sX_col,
+                  const float *Y, int64_t sY_batch, int64_t sY_row, int64_t sY_col,
+                  float *D, int64_t sD_batch, int64_t sD_row, int64_t sD_col,
+                  int64_t count, const int64_t *idx, float *out)
+{
+    if (batch < 0 || m < 0 || n < 0 || k < 0)
+        return -1;
+    if (idx)
+        for (int64_t q = 0; q < count; ++q)
+            if (idx[3 * q] < 0 || idx[3 * q] >= batch || idx[3 * q + 1] < 0 || idx[3 * q + 1] >= m ||
+                idx[3 * q + 2] < 0 || idx[3 * q + 2] >= n)
+                return -2;
+    int64_t total = idx ? count : batch * m * n;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t q = 0; q < total; ++q) {
+        int64_t bq = idx ? idx[3 * q] : q / (m * n);
+        int64_t iq = idx ? idx[3 * q + 1] : (q / n) % m;
+        int64_t jq = idx ? idx[3 * q + 2] : q % n;
+        double d = 0.0;
+        for (int64_t e = 0; e < k; ++e) {
+            double diff = (double)X[bq * sX_batch + iq * sX_row + e * sX_col] -
+                          (double)Y[bq * sY_batch + jq * sY_row + e * sY_col];
+            d += diff * diff;
+        }
+        if (idx)
+            out[q] = (float)d;
+        else
+            D[bq * sD_batch + iq * sD_row + jq * sD_col] = (float)d;
     }
     return 0;
 }

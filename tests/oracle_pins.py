@@ -348,7 +348,145 @@ def pin_nan_and_canaries(lib):
     assert np.all(np.isnan(C[~covered]))
 
 
+# ------------------------------------------------ general epilogue, distances
+
+def _ex_case(lib, rng, batch, m, n, k, a_major, b_major, alpha, beta, use_row, use_col,
+             vec_batch_stride=True, reverse=False):
+    """Integer data: alpha*A@B + beta*C_old + r[i] + c[j] is exact in fp32
+    for these sizes, so numpy's int64 arithmetic gives the unique result."""
+    per_a, sa = layout_strides(m, k, a_major)
+    per_b, sb = layout_strides(k, n, b_major)
+    per_c, sc = layout_strides(m, n, "row")
+    A = rng.integers(-3, 4, per_a * batch).astype(np.float32)
+    B = rng.integers(-3, 4, per_b * batch).astype(np.float32)
+    C = rng.integers(-3, 4, per_c * batch).astype(np.float32)
+    nvb = batch if vec_batch_stride else 1
+    r = rng.integers(-9, 10, m * nvb + 2).astype(np.float32)
+    c = rng.integers(-9, 10, n * nvb + 2).astype(np.float32)
+    sR = (m if vec_batch_stride else 0, 1)
+    sL = (n if vec_batch_stride else 0, 1)
+    exact = np.matmul(view(A, batch, m, k, sa).astype(np.int64),
+                      view(B, batch, k, n, sb).astype(np.int64)).astype(np.float64) * alpha
+    if beta != 0:
+        exact = exact + beta * view(C, batch, m, n, sc)
+    if use_row:
+        exact = exact + np.array([[r[b * sR[0] + i] for i in range(m)] for b in range(batch)])[:, :, None]
+    if use_col:
+        exact = exact + np.array([[c[b * sL[0] + j] for j in range(n)] for b in range(batch)])[:, None, :]
+    out = C.copy()
+    oracle.ref_sgemm_ex(batch, m, n, k, alpha, A, sa, B, sb, beta, out, sc,
+                        row_add=r if use_row else None, sR=sR, col_add=c if use_col else None,
+                        sL=sL, reverse=reverse, lib=lib)
+    got = view(out, batch, m, n, sc)
+    assert np.array_equal(got, exact.astype(np.float32)), (batch, m, n, k, alpha, beta, use_row, use_col)
+
+
+def pin_epilogue_bruteforce(lib):
+    """C <- alpha*A*B + beta*C_old + r[b,i] + c[b,j] on integer data, every
+    transpose case, beta in {0, 1, -2, 0.5}, each vector term on and off,
+    per-batch and shared (batch stride 0) vectors: exact against int64."""
+    rng = np.random.default_rng(7)
+    for a_major, b_major in LAYOUTS:
+        for beta in (0.0, 1.0, -2.0, 0.5):
+            for use_row in (False, True):
+                for use_col in (False, True):
+                    for shared in (False, True):
+                        _ex_case(lib, rng, 3, 5, 6, 4, a_major, b_major, -2.0, beta, use_row, use_col,
+                                 vec_batch_stride=not shared)
+    for m, n, k in ((1, 1, 1), (7, 3, 8), (2, 9, 1)):
+        _ex_case(lib, rng, 2, m, n, k, "col", "row", 1.0, 1.0, True, True, reverse=True)
+
+
+def pin_epilogue_closed_forms(lib):
+    """All-ones A, B: C = k*alpha + beta*C_old + r[i] + c[j] exactly; beta = 1
+    with no vector terms is "optionally plus C" (the accumulate flag gives
+    the same bits); beta = 0 never reads C_old (a NaN-filled C stays out)."""
+    batch, m, n = 2, 3, 5
+    for k in (1, 64, 4096):
+        p = random_problem(k + 1, batch, m, n, k, dist="ones", alpha=0.5, accumulate=True)
+        r = np.arange(m * batch, dtype=np.float32) * 0.25
+        c = -np.arange(n * batch, dtype=np.float32)
+        for beta in (1.0, -0.5):
+            out = p.C.storage.copy()
+            oracle.ref_sgemm_ex(batch, m, n, k, 0.5, p.A.storage, p.A.strides, p.B.storage, p.B.strides,
+                                beta, out, p.C.strides, row_add=r, sR=(m, 1), col_add=c, sL=(n, 1), lib=lib)
+            cold = view(p.C.storage, batch, m, n, p.C.strides).astype(np.float64)
+            want = k * 0.5 + beta * cold + r.reshape(batch, m, 1) + c.reshape(batch, 1, n)
+            assert np.array_equal(view(out, batch, m, n, p.C.strides), want.astype(np.float32)), (k, beta)
+        flag = _run(p, lib)
+        plain = p.C.storage.copy()
+        oracle.ref_sgemm_ex(batch, m, n, k, 0.5, p.A.storage, p.A.strides, p.B.storage, p.B.strides,
+                            1.0, plain, p.C.strides, lib=lib)
+        assert np.array_equal(flag, plain)
+    q = random_problem(31, 2, 4, 6, 5, dist="normal")
+    nanC = np.full_like(q.C.storage, np.nan)
+    oracle.ref_sgemm_ex(2, 4, 6, 5, 1.0, q.A.storage, q.A.strides, q.B.storage, q.B.strides, 0.0, nanC,
+                        q.C.strides, row_add=np.ones(8, np.float32), sR=(4, 1), lib=lib)
+    assert not np.any(np.isnan(view(nanC, 2, 4, 6, q.C.strides)))
+    idx = np.array([[0, 0, 0], [1, 3, 5], [1, 2, 0]])
+    r = np.arange(8, dtype=np.float32)
+    full = q.C.storage.copy()
+    oracle.ref_sgemm_ex(2, 4, 6, 5, 1.5, q.A.storage, q.A.strides, q.B.storage, q.B.strides, -1.0, full,
+                        q.C.strides, row_add=r, sR=(4, 1), lib=lib)
+    one = oracle.ref_sgemm_ex_entries(2, 4, 6, 5, 1.5, q.A.storage, q.A.strides, q.B.storage,
+                                      q.B.strides, -1.0, q.C.storage, q.C.strides, idx,
+                                      row_add=r, sR=(4, 1), lib=lib)
+    assert np.array_equal(one, view(full, 2, 4, 6, q.C.strides)[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
+def pin_sqnorms(lib):
+    """Squared norms of rows and of columns (the same storage read along
+    either axis) equal numpy's int64 sums of squares; norms of all-ones
+    vectors are their lengths."""
+    rng = np.random.default_rng(8)
+    X = rng.integers(-5, 6, 3 * 7 * 9).astype(np.float32)
+    Xi = X.reshape(3, 7, 9).astype(np.int64)
+    rows = np.zeros(3 * 7, np.float32)
+    oracle.ref_sqnorms(3, 7, 9, X, (63, 9, 1), rows, (7, 1), lib=lib)
+    assert np.array_equal(rows.reshape(3, 7), (Xi ** 2).sum(2).astype(np.float32))
+    cols = np.zeros(3 * 9 * 2, np.float32)
+    oracle.ref_sqnorms(3, 9, 7, X, (63, 1, 9), cols, (18, 2), lib=lib)
+    assert np.array_equal(cols.reshape(3, 9, 2)[:, :, 0], (Xi ** 2).sum(1).astype(np.float32))
+    ones = np.ones(5 * 300, np.float32)
+    out = np.zeros(5, np.float32)
+    oracle.ref_sqnorms(1, 5, 300, ones, (0, 300, 1), out, (0, 1), lib=lib)
+    assert np.array_equal(out, np.full(5, 300.0, np.float32))
+
+
+def pin_sqdist(lib):
+    """Squared distances: integer brute force ((x - y)^2 summed in int64),
+    zero from a point to itself, D(X, Y) = D(Y, X)^T, invariance under a
+    common integer shift, and the expansion |x|^2 + |y|^2 - 2 x.y."""
+    rng = np.random.default_rng(9)
+    for batch, m, n, k in ((1, 1, 1, 1), (2, 5, 4, 7), (3, 8, 9, 3), (1, 16, 2, 33)):
+        X = rng.integers(-4, 5, batch * m * k).astype(np.float32)
+        Y = rng.integers(-4, 5, batch * n * k).astype(np.float32)
+        sX, sY, sD = (m * k, k, 1), (n * k, k, 1), (m * n, n, 1)
+        D = np.zeros(batch * m * n, np.float32)
+        oracle.ref_sqdist(batch, m, n, k, X, sX, Y, sY, D, sD, lib=lib)
+        Xi, Yi = X.reshape(batch, m, 1, k).astype(np.int64), Y.reshape(batch, 1, n, k).astype(np.int64)
+        exact = ((Xi - Yi) ** 2).sum(3)
+        assert np.array_equal(D.reshape(batch, m, n), exact.astype(np.float32))
+        expand = (Xi ** 2).sum(3) + (Yi ** 2).sum(3) - 2 * (Xi * Yi).sum(3)
+        assert np.array_equal(exact, expand)
+        DT = np.zeros(batch * n * m, np.float32)
+        oracle.ref_sqdist(batch, n, m, k, Y, sY, X, sX, DT, (n * m, m, 1), lib=lib)
+        assert np.array_equal(DT.reshape(batch, n, m), D.reshape(batch, m, n).transpose(0, 2, 1))
+        t = rng.integers(-3, 4, k).astype(np.float32)
+        Ds = np.zeros_like(D)
+        oracle.ref_sqdist(batch, m, n, k, (X.reshape(-1, k) + t).ravel(), sX,
+                          (Y.reshape(-1, k) + t).ravel(), sY, Ds, sD, lib=lib)
+        assert np.array_equal(Ds, D)
+        self_d = np.zeros(batch * m * m, np.float32)
+        oracle.ref_sqdist(batch, m, m, k, X, sX, X, sX, self_d, (m * m, m, 1), lib=lib)
+        assert np.all(np.diagonal(self_d.reshape(batch, m, m), axis1=1, axis2=2) == 0)
+        idx = np.stack([rng.integers(0, batch, 9), rng.integers(0, m, 9), rng.integers(0, n, 9)], 1)
+        one = oracle.ref_sqdist_entries(batch, m, n, k, X, sX, Y, sY, idx, lib=lib)
+        assert np.array_equal(one, D.reshape(batch, m, n)[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
 PINS = [pin_all_ones, pin_identity, pin_k_zero, pin_golden_transpose_trace,
         pin_golden_column_major, pin_blas_linear_mapping, pin_blas_rowmajor_trick,
         pin_exact_bruteforce, pin_numpy_float64, pin_stride_swap, pin_transpose_identity,
-        pin_batch_slices, pin_accumulate, pin_order_and_entries, pin_nan_and_canaries]
+        pin_batch_slices, pin_accumulate, pin_order_and_entries, pin_nan_and_canaries,
+        pin_epilogue_bruteforce, pin_epilogue_closed_forms, pin_sqnorms, pin_sqdist]

@@ -28,16 +28,28 @@ MUTANTS = {
                       "elem_offset(b, j, p, sB_batch, sB_row, sB_col)")],
     "strides_exchanged": [("return b * s_batch + r * s_row + c * s_col;",
                            "return b * s_batch + r * s_col + c * s_row;")],
-    "alpha_dropped": [("double out = (double)alpha * sum;", "double out = sum;")],
-    "alpha_on_c_old": [("out += (double)c_old;", "out += (double)alpha * c_old;")],
-    "accumulate_inverted": [("if (accumulate)\n        out +=", "if (!accumulate)\n        out +=")],
-    "always_accumulate": [("float c_old = accumulate ? *c : 0.0f;", "float c_old = *c;"),
-                          ("if (accumulate)\n        out +=", "if (1)\n        out +=")],
+    "alpha_dropped": [("double out = (double)alpha * total;", "double out = total;")],
+    "alpha_on_c_old": [("out += (double)beta * (double)*c_old;", "out += (double)alpha * (double)*c_old;")],
+    "accumulate_inverted": [("return accumulate ? 1.0f : 0.0f;", "return accumulate ? 0.0f : 1.0f;")],
+    "always_accumulate": [("return accumulate ? 1.0f : 0.0f;", "return 1.0f;")],
     "fp32_accumulation": [("double sum = 0.0;", "float sum = 0.0f;")],
     "batch_row_swapped": [("int64_t b = row / m, i = row % m;", "int64_t b = row % m, i = row / m;")],
     "B_batch_ignored": [("elem_offset(b, p, j, sB_batch", "elem_offset(0, p, j, sB_batch")],
     "last_column_skipped": [("for (int64_t jj = 0; jj < n; ++jj)", "for (int64_t jj = 0; jj < n - 1; ++jj)")],
-    "alpha_rounded_to_int": [("double out = (double)alpha * sum;", "double out = (double)(int)alpha * sum;")],
+    "alpha_rounded_to_int": [("double out = (double)alpha * total;", "double out = (double)(int)alpha * total;")],
+    "beta_ignored": [("out += (double)beta * (double)*c_old;", "out += (double)*c_old;")],
+    "c_old_read_at_beta_zero": [("if (beta != 0.0f)", "if (1)")],
+    "row_term_dropped": [("out += (double)row_add[b * sR_batch + i * sR_row];", "out += 0.0;")],
+    "col_term_dropped": [("out += (double)col_add[b * sL_batch + j * sL_col];", "out += 0.0;")],
+    "row_term_by_column": [("row_add[b * sR_batch + i * sR_row]", "row_add[b * sR_batch + j * sR_row]")],
+    "vector_batch_ignored": [("col_add[b * sL_batch + j * sL_col]", "col_add[j * sL_col]")],
+    "norm_not_squared": [("sq += x * x;", "sq += x;")],
+    "norm_last_element_skipped": [("for (int64_t e = 0; e < len; ++e)", "for (int64_t e = 0; e < len - 1; ++e)")],
+    "distance_sum_not_difference": [("(double)X[bq * sX_batch + iq * sX_row + e * sX_col] -",
+                                     "(double)X[bq * sX_batch + iq * sX_row + e * sX_col] +")],
+    "distance_Y_transposed": [("(double)Y[bq * sY_batch + jq * sY_row + e * sY_col]",
+                               "(double)Y[bq * sY_batch + e * sY_row + jq * sY_col]")],
+    "distance_not_squared": [("d += diff * diff;", "d += diff < 0 ? -diff : diff;")],
 }
 
 # The brute-force pin at full size is slow; mutants see a smaller sweep.
