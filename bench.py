@@ -77,15 +77,29 @@ def cpu_baseline(p, seconds: float) -> dict:
     """The oracle on rows 0..R-1 of batch 0 of the same product, R chosen so
     the run takes roughly `seconds`."""
     import oracle
+    from strided_fp32_gemm_amd import workloads as wl
     threads = oracle.num_threads()
-    C = p.C.storage.copy()
+    kind = wl.kind(p.name)
+    out = (p.D if kind == "dist" else p.C).storage.copy()
 
     def run(rows):
         t0 = time.perf_counter()
-        oracle.ref_sgemm(1, rows, p.n, p.k, p.alpha,
-                         p.A.storage, 0, p.A.s_row, p.A.s_col,
-                         p.B.storage, 0, p.B.s_row, p.B.s_col,
-                         int(p.accumulate), C, 0, p.C.s_row, p.C.s_col)
+        if kind == "dist":
+            oracle.ref_sqdist(1, rows, p.n, p.k, p.X.storage, (0,) + tuple(p.X.strides[1:]),
+                              p.Y.storage, (0,) + tuple(p.Y.strides[1:]), out,
+                              (0,) + tuple(p.D.strides[1:]))
+        elif kind == "ex":
+            sv = lambda v: (0, v.strides[1]) if v is not None else (0, 0)
+            oracle.ref_sgemm_ex(1, rows, p.n, p.k, p.alpha, p.A.storage, (0, p.A.s_row, p.A.s_col),
+                                p.B.storage, (0, p.B.s_row, p.B.s_col), p.beta_value, out,
+                                (0, p.C.s_row, p.C.s_col),
+                                row_add=p.row.storage if p.row is not None else None, sR=sv(p.row),
+                                col_add=p.col.storage if p.col is not None else None, sL=sv(p.col))
+        else:
+            oracle.ref_sgemm(1, rows, p.n, p.k, p.alpha,
+                             p.A.storage, 0, p.A.s_row, p.A.s_col,
+                             p.B.storage, 0, p.B.s_row, p.B.s_col,
+                             int(p.accumulate), out, 0, p.C.s_row, p.C.s_col)
         return time.perf_counter() - t0
 
     rows = min(p.m, threads)
@@ -102,23 +116,48 @@ def cpu_baseline(p, seconds: float) -> dict:
                       f"{flops / 1e9:.1f} GFLOP in {t:.1f} s)"}
 
 
-def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
+def _step_fn(p, dev, stream):
+    """Device copies of the workload's inputs and one step of it (the call
+    the benchmark times), plus the plan that step launches."""
     import torch
     import strided_fp32_gemm_amd as sg
+    from strided_fp32_gemm_amd import workloads as wl
+
+    kind = wl.kind(p.name)
+    if kind == "dist":
+        dX, dY = torch.from_numpy(p.X.storage).to(dev), torch.from_numpy(p.Y.storage).to(dev)
+        dD = torch.from_numpy(p.D.storage).to(dev)
+        ws = torch.empty(p.workspace_floats, device=dev)
+        args = p.call_args(dX, dY, dD, ws)
+        sX, sY = p.X.strides, p.Y.strides
+        info = sg.sgemm_plan_describe(p.batch, p.m, p.n, p.k, -2.0, dX.data_ptr(), *sX, dY.data_ptr(),
+                                      sY[0], sY[2], sY[1], 0, dD.data_ptr(), *p.D.strides, num_cus=0)
+        info["kernel"] += "_vec (after 2 sqnorms launches)"
+        return (lambda: sg.sgemm_pairwise_sqdist(*args, stream=stream)), info, (dX, dY, dD, ws)
+    dA, dB = torch.from_numpy(p.A.storage).to(dev), torch.from_numpy(p.B.storage).to(dev)
+    dC = torch.from_numpy(p.C.storage).to(dev)
+    info = sg.sgemm_plan_describe(*p.call_args(dA.data_ptr(), dB.data_ptr(), dC.data_ptr()), num_cus=0)
+    if kind == "ex":
+        dr = torch.from_numpy(p.row.storage).to(dev) if p.row is not None else None
+        dl = torch.from_numpy(p.col.storage).to(dev) if p.col is not None else None
+        args = p.ex_call_args(dA, dB, dC, dr, dl)
+        info["kernel"] += "_vec"
+        return (lambda: sg.sgemm_strided_batched_ex(*args, stream=stream)), info, (dA, dB, dC, dr, dl)
+    args = p.call_args(dA, dB, dC)
+    return (lambda: sg.sgemm_strided_batched(*args, stream=stream)), info, (dA, dB, dC)
+
+
+def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
+    import torch
     from strided_fp32_gemm_amd import workloads as wl
 
     p = wl.workload(name)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    dA = torch.from_numpy(p.A.storage).to(dev)
-    dB = torch.from_numpy(p.B.storage).to(dev)
-    dC = torch.from_numpy(p.C.storage).to(dev)
     stream = torch.cuda.current_stream(dev)
-    args = p.call_args(dA, dB, dC)
-    info = sg.sgemm_plan_describe(*p.call_args(dA.data_ptr(), dB.data_ptr(), dC.data_ptr()),
-                                  num_cus=0)
+    step, info, keep = _step_fn(p, dev, stream)
     for _ in range(warmup):
-        sg.sgemm_strided_batched(*args, stream=stream)
+        step()
     torch.cuda.synchronize(dev)
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -127,7 +166,7 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
-        sg.sgemm_strided_batched(*args, stream=stream)
+        step()
         ends[i].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
@@ -151,14 +190,7 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": name,
-            "batch": p.batch, "m": p.m, "n": p.n, "k": p.k,
-            "alpha": p.alpha, "accumulate": bool(p.accumulate),
-            "strides": {"A": list(p.A.strides), "B": list(p.B.strides), "C": list(p.C.strides)},
-            "kernel": info["kernel"],
-            "workgroups": info["workgroups"],
-        },
+        "config": _config(p, info),
         "frac_of_peak": round(value / PEAK_FP32_MATRIX_TFLOPS, 4),
         "roofline": {
             "bound": "mfma",
@@ -175,9 +207,29 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
     }
     if cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(p, cpu_seconds)
-    del dA, dB, dC
+    del keep
     torch.cuda.empty_cache()
     return line
+
+
+def _config(p, info) -> dict:
+    from strided_fp32_gemm_amd import workloads as wl
+
+    c = {"workload": p.name, "batch": p.batch, "m": p.m, "n": p.n, "k": p.k}
+    if wl.kind(p.name) == "dist":
+        c["op"] = "squared distances |x_i - y_j|^2 (sqnorms x2 + product, alpha -2, row/col terms)"
+        c["strides"] = {"X": list(p.X.strides), "Y": list(p.Y.strides), "D": list(p.D.strides)}
+    else:
+        c["alpha"] = p.alpha
+        c["accumulate"] = bool(p.accumulate)
+        c["strides"] = {"A": list(p.A.strides), "B": list(p.B.strides), "C": list(p.C.strides)}
+        if p.is_ex:
+            c["beta"] = p.beta_value
+            c["row_term"] = p.row is not None
+            c["col_term"] = p.col is not None
+    c["kernel"] = info["kernel"]
+    c["workgroups"] = info["workgroups"]
+    return c
 
 
 def main() -> int:

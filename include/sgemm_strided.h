@@ -56,7 +56,8 @@ enum sgemm_status {
     SGEMM_ERR_C_ALIAS = -4,        /* C's strides map two outputs to one address, or C overlaps A or B */
     SGEMM_ERR_UNSUPPORTED = -5,    /* an extent times its stride overflows int64, or no kernel fits */
     SGEMM_ERR_HIP = -6,            /* the HIP runtime rejected a query or launch; see sgemm_last_error() */
-    SGEMM_ERR_INVALID_PATH = -7    /* unknown path code */
+    SGEMM_ERR_INVALID_PATH = -7,   /* unknown path code */
+    SGEMM_ERR_WORKSPACE = -8       /* workspace NULL or smaller than the call needs */
 };
 
 /* Kernel families the planner chooses between (for sgemm_strided_batched_path
@@ -97,6 +98,85 @@ int sgemm_strided_batched_path(int64_t batch, int64_t m, int64_t n, int64_t k,
                                int accumulate,
                                float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
                                int path, void *stream);
+
+/*
+ * The product with a general epilogue (the matrix-and-bias fusion of
+ * "PyTorch demystified 3", section "Comparison with cuBLAS and outlook", and
+ * the per-row / per-column terms of distance tables, StaleyNET "GPU
+ * Implementation", section "The matrix product"):
+ *
+ *     C[b,i,j] <- alpha * sum_{p<k} A[b,i,p] * B[b,p,j] + beta * C[b,i,j]
+ *                 + row_add[b*sR_batch + i*sR_row] + col_add[b*sL_batch + j*sL_col]
+ *
+ * beta == 0 never reads C (it may hold NaN).  row_add / col_add are device
+ * vectors owned by the caller; NULL drops the term (its strides are then
+ * ignored).  A bias over output features is col_add with sL_batch = 0.
+ * Strides are in elements, >= 0; the vectors must not overlap C
+ * (SGEMM_ERR_C_ALIAS).  beta = 1 with no vectors is exactly
+ * sgemm_strided_batched with accumulate = 1 (same bits), beta = 0 with no
+ * vectors the plain product.  Other arguments, ownership, asynchrony and
+ * determinism as for sgemm_strided_batched.  Returns an sgemm_status.
+ */
+int sgemm_strided_batched_ex(int64_t batch, int64_t m, int64_t n, int64_t k,
+                             float alpha,
+                             const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                             const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                             float beta,
+                             float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                             const float *row_add, int64_t sR_batch, int64_t sR_row,
+                             const float *col_add, int64_t sL_batch, int64_t sL_col,
+                             void *stream);
+
+/* sgemm_strided_batched_ex with the kernel family forced (as for
+ * sgemm_strided_batched_path).  Returns an sgemm_status. */
+int sgemm_strided_batched_ex_path(int64_t batch, int64_t m, int64_t n, int64_t k,
+                                  float alpha,
+                                  const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                                  const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                                  float beta,
+                                  float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                                  const float *row_add, int64_t sR_batch, int64_t sR_row,
+                                  const float *col_add, int64_t sL_batch, int64_t sL_col,
+                                  int path, void *stream);
+
+/*
+ * Squared Euclidean norms of a batch of vectors, the terms a distance table
+ * adds to its product:
+ *
+ *     out[b*sO_batch + i*sO_item] <- sum_{p<len} X[b*sX_batch + i*sX_item + p*sX_elem]^2
+ *
+ * for b < batch, i < count.  Rows of a matrix are (sX_item = row stride,
+ * sX_elem = 1), its columns the same storage with the two exchanged.  Sums
+ * are formed in fp32 in a fixed order (reproducible bits).  X and out are
+ * device pointers owned by the caller and must not overlap.  Returns an
+ * sgemm_status; count or batch == 0 enqueues nothing, len == 0 writes 0.
+ */
+int sgemm_sqnorms(int64_t batch, int64_t count, int64_t len,
+                  const float *X, int64_t sX_batch, int64_t sX_item, int64_t sX_elem,
+                  float *out, int64_t sO_batch, int64_t sO_item,
+                  void *stream);
+
+/*
+ * Squared Euclidean distances between the rows of X [batch][m][k] and the
+ * rows of Y [batch][n][k] (sY_batch = 0 shares one Y, e.g. a codebook):
+ *
+ *     D[b,i,j] <- sum_p (X[b,i,p] - Y[b,j,p])^2
+ *
+ * computed as |x_i|^2 + |y_j|^2 - 2 x_i . y_j: two sgemm_sqnorms launches
+ * into `workspace` followed by one sgemm_strided_batched_ex launch (alpha =
+ * -2, beta = 0, the norms as row_add / col_add), all on `stream`.  For
+ * nearly equal vectors the result may be slightly negative by rounding.
+ * workspace: caller-owned device memory of at least batch*m + nY*n floats,
+ * nY = (sY_batch == 0 ? 1 : batch); it must not overlap X, Y or D.
+ * Returns an sgemm_status (SGEMM_ERR_WORKSPACE if workspace is NULL or
+ * smaller than that).
+ */
+int sgemm_pairwise_sqdist(int64_t batch, int64_t m, int64_t n, int64_t k,
+                          const float *X, int64_t sX_batch, int64_t sX_row, int64_t sX_col,
+                          const float *Y, int64_t sY_batch, int64_t sY_row, int64_t sY_col,
+                          float *D, int64_t sD_batch, int64_t sD_row, int64_t sD_col,
+                          float *workspace, int64_t workspace_floats,
+                          void *stream);
 
 /* What the planner would launch (filled by sgemm_plan_describe). */
 typedef struct sgemm_plan_info {

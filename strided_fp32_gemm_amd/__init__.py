@@ -20,9 +20,13 @@ from ._binding import (  # noqa: F401
     SgemmError,
     load,
     sgemm_last_error,
+    sgemm_pairwise_sqdist,
     sgemm_plan_describe,
+    sgemm_sqnorms,
     sgemm_status_string,
     sgemm_strided_batched,
+    sgemm_strided_batched_ex,
+    sgemm_strided_batched_ex_path,
     sgemm_strided_batched_path,
 )
 

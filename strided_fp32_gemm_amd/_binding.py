@@ -24,11 +24,13 @@ STATUS = {
     -5: "SGEMM_ERR_UNSUPPORTED",
     -6: "SGEMM_ERR_HIP",
     -7: "SGEMM_ERR_INVALID_PATH",
+    -8: "SGEMM_ERR_WORKSPACE",
 }
 
 # Every symbol include/sgemm_strided.h declares.
-EXPORTS = ("sgemm_strided_batched", "sgemm_strided_batched_path", "sgemm_plan_describe",
-           "sgemm_status_string", "sgemm_last_error")
+EXPORTS = ("sgemm_strided_batched", "sgemm_strided_batched_path", "sgemm_strided_batched_ex",
+           "sgemm_strided_batched_ex_path", "sgemm_sqnorms", "sgemm_pairwise_sqdist",
+           "sgemm_plan_describe", "sgemm_status_string", "sgemm_last_error")
 
 
 class SgemmError(RuntimeError):
@@ -71,6 +73,14 @@ _GEMM_ARGS = [_i64, _i64, _i64, _i64, _f32,
               _int,
               _vp, _i64, _i64, _i64]
 
+_EX_ARGS = [_i64, _i64, _i64, _i64, _f32,
+            _vp, _i64, _i64, _i64,
+            _vp, _i64, _i64, _i64,
+            _f32,
+            _vp, _i64, _i64, _i64,
+            _vp, _i64, _i64,
+            _vp, _i64, _i64]
+
 _lib = None
 
 
@@ -88,6 +98,18 @@ def load(path: str = LIB_PATH):
     lib.sgemm_strided_batched.argtypes = _GEMM_ARGS + [_vp]
     lib.sgemm_strided_batched_path.restype = _int
     lib.sgemm_strided_batched_path.argtypes = _GEMM_ARGS + [_int, _vp]
+    lib.sgemm_strided_batched_ex.restype = _int
+    lib.sgemm_strided_batched_ex.argtypes = _EX_ARGS + [_vp]
+    lib.sgemm_strided_batched_ex_path.restype = _int
+    lib.sgemm_strided_batched_ex_path.argtypes = _EX_ARGS + [_int, _vp]
+    lib.sgemm_sqnorms.restype = _int
+    lib.sgemm_sqnorms.argtypes = [_i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp]
+    lib.sgemm_pairwise_sqdist.restype = _int
+    lib.sgemm_pairwise_sqdist.argtypes = [_i64, _i64, _i64, _i64,
+                                          _vp, _i64, _i64, _i64,
+                                          _vp, _i64, _i64, _i64,
+                                          _vp, _i64, _i64, _i64,
+                                          _vp, _i64, _vp]
     lib.sgemm_plan_describe.restype = _int
     lib.sgemm_plan_describe.argtypes = _GEMM_ARGS + [_int, _int, ctypes.POINTER(PlanInfo)]
     lib.sgemm_status_string.restype = ctypes.c_char_p
@@ -156,6 +178,71 @@ def sgemm_strided_batched_path(batch, m, n, k, alpha,
     args = _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
                       sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col)
     _check(load().sgemm_strided_batched_path(*args, int(path), _stream(stream)))
+
+
+def _ex_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row, sB_col,
+             beta, C, sC_batch, sC_row, sC_col, row_add, sR_batch, sR_row, col_add, sL_batch,
+             sL_col):
+    return [int(batch), int(m), int(n), int(k), float(alpha),
+            _ptr(A), int(sA_batch), int(sA_row), int(sA_col),
+            _ptr(B), int(sB_batch), int(sB_row), int(sB_col),
+            float(beta),
+            _ptr(C), int(sC_batch), int(sC_row), int(sC_col),
+            _ptr(row_add), int(sR_batch), int(sR_row),
+            _ptr(col_add), int(sL_batch), int(sL_col)]
+
+
+def sgemm_strided_batched_ex(batch, m, n, k, alpha,
+                             A, sA_batch, sA_row, sA_col,
+                             B, sB_batch, sB_row, sB_col,
+                             beta,
+                             C, sC_batch, sC_row, sC_col,
+                             row_add=None, sR_batch=0, sR_row=0,
+                             col_add=None, sL_batch=0, sL_col=0,
+                             stream=None) -> None:
+    """C <- alpha*A*B + beta*C + row_add[b,i] + col_add[b,j] through the C
+    ABI (beta 0 never reads C; None drops a vector term)."""
+    args = _ex_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row,
+                    sB_col, beta, C, sC_batch, sC_row, sC_col, row_add, sR_batch, sR_row,
+                    col_add, sL_batch, sL_col)
+    _check(load().sgemm_strided_batched_ex(*args, _stream(stream)))
+
+
+def sgemm_strided_batched_ex_path(batch, m, n, k, alpha,
+                                  A, sA_batch, sA_row, sA_col,
+                                  B, sB_batch, sB_row, sB_col,
+                                  beta,
+                                  C, sC_batch, sC_row, sC_col,
+                                  row_add=None, sR_batch=0, sR_row=0,
+                                  col_add=None, sL_batch=0, sL_col=0,
+                                  path=PATH_AUTO, stream=None) -> None:
+    """sgemm_strided_batched_ex with the kernel family forced."""
+    args = _ex_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row,
+                    sB_col, beta, C, sC_batch, sC_row, sC_col, row_add, sR_batch, sR_row,
+                    col_add, sL_batch, sL_col)
+    _check(load().sgemm_strided_batched_ex_path(*args, int(path), _stream(stream)))
+
+
+def sgemm_sqnorms(batch, count, length, X, sX_batch, sX_item, sX_elem, out, sO_batch, sO_item,
+                  stream=None) -> None:
+    """out[b,i] <- sum_p X[b,i,p]^2 through the C ABI."""
+    _check(load().sgemm_sqnorms(int(batch), int(count), int(length), _ptr(X), int(sX_batch),
+                                int(sX_item), int(sX_elem), _ptr(out), int(sO_batch),
+                                int(sO_item), _stream(stream)))
+
+
+def sgemm_pairwise_sqdist(batch, m, n, k,
+                          X, sX_batch, sX_row, sX_col,
+                          Y, sY_batch, sY_row, sY_col,
+                          D, sD_batch, sD_row, sD_col,
+                          workspace, workspace_floats, stream=None) -> None:
+    """D[b,i,j] <- |X[b,i,:] - Y[b,j,:]|^2 through the C ABI; `workspace`
+    holds batch*m + nY*n floats (nY = 1 when sY_batch == 0, else batch)."""
+    _check(load().sgemm_pairwise_sqdist(int(batch), int(m), int(n), int(k),
+                                        _ptr(X), int(sX_batch), int(sX_row), int(sX_col),
+                                        _ptr(Y), int(sY_batch), int(sY_row), int(sY_col),
+                                        _ptr(D), int(sD_batch), int(sD_row), int(sD_col),
+                                        _ptr(workspace), int(workspace_floats), _stream(stream)))
 
 
 def sgemm_plan_describe(batch, m, n, k, alpha,

@@ -10,7 +10,9 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cstring>
 #include <string>
 
@@ -64,11 +66,57 @@ sgemm::GemmArgs pack(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha
     a.A = reinterpret_cast<uintptr_t>(A); a.sA_batch = sA_batch; a.sA_row = sA_row; a.sA_col = sA_col;
     a.B = reinterpret_cast<uintptr_t>(B); a.sB_batch = sB_batch; a.sB_row = sB_row; a.sB_col = sB_col;
     a.accumulate = accumulate;
+    a.beta = accumulate ? 1.0f : 0.0f;
     a.C = reinterpret_cast<uintptr_t>(C); a.sC_batch = sC_batch; a.sC_row = sC_row; a.sC_col = sC_col;
     return a;
 }
 
 bool path_ok(int path) { return path >= SGEMM_PATH_AUTO && path <= SGEMM_PATH_GENERIC; }
+
+// Validate, plan and enqueue one product.
+int run_gemm(const sgemm::GemmArgs &a, int path, void *stream) {
+    std::string why;
+    int st = sgemm::validate(a, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    if (a.batch == 0 || a.m == 0 || a.n == 0) return SGEMM_OK;
+    int cus = 0;
+    st = current_cus(cus, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    sgemm::Plan plan;
+    st = sgemm::make_plan(a, static_cast<sgemm::Family>(path), cus, plan, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    st = sgemm::launch_plan(plan, static_cast<hipStream_t>(stream), why);
+    if (st != sgemm::kOk) return fail(st, why);
+    return SGEMM_OK;
+}
+
+bool ranges_meet(uintptr_t p, int64_t p_floats, uintptr_t q, int64_t q_floats) {
+    return p < q + 4u * uintptr_t(q_floats) && q < p + 4u * uintptr_t(p_floats);
+}
+
+// True if a [e0][e1] view with strides (s0, s1) gives every element its own
+// address: sorted by stride, each axis of extent > 1 must step past all the
+// smaller axes reach.
+bool distinct_2d(int64_t e0, int64_t s0, int64_t e1, int64_t s1) {
+    if (s0 > s1) { std::swap(e0, e1); std::swap(s0, s1); }
+    int64_t reach = 0;
+    if (e0 > 1) {
+        if (s0 <= reach) return false;
+        reach = (e0 - 1) * s0;
+    }
+    return e1 <= 1 || s1 > reach;
+}
+
+// Elements spanned by a [batch][count][len] view (0 if empty), or -1 on overflow.
+int64_t span3(int64_t e0, int64_t s0, int64_t e1, int64_t s1, int64_t e2, int64_t s2) {
+    if (e0 == 0 || e1 == 0 || e2 == 0) return 0;
+    int64_t a, b, c, t, r;
+    if (__builtin_mul_overflow(e0 - 1, s0, &a) || __builtin_mul_overflow(e1 - 1, s1, &b) ||
+        __builtin_mul_overflow(e2 - 1, s2, &c) || __builtin_add_overflow(a, b, &t) ||
+        __builtin_add_overflow(t, c, &r) || r == INT64_MAX)
+        return -1;
+    return r + 1;
+}
 
 }  // namespace
 
@@ -80,21 +128,99 @@ int sgemm_strided_batched_path(int64_t batch, int64_t m, int64_t n, int64_t k, f
                                int accumulate, float *C, int64_t sC_batch, int64_t sC_row,
                                int64_t sC_col, int path, void *stream) {
     if (!path_ok(path)) return fail(SGEMM_ERR_INVALID_PATH, "unknown path code");
+    return run_gemm(pack(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row,
+                         sB_col, accumulate, C, sC_batch, sC_row, sC_col),
+                    path, stream);
+}
+
+int sgemm_strided_batched_ex_path(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                                  const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                                  const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                                  float beta, float *C, int64_t sC_batch, int64_t sC_row,
+                                  int64_t sC_col, const float *row_add, int64_t sR_batch,
+                                  int64_t sR_row, const float *col_add, int64_t sL_batch,
+                                  int64_t sL_col, int path, void *stream) {
+    if (!path_ok(path)) return fail(SGEMM_ERR_INVALID_PATH, "unknown path code");
     sgemm::GemmArgs a = pack(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
-                             sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col);
+                             sB_row, sB_col, beta != 0.0f, C, sC_batch, sC_row, sC_col);
+    a.beta = beta;
+    a.row_add = reinterpret_cast<uintptr_t>(row_add); a.sR_batch = sR_batch; a.sR_row = sR_row;
+    a.col_add = reinterpret_cast<uintptr_t>(col_add); a.sL_batch = sL_batch; a.sL_col = sL_col;
+    return run_gemm(a, path, stream);
+}
+
+int sgemm_strided_batched_ex(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                             const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                             const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                             float beta, float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                             const float *row_add, int64_t sR_batch, int64_t sR_row,
+                             const float *col_add, int64_t sL_batch, int64_t sL_col, void *stream) {
+    return sgemm_strided_batched_ex_path(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B,
+                                         sB_batch, sB_row, sB_col, beta, C, sC_batch, sC_row,
+                                         sC_col, row_add, sR_batch, sR_row, col_add, sL_batch,
+                                         sL_col, SGEMM_PATH_AUTO, stream);
+}
+
+int sgemm_sqnorms(int64_t batch, int64_t count, int64_t len, const float *X, int64_t sX_batch,
+                  int64_t sX_item, int64_t sX_elem, float *out, int64_t sO_batch, int64_t sO_item,
+                  void *stream) {
+    if (batch < 0 || count < 0 || len < 0)
+        return fail(SGEMM_ERR_INVALID_SIZE, "negative size (batch, count, len must be >= 0)");
+    if (sX_batch < 0 || sX_item < 0 || sX_elem < 0 || sO_batch < 0 || sO_item < 0)
+        return fail(SGEMM_ERR_INVALID_STRIDE, "negative stride");
+    if (batch == 0 || count == 0) return SGEMM_OK;
+    if (!out || (len > 0 && !X)) return fail(SGEMM_ERR_NULL_POINTER, out ? "X is NULL" : "out is NULL");
+    const int64_t xs = span3(batch, sX_batch, count, sX_item, len, sX_elem);
+    const int64_t os = span3(batch, sO_batch, count, sO_item, 1, 0);
+    int64_t bytes;
+    if (xs < 0 || os < 0 || __builtin_mul_overflow(std::max(xs, os), int64_t(4), &bytes))
+        return fail(SGEMM_ERR_UNSUPPORTED, "an extent times its strides overflows int64");
+    if (!distinct_2d(batch, sO_batch, count, sO_item))
+        return fail(SGEMM_ERR_C_ALIAS, "out's strides map two norms to one element");
+    if (len > 0 && ranges_meet(reinterpret_cast<uintptr_t>(X), xs, reinterpret_cast<uintptr_t>(out), os))
+        return fail(SGEMM_ERR_C_ALIAS, "out overlaps X");
+    std::string why;
+    int st = sgemm::launch_sqnorms(batch, count, len, X, sX_batch, sX_item, sX_elem, out, sO_batch,
+                                   sO_item, static_cast<hipStream_t>(stream), why);
+    return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
+}
+
+int sgemm_pairwise_sqdist(int64_t batch, int64_t m, int64_t n, int64_t k, const float *X,
+                          int64_t sX_batch, int64_t sX_row, int64_t sX_col, const float *Y,
+                          int64_t sY_batch, int64_t sY_row, int64_t sY_col, float *D,
+                          int64_t sD_batch, int64_t sD_row, int64_t sD_col, float *workspace,
+                          int64_t workspace_floats, void *stream) {
+    // Validate the whole call first (as the product D <- -2 X Y^T), so that
+    // an error enqueues nothing.
+    sgemm::GemmArgs a = pack(batch, m, n, k, -2.0f, X, sX_batch, sX_row, sX_col, Y, sY_batch,
+                             sY_col, sY_row, 0, D, sD_batch, sD_row, sD_col);
     std::string why;
     int st = sgemm::validate(a, why);
     if (st != sgemm::kOk) return fail(st, why);
     if (batch == 0 || m == 0 || n == 0) return SGEMM_OK;
-    int cus = 0;
-    st = current_cus(cus, why);
-    if (st != sgemm::kOk) return fail(st, why);
-    sgemm::Plan plan;
-    st = sgemm::make_plan(a, static_cast<sgemm::Family>(path), cus, plan, why);
-    if (st != sgemm::kOk) return fail(st, why);
-    st = sgemm::launch_plan(plan, static_cast<hipStream_t>(stream), why);
-    if (st != sgemm::kOk) return fail(st, why);
-    return SGEMM_OK;
+    const int64_t ny = sY_batch == 0 ? 1 : batch;
+    int64_t need, ny_n;
+    if (__builtin_mul_overflow(batch, m, &need) || __builtin_mul_overflow(ny, n, &ny_n) ||
+        __builtin_add_overflow(need, ny_n, &need))
+        return fail(SGEMM_ERR_UNSUPPORTED, "workspace size overflows int64");
+    if (!workspace || workspace_floats < need)
+        return fail(SGEMM_ERR_WORKSPACE, "workspace needs batch*m + nY*n floats");
+    const uintptr_t ws = reinterpret_cast<uintptr_t>(workspace);
+    const int64_t xs = span3(batch, sX_batch, m, sX_row, k, sX_col);
+    const int64_t ys = span3(ny, sY_batch, n, sY_row, k, sY_col);
+    const int64_t ds = span3(batch, sD_batch, m, sD_row, n, sD_col);
+    if ((k > 0 && (ranges_meet(ws, need, reinterpret_cast<uintptr_t>(X), xs) ||
+                   ranges_meet(ws, need, reinterpret_cast<uintptr_t>(Y), ys))) ||
+        ranges_meet(ws, need, reinterpret_cast<uintptr_t>(D), ds))
+        return fail(SGEMM_ERR_C_ALIAS, "workspace overlaps X, Y or D");
+    float *nx = workspace, *nyv = workspace + batch * m;
+    st = sgemm_sqnorms(batch, m, k, X, sX_batch, sX_row, sX_col, nx, m, 1, stream);
+    if (st != SGEMM_OK) return st;
+    st = sgemm_sqnorms(ny, n, k, Y, sY_batch, sY_row, sY_col, nyv, n, 1, stream);
+    if (st != SGEMM_OK) return st;
+    a.row_add = reinterpret_cast<uintptr_t>(nx); a.sR_batch = m; a.sR_row = 1;
+    a.col_add = reinterpret_cast<uintptr_t>(nyv); a.sL_batch = sY_batch == 0 ? 0 : n; a.sL_col = 1;
+    return run_gemm(a, SGEMM_PATH_AUTO, stream);
 }
 
 int sgemm_strided_batched(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
@@ -164,6 +290,7 @@ const char *sgemm_status_string(int status) {
     case SGEMM_ERR_UNSUPPORTED: return "SGEMM_ERR_UNSUPPORTED: extent or offset overflow";
     case SGEMM_ERR_HIP: return "SGEMM_ERR_HIP: HIP runtime error";
     case SGEMM_ERR_INVALID_PATH: return "SGEMM_ERR_INVALID_PATH: unknown path code";
+    case SGEMM_ERR_WORKSPACE: return "SGEMM_ERR_WORKSPACE: workspace missing or too small";
     default: return "unknown sgemm status";
     }
 }

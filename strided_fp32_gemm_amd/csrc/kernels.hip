@@ -1,6 +1,7 @@
 // kernels.hip -- the generic kernel and the launch dispatch.
 //
-// C[b,i,j] <- alpha * sum_p A[b,i,p] B[b,p,j] (+ C[b,i,j]); operands are
+// C[b,i,j] <- alpha * sum_p A[b,i,p] B[b,p,j] (+ beta C[b,i,j] + row[b,i] +
+// col[b,j], the general epilogue of epilogue.hpp); operands are
 // addressed through (batch, row, col) element strides (StaleyNET "GPU
 // Implementation", section "The matrix product").  The matrix-core kernels
 // live in mfma_kernel.hpp (LDS-tiled) and wave_kernel.hpp (direct
@@ -8,8 +9,10 @@
 // offsets exceed the 32-bit buffer range, and launch_plan().
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <string>
 
+#include "epilogue.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
 
@@ -62,19 +65,93 @@ __global__ __launch_bounds__(256) void sgemm_generic(GenericArgs p) {
             __syncthreads();
         }
         float *C = p.C + b * p.sC_b;
+        const Epilogue &e = p.epi;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const long long i = i0 + ty + 16 * r;
             if (i >= p.m) continue;
+            const float rv = e.has_row ? e.row[b * e.sR_b + i * e.sR_m] : 0.0f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const long long j = j0 + tx + 16 * c;
                 if (j >= p.n) continue;
                 float *dst = C + i * p.sC_m + j * p.sC_n;
-                *dst = p.accumulate ? __builtin_fmaf(p.alpha, acc[r][c], *dst) : p.alpha * acc[r][c];
+                const float cv = e.has_col ? e.col[b * e.sL_b + j * e.sL_n] : 0.0f;
+                const float old = p.accumulate ? *dst : 0.0f;
+                *dst = epilogue_value(p.alpha, acc[r][c], p.accumulate != 0, e.beta, old, e.has_row != 0,
+                                      rv, e.has_col != 0, cv);
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Squared norms out[b,i] = sum_p X[b,i,p]^2 (the terms a distance table adds
+// to its product).  Vectors whose elements are contiguous: one wavefront per
+// vector, lanes striding by 64 elements, then a fixed butterfly over the
+// wavefront.  Otherwise one thread per vector, elements in order, so that
+// neighbouring threads read neighbouring items.  fp32 sums in a fixed order
+// either way: the same bits on every run.  Grid-stride loops, 64-bit
+// addressing; every loop bound is uniform across a wavefront.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sqnorms_contiguous(const float *X, long long sX_b, long long sX_i,
+                                                          float *out, long long sO_b, long long sO_i,
+                                                          long long batch, long long count, long long len) {
+    const int lane = threadIdx.x & 63;
+    const long long total = batch * count;
+    for (long long v = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); v < total;
+         v += (long long)gridDim.x * 4) {
+        const long long b = v / count, i = v - b * count;
+        const float *x = X + b * sX_b + i * sX_i;
+        float sq = 0.0f;
+        for (long long e = lane; e < len; e += 64) {
+            const float t = x[e];
+            sq = __builtin_fmaf(t, t, sq);
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off, 64);
+        if (lane == 0) out[b * sO_b + i * sO_i] = sq;
+    }
+}
+
+__global__ __launch_bounds__(256) void sqnorms_strided(const float *X, long long sX_b, long long sX_i,
+                                                       long long sX_e, float *out, long long sO_b,
+                                                       long long sO_i, long long batch, long long count,
+                                                       long long len) {
+    const long long total = batch * count;
+    for (long long v = (long long)blockIdx.x * 256 + threadIdx.x; v < total; v += (long long)gridDim.x * 256) {
+        const long long b = v / count, i = v - b * count;
+        const float *x = X + b * sX_b + i * sX_i;
+        float sq = 0.0f;
+        for (long long e = 0; e < len; ++e) {
+            const float t = x[e * sX_e];
+            sq = __builtin_fmaf(t, t, sq);
+        }
+        out[b * sO_b + i * sO_i] = sq;
+    }
+}
+
+int launch_sqnorms(long long batch, long long count, long long len, const float *X, long long sX_b,
+                   long long sX_i, long long sX_e, float *out, long long sO_b, long long sO_i,
+                   hipStream_t stream, std::string &why) {
+    const long long total = batch * count;
+    if (total == 0) return kOk;
+    (void)hipGetLastError();
+    if (sX_e == 1 && len >= 64) {
+        const long long grid = std::min<long long>((total + 3) / 4, 65536);
+        hipLaunchKernelGGL(sqnorms_contiguous, dim3(unsigned(grid)), dim3(256), 0, stream, X, sX_b, sX_i,
+                           out, sO_b, sO_i, batch, count, len);
+    } else {
+        const long long grid = std::min<long long>((total + 255) / 256, 65536);
+        hipLaunchKernelGGL(sqnorms_strided, dim3(unsigned(grid)), dim3(256), 0, stream, X, sX_b, sX_i,
+                           sX_e, out, sO_b, sO_i, batch, count, len);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        why = std::string("kernel launch failed: ") + hipGetErrorString(e);
+        return kErrHip;
+    }
+    return kOk;
 }
 
 namespace {
@@ -127,6 +204,18 @@ const PersistTable &persist_table() {
 
 }  // namespace
 
+Epilogue make_epilogue(const Plan &p) {
+    Epilogue e;
+    e.beta = p.beta;
+    e.row = reinterpret_cast<const float *>(p.row_add);
+    e.col = reinterpret_cast<const float *>(p.col_add);
+    e.sR_b = p.sR_b; e.sR_m = p.sR_m; e.sL_b = p.sL_b; e.sL_n = p.sL_n;
+    e.has_row = p.row_add ? 1 : 0;
+    e.has_col = p.col_add ? 1 : 0;
+    e.col_vec4 = p.col_vec4 ? 1 : 0;
+    return e;
+}
+
 int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
     if (p.empty) return kOk;
     (void)hipGetLastError();  // clear a stale error left by unrelated work
@@ -141,6 +230,7 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         g.m = p.m; g.n = p.n; g.k = p.k; g.batch = p.batch;
         g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n;
         g.alpha = p.alpha; g.accumulate = p.accumulate;
+        g.epi = make_epilogue(p);
         hipLaunchKernelGGL(sgemm_generic, dim3(unsigned(p.workgroups)), dim3(256), 0, stream, g);
     } else {
         MfmaArgs a;
@@ -157,6 +247,7 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         a.accumulate = p.accumulate;
         a.c_vec4 = p.c_vec4 ? 1 : 0;
         a.alpha = p.alpha;
+        a.epi = make_epilogue(p);
         if (p.persist)
             persist_table().f[p.tile][p.a_kfast][p.b_kfast][p.accumulate != 0](
                 a, unsigned(p.workgroups), stream);

@@ -9,6 +9,17 @@
 
 namespace sgemm {
 
+// The general epilogue's extra terms: C <- alpha*acc + beta*C_old + row[i] +
+// col[j], the vectors at row + b*sR_b + i*sR_m and col + b*sL_b + j*sL_n.
+struct Epilogue {
+    float beta;
+    const float *row;
+    const float *col;
+    long long sR_b, sR_m, sL_b, sL_n;
+    int has_row, has_col;
+    int col_vec4;   // col is contiguous and 16-byte aligned per row quad (one 16-byte load)
+};
+
 // Arguments of the MFMA kernels (kernel terms: A m x k, B k x n, C m x n).
 // 64-bit strides place each workgroup's base; offsets inside a workgroup's
 // slice fit 32 bits (checked by the planner).
@@ -23,9 +34,10 @@ struct MfmaArgs {
     int tiles_m, tiles_n;
     int total_tiles;   // batch * tiles_m * tiles_n (the persistent kernel's loop bound)
     TileMap map;       // tile id -> (batch, tile row, tile column)
-    int accumulate;
+    int accumulate;   // beta != 0: C is read
     int c_vec4;   // C rows take 16-byte stores (n-contiguous, aligned, n % 4 == 0)
     float alpha;
+    Epilogue epi;
 };
 
 // Arguments of the generic kernel: everything 64-bit.
@@ -40,6 +52,7 @@ struct GenericArgs {
     long long tiles_m, tiles_n;
     float alpha;
     int accumulate;
+    Epilogue epi;
 };
 
 // Launchers indexed [tile][A k-fast][B k-fast][A 16-byte loads]
@@ -76,6 +89,11 @@ void fill_wave_3(WaveTable &);
 void fill_persist_0(PersistTable &);
 void fill_persist_1(PersistTable &);
 void fill_persist_2(PersistTable &);
+
+// Squared norms of batch x count vectors of length len (see sgemm_sqnorms).
+int launch_sqnorms(long long batch, long long count, long long len, const float *X, long long sX_b,
+                   long long sX_i, long long sX_e, float *out, long long sO_b, long long sO_i,
+                   hipStream_t stream, std::string &why);
 
 // Enqueues the plan on `stream`.  Returns kOk, or kErrHip with `why` set when
 // the runtime rejects the launch.

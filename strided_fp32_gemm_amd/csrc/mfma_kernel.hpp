@@ -40,6 +40,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "epilogue.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
 
@@ -374,13 +375,28 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
         }
     }
 
-    // Epilogue: C = alpha*acc, or C_old + alpha*acc as one fused
-    // multiply-add when accumulating.
+    // Epilogue (epilogue_value): C = alpha*acc, or one fused multiply-add
+    // onto beta*C_old (+ the row and column terms of the general epilogue).
+    // The vector terms come through their own buffer resources with the same
+    // out-of-range convention as C.
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(p.C + (long long)b * p.sC_b + (long long)i0 * p.sC_m + (long long)j0 * p.sC_n);
     const unsigned sCm = unsigned(p.sC_m), sCn = unsigned(p.sC_n);
     const float alpha = p.alpha;
     const bool accumulate = p.accumulate != 0;
+    const Epilogue &ep = p.epi;
+    const bool has_row = ep.has_row != 0, has_col = ep.has_col != 0;
+    const __amdgpu_buffer_rsrc_t rR =
+        make_rsrc(has_row ? ep.row + (long long)b * ep.sR_b + (long long)i0 * ep.sR_m : p.C);
+    const __amdgpu_buffer_rsrc_t rL =
+        make_rsrc(has_col ? ep.col + (long long)b * ep.sL_b + (long long)j0 * ep.sL_n : p.C);
+    const unsigned sRm = unsigned(ep.sR_m), sLn = unsigned(ep.sL_n);
+    auto row_term = [&](unsigned row) {
+        return has_row ? load1(rR, row < m_left ? row * sRm * 4u : kOutOfRange) : 0.0f;
+    };
+    auto col_term = [&](unsigned col) {
+        return has_col ? load1(rL, col < n_left ? col * sLn * 4u : kOutOfRange) : 0.0f;
+    };
     constexpr int R = M::kRegs;
     if (p.c_vec4) {
         // Staged: each wavefront writes its WM x WN sub-tile to its own LDS
@@ -416,10 +432,23 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
             const unsigned grow = unsigned(wm * WM + row), gcol = unsigned(wn * WN + c4);
             const unsigned off = (grow < m_left && gcol < n_left) ? (grow * sCm + gcol) * 4u : kOutOfRange;
             f32x4 o;
-            if (accumulate) {
+            if (has_row || has_col) {
+                const f32x4 old = accumulate ? load4(rC, off) : f32x4{};
+                const float rv = row_term(grow);
+                f32x4 cv;
+                if (ep.col_vec4) {
+                    cv = load4(rL, gcol < n_left ? gcol * 4u : kOutOfRange);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cv[e] = col_term(gcol + unsigned(e));
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = epilogue_value(alpha, v[e], accumulate, ep.beta, old[e], has_row, rv, has_col, cv[e]);
+            } else if (accumulate) {
                 const f32x4 old = load4(rC, off);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(alpha, v[e], old[e]);
+                for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(alpha, v[e], ep.beta * old[e]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = alpha * v[e];
@@ -441,12 +470,21 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
                 const unsigned row = unsigned(arow(a, M::row(r, lh)));
                 off[r] = (row < m_left && col < n_left) ? (row * sCm + col * sCn) * 4u : kOutOfRange;
             }
-            if (accumulate) {
+            if (has_row || has_col) {
+                const float cv = col_term(col);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float old = accumulate ? load1(rC, off[r]) : 0.0f;
+                    store1(rC, off[r], epilogue_value(alpha, acc[a][c][r], accumulate, ep.beta, old, has_row,
+                                                      row_term(unsigned(arow(a, M::row(r, lh)))), has_col, cv));
+                }
+            } else if (accumulate) {
                 float old[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) old[r] = load1(rC, off[r]);
 #pragma unroll
-                for (int r = 0; r < R; ++r) store1(rC, off[r], __builtin_fmaf(alpha, acc[a][c][r], old[r]));
+                for (int r = 0; r < R; ++r)
+                    store1(rC, off[r], __builtin_fmaf(alpha, acc[a][c][r], ep.beta * old[r]));
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) store1(rC, off[r], alpha * acc[a][c][r]);

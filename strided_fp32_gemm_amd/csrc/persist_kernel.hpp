@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kPersistTiles[P].wgm * kPersistTiles[P].wgn * 64) v
     // fetched at the start of the step that multiplies it, one step before
     // its stores, and ahead of the operand requests issued in that step.
     constexpr int NB = TM * TN;
-    const float alpha = p.alpha;
+    const float alpha = p.alpha, beta = p.epi.beta;  // no vector terms here (the planner checks)
     auto offset = [&](const Tile &t, int a, int c) {
         const unsigned row = unsigned(wm * WM + a * 16 + lr);
         const unsigned col = unsigned(wn * WN + c * 16 + 4 * lh);
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kPersistTiles[P].wgm * kPersistTiles[P].wgn * 64) v
     auto store_block = [&](const Tile &t, const f32x4 (&acc)[NB], const f32x4 (&old)[NB], int x) {
         f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = ACC ? __builtin_fmaf(alpha, acc[x][e], old[x][e]) : alpha * acc[x][e];
+        for (int e = 0; e < 4; ++e) o[e] = ACC ? __builtin_fmaf(alpha, acc[x][e], beta * old[x][e]) : alpha * acc[x][e];
         store4(t.rC, offset(t, x / TN, x % TN), o);
     };
 

@@ -91,6 +91,10 @@ int validate(const GemmArgs &a, std::string &why) {
             why = std::string("negative stride ") + names[i];
             return kErrStride;
         }
+    if ((a.row_add && (a.sR_batch < 0 || a.sR_row < 0)) || (a.col_add && (a.sL_batch < 0 || a.sL_col < 0))) {
+        why = "negative stride of row_add or col_add";
+        return kErrStride;
+    }
     int64_t bm, work;
     if (!mul64(a.batch, a.m, bm) || !mul64(bm, a.n, work)) {
         why = "batch*m*n overflows int64";
@@ -111,8 +115,11 @@ int validate(const GemmArgs &a, std::string &why) {
         lastA = last_offset(a.batch, a.sA_batch, a.m, a.sA_row, a.k, a.sA_col);
         lastB = last_offset(a.batch, a.sB_batch, a.k, a.sB_row, a.n, a.sB_col);
     }
+    int64_t lastR = a.row_add ? last_offset(a.batch, a.sR_batch, a.m, a.sR_row, 1, 0) : 0;
+    int64_t lastL = a.col_add ? last_offset(a.batch, a.sL_batch, a.n, a.sL_col, 1, 0) : 0;
     int64_t bytes;
-    if (lastC < 0 || lastA < 0 || lastB < 0 || !mul64(std::max({lastA, lastB, lastC}) + 1, 4, bytes)) {
+    if (lastC < 0 || lastA < 0 || lastB < 0 || lastR < 0 || lastL < 0 ||
+        !mul64(std::max({lastA, lastB, lastC, lastR, lastL}) + 1, 4, bytes)) {
         why = "an operand's extent times its strides overflows int64";
         return kErrUnsupported;
     }
@@ -134,6 +141,11 @@ int validate(const GemmArgs &a, std::string &why) {
         why = "C's address range overlaps A or B";
         return kErrAlias;
     }
+    if ((a.row_add && ranges_overlap(a.C, lastC, a.row_add, lastR)) ||
+        (a.col_add && ranges_overlap(a.C, lastC, a.col_add, lastL))) {
+        why = "C's address range overlaps row_add or col_add";
+        return kErrAlias;
+    }
     return kOk;
 }
 
@@ -146,7 +158,8 @@ bool tile_fits(const Plan &p, int bm, int bn) {
     // and their offsets are never formed from valid rows.)
     int64_t kspan = p.k;
     return fits_buffer(bm, p.sA_m, kspan, p.sA_k) && fits_buffer(kspan, p.sB_k, bn, p.sB_n) &&
-           fits_buffer(bm, p.sC_m, bn, p.sC_n);
+           fits_buffer(bm, p.sC_m, bn, p.sC_n) && (!p.row_add || fits_buffer(bm, p.sR_m, 1, 0)) &&
+           (!p.col_add || fits_buffer(1, 0, bn, p.sL_n));
 }
 
 // Estimated cycles of a launch.  Tiles are spread over the CUs and up to
@@ -229,7 +242,8 @@ double persist_cost(const Plan &p, const PersistCfg &t, int num_cus, int64_t gri
 }
 
 bool persist_serves(const Plan &p, const PersistCfg &t) {
-    return p.vec_a == 4 && p.vec_b == 4 && p.c_vec4 && p.k >= 1 && p.k <= t.kmax;
+    return p.vec_a == 4 && p.vec_b == 4 && p.c_vec4 && p.k >= 1 && p.k <= t.kmax && !p.row_add &&
+           !p.col_add;
 }
 
 }  // namespace
@@ -239,7 +253,9 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
     if (st != kOk) return st;
     p = Plan();
     p.batch = a.batch; p.m = a.m; p.n = a.n; p.k = a.k;
-    p.alpha = a.alpha; p.accumulate = a.accumulate ? 1 : 0;
+    p.alpha = a.alpha; p.beta = a.beta; p.accumulate = a.beta != 0.0f ? 1 : 0;
+    p.row_add = a.row_add; p.sR_b = a.sR_batch; p.sR_m = a.sR_row;
+    p.col_add = a.col_add; p.sL_b = a.sL_batch; p.sL_n = a.sL_col;
     if (a.batch == 0 || a.m == 0 || a.n == 0) {
         p.empty = true;
         p.kernel_name = "none";
@@ -263,10 +279,14 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         p.A = p.B; p.sA_b = p.sB_b; p.sA_m = p.sB_n; p.sA_k = p.sB_k;
         p.B = A0; p.sB_b = a_b; p.sB_k = a_k; p.sB_n = a_m;
         std::swap(p.sC_m, p.sC_n);
+        // Rows of C^T are the columns of C: the two vector terms trade places.
+        std::swap(p.row_add, p.col_add);
+        std::swap(p.sR_b, p.sL_b);
+        std::swap(p.sR_m, p.sL_n);
     }
     // Broadcast strides of extent-1 axes never matter; zero them so that
     // alignment checks see only strides that are used.
-    if (p.batch == 1) { p.sA_b = 0; p.sB_b = 0; p.sC_b = 0; }
+    if (p.batch == 1) { p.sA_b = 0; p.sB_b = 0; p.sC_b = 0; p.sR_b = 0; p.sL_b = 0; }
 
     p.a_kfast = cols_fast(p.m, p.sA_m, p.k, p.sA_k);
     p.b_kfast = !cols_fast(p.k, p.sB_k, p.n, p.sB_n);
@@ -277,6 +297,8 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
 
     p.c_vec4 = p.sC_n == 1 && p.n % 4 == 0 && p.C % 16 == 0 && p.sC_m % 4 == 0 &&
                (p.batch == 1 || p.sC_b % 4 == 0);
+    p.col_vec4 = p.c_vec4 && p.col_add && p.sL_n == 1 && p.col_add % 16 == 0 &&
+                 (p.batch == 1 || p.sL_b % 4 == 0);
 
     const int64_t i32max = (int64_t(1) << 31) - 1;
     bool small_enough = p.m <= i32max && p.n <= i32max && p.k <= i32max && p.batch <= i32max;
@@ -342,7 +364,7 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         if (best_persist) p.workgroups = persist_grid(p, kPersistTiles[best], num_cus, p.workgroups);
         p.kernel_name = std::string(best_wave ? "wave_" : best_persist ? "persist_" : "mfma_") + name +
                         (p.a_kfast ? "_ak" : "_am") + (p.b_kfast ? "_bk" : "_bn") +
-                        (p.accumulate ? "_acc" : "");
+                        (p.accumulate ? "_acc" : "") + (p.row_add || p.col_add ? "_vec" : "");
     } else {
         p.family = Family::Generic;
         p.tile = -1;
@@ -351,7 +373,8 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         p.tiles_n = (p.n + 63) / 64;
         int64_t tiles = p.batch * p.tiles_m * p.tiles_n;
         p.workgroups = std::min<int64_t>(tiles, 65536);
-        p.kernel_name = std::string("generic_t64x64") + (p.accumulate ? "_acc" : "");
+        p.kernel_name = std::string("generic_t64x64") + (p.accumulate ? "_acc" : "") +
+                        (p.row_add || p.col_add ? "_vec" : "");
     }
     return kOk;
 }

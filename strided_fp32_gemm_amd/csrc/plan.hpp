@@ -15,8 +15,13 @@ struct GemmArgs {
     float alpha;
     uintptr_t A; int64_t sA_batch, sA_row, sA_col;
     uintptr_t B; int64_t sB_batch, sB_row, sB_col;
-    int accumulate;
+    int accumulate;            // beta != 0
     uintptr_t C; int64_t sC_batch, sC_row, sC_col;
+    // General epilogue: C <- alpha*A*B + beta*C + row_add[b,i] + col_add[b,j];
+    // a zero vector pointer drops its term.
+    float beta = 0.0f;
+    uintptr_t row_add = 0; int64_t sR_batch = 0, sR_row = 0;
+    uintptr_t col_add = 0; int64_t sL_batch = 0, sL_col = 0;
 };
 
 enum class Family : int { Auto = 0, Mfma = 1, Wave = 2, Generic = 3 };
@@ -190,7 +195,11 @@ struct Plan {
     bool c_vec4 = false;       // C rows take 16-byte stores
     int64_t batch = 0, m = 0, n = 0, k = 0;
     float alpha = 1.0f;
-    int accumulate = 0;
+    int accumulate = 0;        // beta != 0: C is read
+    float beta = 0.0f;
+    uintptr_t row_add = 0, col_add = 0;   // per-row / per-column terms (kernel terms, after any rewrite)
+    int64_t sR_b = 0, sR_m = 0, sL_b = 0, sL_n = 0;
+    bool col_vec4 = false;     // column term read 4 at a time (with c_vec4)
     uintptr_t A = 0, B = 0, C = 0;
     int64_t sA_b = 0, sA_m = 0, sA_k = 0;
     int64_t sB_b = 0, sB_k = 0, sB_n = 0;

@@ -133,39 +133,56 @@ __global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
         if (g < NG) multiply(fa0, fb0);
     }
 
-    // Epilogue: lane (lr, lh) of block (a, c) holds C[a*16 + lr][c*16 + 4*lh + r].
+    // Epilogue: lane (lr, lh) of block (a, c) holds C[a*16 + lr][c*16 + 4*lh + r]
+    // (epilogue_value; the general epilogue's vector terms come through
+    // their own buffer resources, out-of-range convention as for C).
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(p.C + (long long)b * p.sC_b + (long long)i0 * p.sC_m + (long long)j0 * p.sC_n);
     const unsigned sCm = unsigned(p.sC_m), sCn = unsigned(p.sC_n);
     const float alpha = p.alpha;
     const bool accumulate = p.accumulate != 0;
+    const Epilogue &ep = p.epi;
+    const bool has_row = ep.has_row != 0, has_col = ep.has_col != 0;
+    const __amdgpu_buffer_rsrc_t rR =
+        make_rsrc(has_row ? ep.row + (long long)b * ep.sR_b + (long long)i0 * ep.sR_m : p.C);
+    const __amdgpu_buffer_rsrc_t rL =
+        make_rsrc(has_col ? ep.col + (long long)b * ep.sL_b + (long long)j0 * ep.sL_n : p.C);
+    const unsigned sRm = unsigned(ep.sR_m), sLn = unsigned(ep.sL_n);
+    auto col_term = [&](unsigned col) {
+        return has_col ? load1(rL, col < n_left ? col * sLn * 4u : kOutOfRange) : 0.0f;
+    };
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
         const unsigned row = unsigned(a * 16 + lr);
         const bool rv = row < m_left;
+        const float rterm = has_row ? load1(rR, rv ? row * sRm * 4u : kOutOfRange) : 0.0f;
 #pragma unroll
         for (int c = 0; c < TN; ++c) {
             const unsigned col = unsigned(c * 16 + 4 * lh);
             const f32x4 v = acc[a][c];
             if (p.c_vec4) {
                 const unsigned off = (rv && col < n_left) ? (row * sCm + col) * 4u : kOutOfRange;
-                f32x4 o;
-                if (accumulate) {
-                    const f32x4 old = load4(rC, off);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(alpha, v[e], old[e]);
+                const f32x4 old = accumulate ? load4(rC, off) : f32x4{};
+                f32x4 cv;
+                if (has_col && ep.col_vec4) {
+                    cv = load4(rL, col < n_left ? col * 4u : kOutOfRange);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = alpha * v[e];
+                    for (int e = 0; e < 4; ++e) cv[e] = col_term(col + unsigned(e));
                 }
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = epilogue_value(alpha, v[e], accumulate, ep.beta, old[e], has_row, rterm, has_col, cv[e]);
                 store4(rC, off, o);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const unsigned ce = col + unsigned(e);
                     const unsigned off = (rv && ce < n_left) ? (row * sCm + ce * sCn) * 4u : kOutOfRange;
-                    const float o = accumulate ? __builtin_fmaf(alpha, v[e], load1(rC, off)) : alpha * v[e];
-                    store1(rC, off, o);
+                    const float old = accumulate ? load1(rC, off) : 0.0f;
+                    store1(rC, off, epilogue_value(alpha, v[e], accumulate, ep.beta, old, has_row, rterm,
+                                                   has_col, col_term(ce)));
                 }
             }
         }

@@ -34,11 +34,20 @@ ROOT_SEED = 2024
 
 # Benchmark workloads.
 WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
-             "linear_bwd_dx", "linear_bwd_dw", "linear_xT")
+             "linear_bwd_dx", "linear_bwd_dw", "linear_xT", "linear_bias", "sqdist")
+# Entry point each workload goes through: "plain" (sgemm_strided_batched),
+# "ex" (sgemm_strided_batched_ex) or "dist" (sgemm_pairwise_sqdist).
+KINDS = {"linear_bias": "ex", "sqdist": "dist"}
+
+
+def kind(name: str) -> str:
+    return KINDS.get(name, "plain")
+
+
 # Children of the root seed, in spawn order (the two halves of the linear
 # layer's backward pass share one draw of dy, W and x).
 SEED_NAMES = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
-              "linear_bwd", "linear_xT")
+              "linear_bwd", "linear_xT", "linear_bias", "sqdist")
 
 
 @dataclasses.dataclass
@@ -62,8 +71,18 @@ class Operand:
 
 
 @dataclasses.dataclass
+class Vector:
+    """A flat float32 host storage plus the (batch, index) strides of a
+    batch of vectors over it (the general epilogue's row / column terms)."""
+    storage: np.ndarray
+    strides: tuple
+
+
+@dataclasses.dataclass
 class Problem:
-    """One call: C <- alpha*A*B (+C) over batch x (m x k)(k x n)."""
+    """One call: C <- alpha*A*B (+C) over batch x (m x k)(k x n), or, when
+    `beta`, `row` or `col` is given, the general epilogue C <- alpha*A*B +
+    beta*C + row[b,i] + col[b,j] (sgemm_strided_batched_ex)."""
     name: str
     batch: int
     m: int
@@ -75,10 +94,31 @@ class Problem:
     B: Operand
     C: Operand          # storage holds C_old (read only when accumulating)
     notes: str = ""
+    beta: float = None  # None: 1 if accumulate else 0, plain entry point
+    row: Vector = None
+    col: Vector = None
 
     @property
     def flops(self) -> int:
         return 2 * self.batch * self.m * self.n * self.k
+
+    @property
+    def is_ex(self) -> bool:
+        return self.beta is not None or self.row is not None or self.col is not None
+
+    @property
+    def beta_value(self) -> float:
+        return self.beta if self.beta is not None else (1.0 if self.accumulate else 0.0)
+
+    def ex_call_args(self, a, b, c, r=None, l=None):
+        """Positional argument list of sgemm_strided_batched_ex (without the
+        stream) with the storages replaced by a, b, c and the vectors by r, l
+        (None when the problem has no such term)."""
+        sr = self.row.strides if self.row is not None else (0, 0)
+        sl = self.col.strides if self.col is not None else (0, 0)
+        return [self.batch, self.m, self.n, self.k, self.alpha,
+                a, *self.A.strides, b, *self.B.strides, self.beta_value, c, *self.C.strides,
+                r, *sr, l, *sl]
 
     def call_args(self, a, b, c):
         """Positional argument list of the entry point with the three storages
@@ -237,6 +277,62 @@ def linear_xT() -> Problem:
                    Operand(xT, (0, 1, 2048)), Operand(W, (0, 1, 960)), Operand(y, (0, 2560, 1)))
 
 
+def linear_bias() -> Problem:
+    """The linear layer with its bias fused into the product's epilogue
+    ("PyTorch demystified 3", "Comparison with cuBLAS and outlook"): y = x W^T
+    + b, x [2048][960] N(0,1), W stored [2560][960] N(0,0.02) read
+    transposed, b [2560] N(0,1) added to every row (a column term)."""
+    gx, gw, gb = _gens("linear_bias", 3)
+    x = _f32(gx.normal(0.0, 1.0, (2048, 960)))
+    W = _f32(gw.normal(0.0, 0.02, (2560, 960)))
+    bias = _f32(gb.normal(0.0, 1.0, 2560))
+    y = np.zeros(2048 * 2560, np.float32)
+    return Problem("linear_bias", 1, 2048, 2560, 960, 1.0, False,
+                   Operand(x, (0, 960, 1)), Operand(W, (0, 1, 960)), Operand(y, (0, 2560, 1)),
+                   beta=0.0, col=Vector(bias, (0, 1)))
+
+
+@dataclasses.dataclass
+class DistProblem:
+    """Squared distances D[b,i,j] = |X[b,i,:] - Y[b,j,:]|^2 between the rows
+    of X [batch][m][k] and of Y [batch][n][k] (sgemm_pairwise_sqdist).  The
+    FLOP count is the product's, 2*batch*m*n*k."""
+    name: str
+    batch: int
+    m: int
+    n: int
+    k: int
+    X: Operand
+    Y: Operand
+    D: Operand
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.m * self.n * self.k
+
+    @property
+    def workspace_floats(self) -> int:
+        ny = 1 if self.Y.strides[0] == 0 else self.batch
+        return self.batch * self.m + ny * self.n
+
+    def call_args(self, x, y, d, ws):
+        return [self.batch, self.m, self.n, self.k, x, *self.X.strides, y, *self.Y.strides,
+                d, *self.D.strides, ws, self.workspace_floats]
+
+
+def sqdist() -> DistProblem:
+    """The tokenizer's distance table (StaleyNET "GPU Implementation", "The
+    matrix product"): 4 x 4096 frame vectors of 512 features, N(0,1), against
+    one shared codebook of 1024 entries, N(0,1) (batch stride 0).  The sizes
+    are assumed; the page gives none."""
+    gx, gy = _gens("sqdist", 2)
+    X = _f32(gx.normal(0.0, 1.0, (4, 4096, 512)))
+    Y = _f32(gy.normal(0.0, 1.0, (1024, 512)))
+    D = np.zeros(4 * 4096 * 1024, np.float32)
+    return DistProblem("sqdist", 4, 4096, 1024, 512, Operand(X, (4096 * 512, 512, 1)),
+                       Operand(Y, (0, 512, 1)), Operand(D, (4096 * 1024, 1024, 1)))
+
+
 BUILDERS = {
     "square64": square64,
     "linear_xWt": linear_xWt,
@@ -247,10 +343,12 @@ BUILDERS = {
     "linear_bwd_dx": linear_bwd_dx,
     "linear_bwd_dw": linear_bwd_dw,
     "linear_xT": linear_xT,
+    "linear_bias": linear_bias,
+    "sqdist": sqdist,
 }
 
 
-def workload(name: str) -> Problem:
+def workload(name: str):
     return BUILDERS[name]()
 
 

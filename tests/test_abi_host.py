@@ -193,3 +193,29 @@ def test_persistent_tile_serves_short_k_only(monkeypatch):
     assert plan(120, 512, 512, 64, (512 * 64, 64, 1), (512 * 64, 1, 64), (512 * 512, 512, 1))["workgroups"] == 7
     monkeypatch.setenv("SGEMM_PERSIST_WGS", "100000")
     assert plan(1, 64, 128, 64, (0, 64, 1), (0, 1, 64), (0, 128, 1))["workgroups"] == 2
+
+
+def test_extended_entry_points_validate_before_the_device():
+    """The general epilogue, the squared norms and the distance table reject
+    bad arguments with a status before any device call (no GPU here)."""
+    ex = lambda **kw: sg.sgemm_strided_batched_ex(
+        kw.get("batch", 1), 8, 8, 4, 1.0, PA, 0, 4, 1, PB, 0, 8, 1, kw.get("beta", 0.0),
+        PC, 0, 8, 1, kw.get("row"), *kw.get("sR", (0, 1)), kw.get("col"), *kw.get("sL", (0, 1)))
+    assert status_of(lambda: ex(row=PA + (1 << 20), sR=(0, -1))) == -2
+    assert status_of(lambda: ex(col=PC + 4, sL=(0, 1))) == -4          # column term inside C
+    assert status_of(lambda: ex(row=PC - 16, sR=(0, 1))) == -4         # row term reaching into C
+    assert status_of(lambda: ex(col=PA, sL=(1 << 62, 1), batch=4)) == -5
+    sq = lambda *a: sg.sgemm_sqnorms(*a)
+    assert status_of(lambda: sq(1, 4, -1, PA, 0, 4, 1, PC, 0, 1)) == -1
+    assert status_of(lambda: sq(1, 4, 4, PA, 0, -4, 1, PC, 0, 1)) == -2
+    assert status_of(lambda: sq(1, 4, 4, None, 0, 4, 1, PC, 0, 1)) == -3
+    assert status_of(lambda: sq(2, 4, 4, PA, 16, 4, 1, PC, 2, 1)) == -4   # outputs collide
+    assert status_of(lambda: sq(1, 4, 4, PA, 0, 4, 1, PA + 8, 0, 1)) == -4  # out inside X
+    sg.sgemm_sqnorms(0, 4, 4, None, 0, 4, 1, None, 0, 1)                # empty: nothing to do
+    dist = lambda ws, floats: sg.sgemm_pairwise_sqdist(2, 8, 8, 4, PA, 32, 4, 1, PB, 0, 4, 1,
+                                                       PC, 64, 8, 1, ws, floats)
+    assert status_of(lambda: dist(None, 100)) == -8
+    assert status_of(lambda: dist(PA + (1 << 24), 2 * 8 + 8 - 1)) == -8  # needs batch*m + 1*n
+    assert status_of(lambda: dist(PC + 4, 24)) == -4                      # workspace inside D
+    assert sg.sgemm_status_string(-8).startswith("SGEMM_ERR_WORKSPACE")
+

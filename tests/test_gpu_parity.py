@@ -337,7 +337,7 @@ def _sample_indices(p, rng, count=3000):
     return idx.astype(np.int64)
 
 
-@pytest.mark.parametrize("name", wl.WORKLOADS)
+@pytest.mark.parametrize("name", [w for w in wl.WORKLOADS if wl.kind(w) == "plain"])
 def test_workload_full_size(name):
     """Each workload at its full size, in the launch configuration the
     benchmark times (planner's choice, torch's current stream): sampled
