@@ -93,6 +93,14 @@ def _bind(lib):
                                   _fptr, _i64, _i64, _i64,
                                   _fptr, _i64, _i64, _i64,
                                   _i64, _i64ptr, _fptr]
+    lib.oracle_sgemm_batched2.restype = _int
+    lib.oracle_sgemm_batched2.argtypes = [
+        _i64, _i64, _i64, _i64, _i64, _f32,
+        _fptr, _i64, _i64, _i64, _i64, _i64,
+        _fptr, _i64, _i64, _i64, _i64, _i64,
+        _int,
+        _fptr, _i64, _i64, _i64, _i64,
+    ]
     lib.oracle_num_threads.restype = _int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -314,6 +322,36 @@ def ref_sqdist_entries(batch, m, n, k, X, sX, Y, sY, idx, lib=None):
     if rc != 0:
         raise ValueError("oracle_sqdist: index outside the table")
     return out
+
+
+def ref_sgemm_batched2(nb_outer, nb_inner, m, n, k, alpha,
+                       A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                       B, sB_outer, sB_inner, gB, sB_row, sB_col,
+                       accumulate,
+                       C, sC_outer, sC_inner, sC_row, sC_col, lib=None):
+    """Two batch levels with group divisors on the inner level of A and B:
+    C[o,i] <- alpha * A[o, i/gA] @ B[o, i/gB] (+ C); writes C in place."""
+    lib = lib or _get_lib()
+    A = _as_storage(A, "A")
+    B = _as_storage(B, "B")
+    C = _as_storage(C, "C", writable=True)
+    if min(nb_outer, nb_inner, m, n, k) < 0 or gA < 1 or gB < 1:
+        raise ValueError("negative size or group below 1")
+    inner_a = -(-nb_inner // gA) if nb_inner else 0
+    inner_b = -(-nb_inner // gB) if nb_inner else 0
+    if nb_outer and inner_a and m and k:
+        _check_view(A, "A", (nb_outer, inner_a, m, k), (sA_outer, sA_inner, sA_row, sA_col))
+    if nb_outer and inner_b and n and k:
+        _check_view(B, "B", (nb_outer, inner_b, k, n), (sB_outer, sB_inner, sB_row, sB_col))
+    _check_view(C, "C", (nb_outer, nb_inner, m, n), (sC_outer, sC_inner, sC_row, sC_col))
+    rc = lib.oracle_sgemm_batched2(nb_outer, nb_inner, m, n, k, float(alpha),
+                                   _ptr(A), sA_outer, sA_inner, gA, sA_row, sA_col,
+                                   _ptr(B), sB_outer, sB_inner, gB, sB_row, sB_col,
+                                   int(bool(accumulate)),
+                                   _ptr(C), sC_outer, sC_inner, sC_row, sC_col)
+    if rc != 0:
+        raise RuntimeError(f"oracle_sgemm_batched2 returned {rc}")
+    return C
 
 
 def num_threads(lib=None) -> int:

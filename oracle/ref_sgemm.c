@@ -192,6 +192,43 @@ int oracle_sgemm_entries(int64_t batch, int64_t m, int64_t n, int64_t k, float a
 }
 
 /*
+ * Two batch levels (outer o < nb_outer, inner i < nb_inner) with a group
+ * divisor on the inner level of each input:
+ *
+ *   C[o,i,r,c] <- alpha * sum_p A[o, i/gA, r, p] * B[o, i/gB, p, c]  (+ C_old)
+ *
+ * with X[o, j, r, c] at o*sX_outer + j*sX_inner + r*sX_row + c*sX_col.  This
+ * addresses attention over a [sequence][token][head][dim] buffer directly
+ * (outer = sequence, inner = head) and grouped KV heads (gB = query heads per
+ * KV head): the rvllm post ("Matmuls go to cuBLAS") transposes such buffers
+ * with a copy kernel first and folds the query heads of a group into the
+ * rows.  Each (o, i) is one product of the definition above, formed by the
+ * same element function.  Returns 0, or -1 for a negative size or a group
+ * below 1.
+ */
+int oracle_sgemm_batched2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k,
+                          float alpha,
+                          const float *A, int64_t sA_outer, int64_t sA_inner, int64_t gA,
+                          int64_t sA_row, int64_t sA_col,
+                          const float *B, int64_t sB_outer, int64_t sB_inner, int64_t gB,
+                          int64_t sB_row, int64_t sB_col,
+                          int accumulate,
+                          float *C, int64_t sC_outer, int64_t sC_inner, int64_t sC_row, int64_t sC_col)
+{
+    if (nb_outer < 0 || nb_inner < 0 || m < 0 || n < 0 || k < 0 || gA < 1 || gB < 1)
+        return -1;
+    for (int64_t o = 0; o < nb_outer; ++o)
+        for (int64_t i = 0; i < nb_inner; ++i) {
+            const float *Ab = A + o * sA_outer + (i / gA) * sA_inner;
+            const float *Bb = B + o * sB_outer + (i / gB) * sB_inner;
+            float *Cb = C + o * sC_outer + i * sC_inner;
+            oracle_sgemm_ex(1, m, n, k, alpha, Ab, 0, sA_row, sA_col, Bb, 0, sB_row, sB_col,
+                            accumulate_beta(accumulate), Cb, 0, sC_row, sC_col, NULL, 0, 0, NULL, 0, 0, 0);
+        }
+    return 0;
+}
+
+/*
  * Squared Euclidean norms of a batch of vectors: out[b,i] = sum_p X[b,i,p]^2,
  * with X[b,i,p] at b*sX_batch + i*sX_item + p*sX_elem and out[b,i] at
  * b*sO_batch + i*sO_item.  Returns 0, or -1 for a negative size.

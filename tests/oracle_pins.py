@@ -485,8 +485,59 @@ def pin_sqdist(lib):
         assert np.array_equal(one, D.reshape(batch, m, n)[idx[:, 0], idx[:, 1], idx[:, 2]])
 
 
+def pin_batched2_bthd_gqa(lib):
+    """Both attention products straight on [sequence][token][head][dim]
+    buffers with grouped KV heads (G query heads per KV head): integer data,
+    checked against numpy's int64 einsum of the definition, scores written
+    head-major, outputs written back in [B][T][H][D]."""
+    rng = np.random.default_rng(11)
+    for B_, T, Hq, G, D in ((2, 5, 4, 2, 3), (3, 7, 6, 3, 8), (1, 9, 2, 1, 4), (2, 4, 8, 4, 5)):
+        Hk = Hq // G
+        Q = rng.integers(-3, 4, B_ * T * Hq * D).astype(np.float32)
+        K = rng.integers(-3, 4, B_ * T * Hk * D).astype(np.float32)
+        V = rng.integers(-3, 4, B_ * T * Hk * D).astype(np.float32)
+        Qi, Ki, Vi = (x.reshape(B_, T, h, D).astype(np.int64) for x, h in ((Q, Hq), (K, Hk), (V, Hk)))
+        head_of = np.arange(Hq) // G
+        S_exact = np.einsum("bthd,bshd->bhts", Qi, Ki[:, :, head_of, :])
+        S = np.full(B_ * Hq * T * T, 0.25, np.float32)
+        oracle.ref_sgemm_batched2(B_, Hq, T, T, D, 2.0,
+                                  Q, T * Hq * D, D, 1, Hq * D, 1,
+                                  K, T * Hk * D, D, G, 1, Hk * D,
+                                  True, S, Hq * T * T, T * T, T, 1, lib=lib)
+        assert np.array_equal(S.reshape(B_, Hq, T, T), (2 * S_exact + 0.25).astype(np.float32))
+        P = rng.integers(-2, 3, B_ * Hq * T * T).astype(np.float32)
+        Pi = P.reshape(B_, Hq, T, T).astype(np.int64)
+        O_exact = np.einsum("bhts,bshd->bthd", Pi, Vi[:, :, head_of, :])
+        O = np.zeros(B_ * T * Hq * D, np.float32)
+        oracle.ref_sgemm_batched2(B_, Hq, T, D, T, 1.0,
+                                  P, Hq * T * T, T * T, 1, T, 1,
+                                  V, T * Hk * D, D, G, Hk * D, 1,
+                                  False, O, T * Hq * D, D, Hq * D, 1, lib=lib)
+        assert np.array_equal(O.reshape(B_, T, Hq, D), O_exact.astype(np.float32))
+
+
+def pin_batched2_gqa_row_folding(lib):
+    """With head-major buffers the query heads of one KV head are adjacent,
+    so stacking them as extra rows of one product (the rvllm post's folding,
+    "Matmuls go to cuBLAS") is the same computation as one product per query
+    head with the KV head index divided by the group size: same bits."""
+    rng = np.random.default_rng(12)
+    B_, Hq, G, T, D = 2, 8, 4, 6, 5
+    Hk = Hq // G
+    Q = rng.standard_normal(B_ * Hq * T * D).astype(np.float32)
+    K = rng.standard_normal(B_ * Hk * T * D).astype(np.float32)
+    S1 = np.zeros(B_ * Hq * T * T, np.float32)
+    oracle.ref_sgemm_batched2(B_, Hq, T, T, D, 0.125, Q, Hq * T * D, T * D, 1, D, 1,
+                              K, Hk * T * D, T * D, G, 1, D, False, S1, Hq * T * T, T * T, T, 1, lib=lib)
+    S2 = np.zeros_like(S1)
+    oracle.ref_sgemm(B_ * Hk, G * T, T, D, 0.125, Q, G * T * D, D, 1, K, T * D, 1, D, 0,
+                     S2, G * T * T, T, 1, lib=lib)
+    assert np.array_equal(S1, S2)
+
+
 PINS = [pin_all_ones, pin_identity, pin_k_zero, pin_golden_transpose_trace,
         pin_golden_column_major, pin_blas_linear_mapping, pin_blas_rowmajor_trick,
         pin_exact_bruteforce, pin_numpy_float64, pin_stride_swap, pin_transpose_identity,
         pin_batch_slices, pin_accumulate, pin_order_and_entries, pin_nan_and_canaries,
-        pin_epilogue_bruteforce, pin_epilogue_closed_forms, pin_sqnorms, pin_sqdist]
+        pin_epilogue_bruteforce, pin_epilogue_closed_forms, pin_sqnorms, pin_sqdist,
+        pin_batched2_bthd_gqa, pin_batched2_gqa_row_folding]

@@ -50,6 +50,9 @@ MUTANTS = {
     "distance_Y_transposed": [("(double)Y[bq * sY_batch + jq * sY_row + e * sY_col]",
                                "(double)Y[bq * sY_batch + e * sY_row + jq * sY_col]")],
     "distance_not_squared": [("d += diff * diff;", "d += diff < 0 ? -diff : diff;")],
+    "kv_group_ignored": [("B + o * sB_outer + (i / gB) * sB_inner", "B + o * sB_outer + (i / 1) * sB_inner")],
+    "group_of_the_wrong_operand": [("B + o * sB_outer + (i / gB) * sB_inner", "B + o * sB_outer + (i / gA) * sB_inner")],
+    "batch_levels_swapped_in_C": [("C + o * sC_outer + i * sC_inner", "C + i * sC_outer + o * sC_inner")],
 }
 
 # The brute-force pin at full size is slow; mutants see a smaller sweep.
