@@ -88,6 +88,12 @@ def cpu_baseline(p, seconds: float) -> dict:
             oracle.ref_sqdist(1, rows, p.n, p.k, p.X.storage, (0,) + tuple(p.X.strides[1:]),
                               p.Y.storage, (0,) + tuple(p.Y.strides[1:]), out,
                               (0,) + tuple(p.D.strides[1:]))
+        elif kind == "batched2":
+            # Entry (outer 0, inner 0) starts at each storage's first element.
+            oracle.ref_sgemm(1, rows, p.n, p.k, p.alpha,
+                             p.A.storage, 0, p.A.strides[2], p.A.strides[3],
+                             p.B.storage, 0, p.B.strides[2], p.B.strides[3],
+                             int(p.accumulate), out, 0, p.C.strides[2], p.C.strides[3])
         elif kind == "ex":
             sv = lambda v: (0, v.strides[1]) if v is not None else (0, 0)
             oracle.ref_sgemm_ex(1, rows, p.n, p.k, p.alpha, p.A.storage, (0, p.A.s_row, p.A.s_col),
@@ -136,6 +142,11 @@ def _step_fn(p, dev, stream):
         return (lambda: sg.sgemm_pairwise_sqdist(*args, stream=stream)), info, (dX, dY, dD, ws)
     dA, dB = torch.from_numpy(p.A.storage).to(dev), torch.from_numpy(p.B.storage).to(dev)
     dC = torch.from_numpy(p.C.storage).to(dev)
+    if kind == "batched2":
+        args = p.call_args(dA, dB, dC)
+        info = sg.sgemm_plan_describe2(*p.call_args(dA.data_ptr(), dB.data_ptr(), dC.data_ptr()),
+                                       num_cus=0)
+        return (lambda: sg.sgemm_strided_batched2(*args, stream=stream)), info, (dA, dB, dC)
     info = sg.sgemm_plan_describe(*p.call_args(dA.data_ptr(), dB.data_ptr(), dC.data_ptr()), num_cus=0)
     if kind == "ex":
         dr = torch.from_numpy(p.row.storage).to(dev) if p.row is not None else None
@@ -216,7 +227,11 @@ def _config(p, info) -> dict:
     from strided_fp32_gemm_amd import workloads as wl
 
     c = {"workload": p.name, "batch": p.batch, "m": p.m, "n": p.n, "k": p.k}
-    if wl.kind(p.name) == "dist":
+    if wl.kind(p.name) == "batched2":
+        c.update({"nb_outer": p.nb_outer, "nb_inner": p.nb_inner, "gA": p.A.group, "gB": p.B.group,
+                  "alpha": p.alpha, "accumulate": bool(p.accumulate),
+                  "strides": {"A": list(p.A.strides), "B": list(p.B.strides), "C": list(p.C.strides)}})
+    elif wl.kind(p.name) == "dist":
         c["op"] = "squared distances |x_i - y_j|^2 (sqnorms x2 + product, alpha -2, row/col terms)"
         c["strides"] = {"X": list(p.X.strides), "Y": list(p.Y.strides), "D": list(p.D.strides)}
     else:

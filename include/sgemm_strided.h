@@ -140,6 +140,51 @@ int sgemm_strided_batched_ex_path(int64_t batch, int64_t m, int64_t n, int64_t k
                                   int path, void *stream);
 
 /*
+ * The product over two batch levels, with a group divisor on the inner level
+ * of each input (attention scores for every sequence and every head in one
+ * launch, with several query heads sharing one key/value head: the rvllm
+ * post, section "Matmuls go to cuBLAS"):
+ *
+ *     C[o,i] <- alpha * A[o, i/gA] @ B[o, i/gB]   (+ C[o,i] when accumulate)
+ *
+ * for o < nb_outer, i < nb_inner, where operand X[o,j] is the matrix whose
+ * element (r,c) sits at X + o*sX_outer + j*sX_inner + r*sX_row + c*sX_col
+ * (C's group is 1).  A [sequence][token][head][dim] buffer is addressed as is,
+ * with no transposing copy: outer = sequence, inner = head, row = token.
+ * Grouped key/value heads: gB = query heads per KV head (B's inner index is
+ * i/gB).  A group >= nb_inner maps every inner entry to the first.  With
+ * nb_inner = 1 this is sgemm_strided_batched with batch = nb_outer, and with
+ * nb_outer = 1 it is sgemm_strided_batched over the inner level when both
+ * groups are 1 (same bits in both cases).  nb_outer may be 0 (nothing is
+ * enqueued); nb_inner, gA, gB must be >= 1 (SGEMM_ERR_INVALID_SIZE); strides
+ * are in elements, >= 0 (SGEMM_ERR_INVALID_STRIDE); C must give every
+ * (o, i, r, c) its own element and must not overlap A or B
+ * (SGEMM_ERR_C_ALIAS).  Other arguments, ownership, asynchrony and
+ * determinism as for sgemm_strided_batched.  Returns an sgemm_status.
+ */
+int sgemm_strided_batched2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k,
+                           float alpha,
+                           const float *A, int64_t sA_outer, int64_t sA_inner, int64_t gA,
+                           int64_t sA_row, int64_t sA_col,
+                           const float *B, int64_t sB_outer, int64_t sB_inner, int64_t gB,
+                           int64_t sB_row, int64_t sB_col,
+                           int accumulate,
+                           float *C, int64_t sC_outer, int64_t sC_inner, int64_t sC_row, int64_t sC_col,
+                           void *stream);
+
+/* sgemm_strided_batched2 with the kernel family forced (as for
+ * sgemm_strided_batched_path).  Returns an sgemm_status. */
+int sgemm_strided_batched2_path(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k,
+                                float alpha,
+                                const float *A, int64_t sA_outer, int64_t sA_inner, int64_t gA,
+                                int64_t sA_row, int64_t sA_col,
+                                const float *B, int64_t sB_outer, int64_t sB_inner, int64_t gB,
+                                int64_t sB_row, int64_t sB_col,
+                                int accumulate,
+                                float *C, int64_t sC_outer, int64_t sC_inner, int64_t sC_row,
+                                int64_t sC_col, int path, void *stream);
+
+/*
  * Squared Euclidean norms of a batch of vectors, the terms a distance table
  * adds to its product:
  *
@@ -205,6 +250,18 @@ int sgemm_plan_describe(int64_t batch, int64_t m, int64_t n, int64_t k,
                         int accumulate,
                         float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
                         int path, int num_cus, sgemm_plan_info *info);
+
+/* sgemm_plan_describe for a sgemm_strided_batched2 call (same arguments,
+ * validated the same way).  Returns an sgemm_status. */
+int sgemm_plan_describe2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k,
+                         float alpha,
+                         const float *A, int64_t sA_outer, int64_t sA_inner, int64_t gA,
+                         int64_t sA_row, int64_t sA_col,
+                         const float *B, int64_t sB_outer, int64_t sB_inner, int64_t gB,
+                         int64_t sB_row, int64_t sB_col,
+                         int accumulate,
+                         float *C, int64_t sC_outer, int64_t sC_inner, int64_t sC_row,
+                         int64_t sC_col, int path, int num_cus, sgemm_plan_info *info);
 
 /* Static description of a status code (never NULL). */
 const char *sgemm_status_string(int status);

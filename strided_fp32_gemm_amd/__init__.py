@@ -22,9 +22,12 @@ from ._binding import (  # noqa: F401
     sgemm_last_error,
     sgemm_pairwise_sqdist,
     sgemm_plan_describe,
+    sgemm_plan_describe2,
     sgemm_sqnorms,
     sgemm_status_string,
     sgemm_strided_batched,
+    sgemm_strided_batched2,
+    sgemm_strided_batched2_path,
     sgemm_strided_batched_ex,
     sgemm_strided_batched_ex_path,
     sgemm_strided_batched_path,

@@ -29,8 +29,9 @@ STATUS = {
 
 # Every symbol include/sgemm_strided.h declares.
 EXPORTS = ("sgemm_strided_batched", "sgemm_strided_batched_path", "sgemm_strided_batched_ex",
-           "sgemm_strided_batched_ex_path", "sgemm_sqnorms", "sgemm_pairwise_sqdist",
-           "sgemm_plan_describe", "sgemm_status_string", "sgemm_last_error")
+           "sgemm_strided_batched_ex_path", "sgemm_strided_batched2", "sgemm_strided_batched2_path",
+           "sgemm_sqnorms", "sgemm_pairwise_sqdist",
+           "sgemm_plan_describe", "sgemm_plan_describe2", "sgemm_status_string", "sgemm_last_error")
 
 
 class SgemmError(RuntimeError):
@@ -81,6 +82,12 @@ _EX_ARGS = [_i64, _i64, _i64, _i64, _f32,
             _vp, _i64, _i64,
             _vp, _i64, _i64]
 
+_B2_ARGS = [_i64, _i64, _i64, _i64, _i64, _f32,
+            _vp, _i64, _i64, _i64, _i64, _i64,
+            _vp, _i64, _i64, _i64, _i64, _i64,
+            _int,
+            _vp, _i64, _i64, _i64, _i64]
+
 _lib = None
 
 
@@ -102,6 +109,10 @@ def load(path: str = LIB_PATH):
     lib.sgemm_strided_batched_ex.argtypes = _EX_ARGS + [_vp]
     lib.sgemm_strided_batched_ex_path.restype = _int
     lib.sgemm_strided_batched_ex_path.argtypes = _EX_ARGS + [_int, _vp]
+    lib.sgemm_strided_batched2.restype = _int
+    lib.sgemm_strided_batched2.argtypes = _B2_ARGS + [_vp]
+    lib.sgemm_strided_batched2_path.restype = _int
+    lib.sgemm_strided_batched2_path.argtypes = _B2_ARGS + [_int, _vp]
     lib.sgemm_sqnorms.restype = _int
     lib.sgemm_sqnorms.argtypes = [_i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp]
     lib.sgemm_pairwise_sqdist.restype = _int
@@ -112,6 +123,8 @@ def load(path: str = LIB_PATH):
                                           _vp, _i64, _vp]
     lib.sgemm_plan_describe.restype = _int
     lib.sgemm_plan_describe.argtypes = _GEMM_ARGS + [_int, _int, ctypes.POINTER(PlanInfo)]
+    lib.sgemm_plan_describe2.restype = _int
+    lib.sgemm_plan_describe2.argtypes = _B2_ARGS + [_int, _int, ctypes.POINTER(PlanInfo)]
     lib.sgemm_status_string.restype = ctypes.c_char_p
     lib.sgemm_status_string.argtypes = [_int]
     lib.sgemm_last_error.restype = ctypes.c_char_p
@@ -223,6 +236,43 @@ def sgemm_strided_batched_ex_path(batch, m, n, k, alpha,
     _check(load().sgemm_strided_batched_ex_path(*args, int(path), _stream(stream)))
 
 
+def _b2_list(nb_outer, nb_inner, m, n, k, alpha, A, sA_outer, sA_inner, gA, sA_row, sA_col,
+             B, sB_outer, sB_inner, gB, sB_row, sB_col, accumulate,
+             C, sC_outer, sC_inner, sC_row, sC_col):
+    return [int(nb_outer), int(nb_inner), int(m), int(n), int(k), float(alpha),
+            _ptr(A), int(sA_outer), int(sA_inner), int(gA), int(sA_row), int(sA_col),
+            _ptr(B), int(sB_outer), int(sB_inner), int(gB), int(sB_row), int(sB_col),
+            int(bool(accumulate)),
+            _ptr(C), int(sC_outer), int(sC_inner), int(sC_row), int(sC_col)]
+
+
+def sgemm_strided_batched2(nb_outer, nb_inner, m, n, k, alpha,
+                           A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                           B, sB_outer, sB_inner, gB, sB_row, sB_col,
+                           accumulate,
+                           C, sC_outer, sC_inner, sC_row, sC_col,
+                           stream=None) -> None:
+    """C[o,i] <- alpha*A[o,i//gA]*B[o,i//gB] (+C[o,i]) over two batch levels
+    through the C ABI; strides in elements."""
+    args = _b2_list(nb_outer, nb_inner, m, n, k, alpha, A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                    B, sB_outer, sB_inner, gB, sB_row, sB_col, accumulate,
+                    C, sC_outer, sC_inner, sC_row, sC_col)
+    _check(load().sgemm_strided_batched2(*args, _stream(stream)))
+
+
+def sgemm_strided_batched2_path(nb_outer, nb_inner, m, n, k, alpha,
+                                A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                                B, sB_outer, sB_inner, gB, sB_row, sB_col,
+                                accumulate,
+                                C, sC_outer, sC_inner, sC_row, sC_col,
+                                path=PATH_AUTO, stream=None) -> None:
+    """sgemm_strided_batched2 with the kernel family forced."""
+    args = _b2_list(nb_outer, nb_inner, m, n, k, alpha, A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                    B, sB_outer, sB_inner, gB, sB_row, sB_col, accumulate,
+                    C, sC_outer, sC_inner, sC_row, sC_col)
+    _check(load().sgemm_strided_batched2_path(*args, int(path), _stream(stream)))
+
+
 def sgemm_sqnorms(batch, count, length, X, sX_batch, sX_item, sX_elem, out, sO_batch, sO_item,
                   stream=None) -> None:
     """out[b,i] <- sum_p X[b,i,p]^2 through the C ABI."""
@@ -256,6 +306,22 @@ def sgemm_plan_describe(batch, m, n, k, alpha,
     args = _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
                       sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col)
     _check(load().sgemm_plan_describe(*args, int(path), int(num_cus), ctypes.byref(info)))
+    return info.as_dict()
+
+
+def sgemm_plan_describe2(nb_outer, nb_inner, m, n, k, alpha,
+                         A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                         B, sB_outer, sB_inner, gB, sB_row, sB_col,
+                         accumulate,
+                         C, sC_outer, sC_inner, sC_row, sC_col,
+                         path=PATH_AUTO, num_cus=256) -> dict:
+    """The plan of a sgemm_strided_batched2 call (no device access when
+    num_cus > 0)."""
+    info = PlanInfo()
+    args = _b2_list(nb_outer, nb_inner, m, n, k, alpha, A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                    B, sB_outer, sB_inner, gB, sB_row, sB_col, accumulate,
+                    C, sC_outer, sC_inner, sC_row, sC_col)
+    _check(load().sgemm_plan_describe2(*args, int(path), int(num_cus), ctypes.byref(info)))
     return info.as_dict()
 
 

@@ -118,6 +118,26 @@ int64_t span3(int64_t e0, int64_t s0, int64_t e1, int64_t s1, int64_t e2, int64_
     return r + 1;
 }
 
+// Two batch levels packed into GemmArgs (flat batch = nb_outer * nb_inner).
+int pack2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k, float alpha,
+          const float *A, int64_t sA_outer, int64_t sA_inner, int64_t gA, int64_t sA_row,
+          int64_t sA_col, const float *B, int64_t sB_outer, int64_t sB_inner, int64_t gB,
+          int64_t sB_row, int64_t sB_col, int accumulate, float *C, int64_t sC_outer,
+          int64_t sC_inner, int64_t sC_row, int64_t sC_col, sgemm::GemmArgs &a) {
+    if (nb_outer < 0 || nb_inner < 1 || gA < 1 || gB < 1)
+        return fail(SGEMM_ERR_INVALID_SIZE, "nb_outer must be >= 0; nb_inner, gA and gB >= 1");
+    int64_t batch;
+    if (__builtin_mul_overflow(nb_outer, nb_inner, &batch))
+        return fail(SGEMM_ERR_UNSUPPORTED, "nb_outer*nb_inner overflows int64");
+    a = pack(batch, m, n, k, alpha, A, sA_outer, sA_row, sA_col, B, sB_outer, sB_row, sB_col,
+             accumulate, C, sC_outer, sC_row, sC_col);
+    a.inner = nb_inner;
+    a.sA_inner = sA_inner; a.gA = gA;
+    a.sB_inner = sB_inner; a.gB = gB;
+    a.sC_inner = sC_inner;
+    return SGEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -159,6 +179,34 @@ int sgemm_strided_batched_ex(int64_t batch, int64_t m, int64_t n, int64_t k, flo
                                          sB_batch, sB_row, sB_col, beta, C, sC_batch, sC_row,
                                          sC_col, row_add, sR_batch, sR_row, col_add, sL_batch,
                                          sL_col, SGEMM_PATH_AUTO, stream);
+}
+
+int sgemm_strided_batched2_path(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k,
+                                float alpha, const float *A, int64_t sA_outer, int64_t sA_inner,
+                                int64_t gA, int64_t sA_row, int64_t sA_col, const float *B,
+                                int64_t sB_outer, int64_t sB_inner, int64_t gB, int64_t sB_row,
+                                int64_t sB_col, int accumulate, float *C, int64_t sC_outer,
+                                int64_t sC_inner, int64_t sC_row, int64_t sC_col, int path,
+                                void *stream) {
+    if (!path_ok(path)) return fail(SGEMM_ERR_INVALID_PATH, "unknown path code");
+    sgemm::GemmArgs a;
+    int st = pack2(nb_outer, nb_inner, m, n, k, alpha, A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                   B, sB_outer, sB_inner, gB, sB_row, sB_col, accumulate, C, sC_outer, sC_inner,
+                   sC_row, sC_col, a);
+    if (st != SGEMM_OK) return st;
+    return run_gemm(a, path, stream);
+}
+
+int sgemm_strided_batched2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k,
+                           float alpha, const float *A, int64_t sA_outer, int64_t sA_inner,
+                           int64_t gA, int64_t sA_row, int64_t sA_col, const float *B,
+                           int64_t sB_outer, int64_t sB_inner, int64_t gB, int64_t sB_row,
+                           int64_t sB_col, int accumulate, float *C, int64_t sC_outer,
+                           int64_t sC_inner, int64_t sC_row, int64_t sC_col, void *stream) {
+    return sgemm_strided_batched2_path(nb_outer, nb_inner, m, n, k, alpha, A, sA_outer, sA_inner, gA,
+                                       sA_row, sA_col, B, sB_outer, sB_inner, gB, sB_row, sB_col,
+                                       accumulate, C, sC_outer, sC_inner, sC_row, sC_col,
+                                       SGEMM_PATH_AUTO, stream);
 }
 
 int sgemm_sqnorms(int64_t batch, int64_t count, int64_t len, const float *X, int64_t sX_batch,
@@ -233,15 +281,14 @@ int sgemm_strided_batched(int64_t batch, int64_t m, int64_t n, int64_t k, float 
                                       sC_col, SGEMM_PATH_AUTO, stream);
 }
 
-int sgemm_plan_describe(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
-                        const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
-                        const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
-                        int accumulate, float *C, int64_t sC_batch, int64_t sC_row,
-                        int64_t sC_col, int path, int num_cus, sgemm_plan_info *info) {
+}  // extern "C"
+
+namespace {
+
+// Validate and plan `a` without touching the device; fill *info.
+int describe(const sgemm::GemmArgs &a, int path, int num_cus, sgemm_plan_info *info) {
     if (!path_ok(path)) return fail(SGEMM_ERR_INVALID_PATH, "unknown path code");
     if (!info) return fail(SGEMM_ERR_NULL_POINTER, "info is NULL");
-    sgemm::GemmArgs a = pack(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
-                             sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col);
     std::string why;
     int st = sgemm::validate(a, why);
     if (st != sgemm::kOk) return fail(st, why);
@@ -278,6 +325,34 @@ int sgemm_plan_describe(int64_t batch, int64_t m, int64_t n, int64_t k, float al
     info->workgroups = plan.empty ? 0 : plan.workgroups;
     std::strncpy(info->kernel, plan.kernel_name.c_str(), sizeof info->kernel - 1);
     return SGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm_plan_describe(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                        const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                        const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                        int accumulate, float *C, int64_t sC_batch, int64_t sC_row,
+                        int64_t sC_col, int path, int num_cus, sgemm_plan_info *info) {
+    return describe(pack(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch, sB_row,
+                         sB_col, accumulate, C, sC_batch, sC_row, sC_col),
+                    path, num_cus, info);
+}
+
+int sgemm_plan_describe2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k,
+                         float alpha, const float *A, int64_t sA_outer, int64_t sA_inner,
+                         int64_t gA, int64_t sA_row, int64_t sA_col, const float *B,
+                         int64_t sB_outer, int64_t sB_inner, int64_t gB, int64_t sB_row,
+                         int64_t sB_col, int accumulate, float *C, int64_t sC_outer,
+                         int64_t sC_inner, int64_t sC_row, int64_t sC_col, int path, int num_cus,
+                         sgemm_plan_info *info) {
+    sgemm::GemmArgs a;
+    int st = pack2(nb_outer, nb_inner, m, n, k, alpha, A, sA_outer, sA_inner, gA, sA_row, sA_col,
+                   B, sB_outer, sB_inner, gB, sB_row, sB_col, accumulate, C, sC_outer, sC_inner,
+                   sC_row, sC_col, a);
+    return st != SGEMM_OK ? st : describe(a, path, num_cus, info);
 }
 
 const char *sgemm_status_string(int status) {

@@ -32,8 +32,9 @@ __global__ __launch_bounds__(256) void sgemm_generic(GenericArgs p) {
     for (long long tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const long long b = tile / per_batch, t = tile - b * per_batch;
         const long long i0 = (t / p.tiles_n) * 64, j0 = (t % p.tiles_n) * 64;
-        const float *A = p.A + b * p.sA_b;
-        const float *B = p.B + b * p.sB_b;
+        const long long bo = b / p.inner, bi = b - bo * p.inner;
+        const float *A = p.A + bo * p.sA_b + (bi / p.gA) * p.sA_i;
+        const float *B = p.B + bo * p.sB_b + (bi / p.gB) * p.sB_i;
         float acc[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void sgemm_generic(GenericArgs p) {
             }
             __syncthreads();
         }
-        float *C = p.C + b * p.sC_b;
+        float *C = p.C + bo * p.sC_b + bi * p.sC_i;
         const Epilogue &e = p.epi;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -231,6 +232,8 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n;
         g.alpha = p.alpha; g.accumulate = p.accumulate;
         g.epi = make_epilogue(p);
+        g.inner = p.inner; g.gA = p.gA; g.gB = p.gB;
+        g.sA_i = p.sA_i; g.sB_i = p.sB_i; g.sC_i = p.sC_i;
         hipLaunchKernelGGL(sgemm_generic, dim3(unsigned(p.workgroups)), dim3(256), 0, stream, g);
     } else {
         MfmaArgs a;
@@ -244,6 +247,8 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         a.tiles_m = int(p.tiles_m); a.tiles_n = int(p.tiles_n);
         a.total_tiles = int(p.batch * p.tiles_m * p.tiles_n);
         a.map = make_tile_map(p.batch, p.tiles_m, p.tiles_n);
+        a.split = make_batch_split(p.inner, p.gA, p.gB);
+        a.sA_i = p.sA_i; a.sB_i = p.sB_i; a.sC_i = p.sC_i;
         a.accumulate = p.accumulate;
         a.c_vec4 = p.c_vec4 ? 1 : 0;
         a.alpha = p.alpha;

@@ -34,6 +34,8 @@ struct MfmaArgs {
     int tiles_m, tiles_n;
     int total_tiles;   // batch * tiles_m * tiles_n (the persistent kernel's loop bound)
     TileMap map;       // tile id -> (batch, tile row, tile column)
+    BatchSplit split;  // flat batch index -> (outer, inner) entries of A, B, C
+    long long sA_i, sB_i, sC_i;   // inner-level batch strides
     int accumulate;   // beta != 0: C is read
     int c_vec4;   // C rows take 16-byte stores (n-contiguous, aligned, n % 4 == 0)
     float alpha;
@@ -53,6 +55,7 @@ struct GenericArgs {
     float alpha;
     int accumulate;
     Epilogue epi;
+    long long inner, gA, gB, sA_i, sB_i, sC_i;   // two batch levels (see BatchSplit)
 };
 
 // Launchers indexed [tile][A k-fast][B k-fast][A 16-byte loads]

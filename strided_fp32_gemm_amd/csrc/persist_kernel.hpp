@@ -78,9 +78,12 @@ __global__ __launch_bounds__(kPersistTiles[P].wgm * kPersistTiles[P].wgn * 64) v
         int b, tm, tn;
         tile_coords(p.map, ok ? v : 0, b, tm, tn);
         const int i0 = tm * BM, j0 = tn * BN;
-        t.rA = make_rsrc(p.A + (long long)b * p.sA_b + (long long)i0 * p.sA_m);
-        t.rB = make_rsrc(p.B + (long long)b * p.sB_b + (long long)j0 * p.sB_n);
-        t.rC = make_rsrc(p.C + (long long)b * p.sC_b + (long long)i0 * p.sC_m + (long long)j0 * p.sC_n);
+        uint32_t bo, ba, bb, bc;
+        batch_entry(p.split, uint32_t(b), bo, ba, bb, bc);
+        t.rA = make_rsrc(p.A + (long long)bo * p.sA_b + (long long)ba * p.sA_i + (long long)i0 * p.sA_m);
+        t.rB = make_rsrc(p.B + (long long)bo * p.sB_b + (long long)bb * p.sB_i + (long long)j0 * p.sB_n);
+        t.rC = make_rsrc(p.C + (long long)bo * p.sC_b + (long long)bc * p.sC_i + (long long)i0 * p.sC_m +
+                         (long long)j0 * p.sC_n);
         t.m_left = ok ? unsigned(p.m - i0) : 0u;
         t.n_left = ok ? unsigned(p.n - j0) : 0u;
         return t;

@@ -30,6 +30,14 @@ int64_t last_offset(int64_t e0, int64_t s0, int64_t e1, int64_t s1, int64_t e2, 
     return r;
 }
 
+// Same for a [e0, e1, e2, e3] view.
+int64_t last_offset4(int64_t e0, int64_t s0, int64_t e1, int64_t s1, int64_t e2, int64_t s2, int64_t e3,
+                     int64_t s3) {
+    int64_t head = last_offset(e0, s0, e1, s1, e2, s2), tail, r;
+    if (head < 0 || !mul64(e3 - 1, s3, tail) || !add64(head, tail, r)) return -1;
+    return r;
+}
+
 bool ranges_overlap(uintptr_t p, int64_t last_p, uintptr_t q, int64_t last_q) {
     uintptr_t p_end = p + 4u * (uintptr_t)(last_p + 1);
     uintptr_t q_end = q + 4u * (uintptr_t)(last_q + 1);
@@ -82,11 +90,15 @@ int validate(const GemmArgs &a, std::string &why) {
         why = "negative size (batch, m, n, k must be >= 0)";
         return kErrSize;
     }
-    const int64_t strides[9] = {a.sA_batch, a.sA_row, a.sA_col, a.sB_batch, a.sB_row,
-                                a.sB_col, a.sC_batch, a.sC_row, a.sC_col};
-    static const char *names[9] = {"sA_batch", "sA_row", "sA_col", "sB_batch", "sB_row",
-                                   "sB_col", "sC_batch", "sC_row", "sC_col"};
-    for (int i = 0; i < 9; ++i)
+    if (a.inner < 1 || a.gA < 1 || a.gB < 1 || (a.batch > 0 && a.batch % a.inner != 0)) {
+        why = "inner batch count and groups must be >= 1, and the inner count must divide the batch";
+        return kErrSize;
+    }
+    const int64_t strides[12] = {a.sA_batch, a.sA_row, a.sA_col, a.sB_batch, a.sB_row, a.sB_col,
+                                 a.sC_batch, a.sC_row, a.sC_col, a.sA_inner, a.sB_inner, a.sC_inner};
+    static const char *names[12] = {"sA_batch", "sA_row", "sA_col", "sB_batch", "sB_row", "sB_col",
+                                    "sC_batch", "sC_row", "sC_col", "sA_inner", "sB_inner", "sC_inner"};
+    for (int i = 0; i < 12; ++i)
         if (strides[i] < 0) {
             why = std::string("negative stride ") + names[i];
             return kErrStride;
@@ -109,11 +121,14 @@ int validate(const GemmArgs &a, std::string &why) {
         why = a.A ? "B is NULL" : "A is NULL";
         return kErrNull;
     }
-    int64_t lastC = last_offset(a.batch, a.sC_batch, a.m, a.sC_row, a.n, a.sC_col);
+    const int64_t outer = a.batch / a.inner;
+    int64_t lastC = last_offset4(outer, a.sC_batch, a.inner, a.sC_inner, a.m, a.sC_row, a.n, a.sC_col);
     int64_t lastA = 0, lastB = 0;
     if (a.k > 0) {
-        lastA = last_offset(a.batch, a.sA_batch, a.m, a.sA_row, a.k, a.sA_col);
-        lastB = last_offset(a.batch, a.sB_batch, a.k, a.sB_row, a.n, a.sB_col);
+        lastA = last_offset4(outer, a.sA_batch, (a.inner + a.gA - 1) / a.gA, a.sA_inner, a.m, a.sA_row,
+                             a.k, a.sA_col);
+        lastB = last_offset4(outer, a.sB_batch, (a.inner + a.gB - 1) / a.gB, a.sB_inner, a.k, a.sB_row,
+                             a.n, a.sB_col);
     }
     int64_t lastR = a.row_add ? last_offset(a.batch, a.sR_batch, a.m, a.sR_row, 1, 0) : 0;
     int64_t lastL = a.col_add ? last_offset(a.batch, a.sL_batch, a.n, a.sL_col, 1, 0) : 0;
@@ -125,9 +140,9 @@ int validate(const GemmArgs &a, std::string &why) {
     }
     // C must address every output at its own element: sorted by stride, each
     // axis of extent > 1 has to step past everything the smaller axes reach.
-    struct Axis { int64_t extent, stride; } ax[3] = {
-        {a.batch, a.sC_batch}, {a.m, a.sC_row}, {a.n, a.sC_col}};
-    std::sort(ax, ax + 3, [](const Axis &x, const Axis &y) { return x.stride < y.stride; });
+    struct Axis { int64_t extent, stride; } ax[4] = {
+        {outer, a.sC_batch}, {a.inner, a.sC_inner}, {a.m, a.sC_row}, {a.n, a.sC_col}};
+    std::sort(ax, ax + 4, [](const Axis &x, const Axis &y) { return x.stride < y.stride; });
     int64_t reach = 0;
     for (const Axis &x : ax) {
         if (x.extent <= 1) continue;
@@ -265,6 +280,12 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
     p.A = a.A; p.sA_b = a.sA_batch; p.sA_m = a.sA_row; p.sA_k = a.sA_col;
     p.B = a.B; p.sB_b = a.sB_batch; p.sB_k = a.sB_row; p.sB_n = a.sB_col;
     p.C = a.C; p.sC_b = a.sC_batch; p.sC_m = a.sC_row; p.sC_n = a.sC_col;
+    p.inner = a.inner;
+    // A group at least as large as the inner count maps every inner entry to
+    // the first, as a group of exactly that size does; this keeps it in 32 bits.
+    p.sA_i = a.sA_inner; p.gA = std::min(a.gA, a.inner);
+    p.sB_i = a.sB_inner; p.gB = std::min(a.gB, a.inner);
+    p.sC_i = a.sC_inner;
     // Outputs are written row segments at a time; a column-major C is served
     // as C^T = B^T A^T (kael book ch. 09, section "cuBLAS": the same bytes
     // read in the other order are the transpose), which only exchanges roles
@@ -279,6 +300,8 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         p.A = p.B; p.sA_b = p.sB_b; p.sA_m = p.sB_n; p.sA_k = p.sB_k;
         p.B = A0; p.sB_b = a_b; p.sB_k = a_k; p.sB_n = a_m;
         std::swap(p.sC_m, p.sC_n);
+        std::swap(p.sA_i, p.sB_i);
+        std::swap(p.gA, p.gB);
         // Rows of C^T are the columns of C: the two vector terms trade places.
         std::swap(p.row_add, p.col_add);
         std::swap(p.sR_b, p.sL_b);
@@ -287,6 +310,8 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
     // Broadcast strides of extent-1 axes never matter; zero them so that
     // alignment checks see only strides that are used.
     if (p.batch == 1) { p.sA_b = 0; p.sB_b = 0; p.sC_b = 0; p.sR_b = 0; p.sL_b = 0; }
+    if (p.inner == 1) { p.sA_i = 0; p.sB_i = 0; p.sC_i = 0; p.gA = 1; p.gB = 1; }
+    if (p.batch == p.inner) { p.sA_b = 0; p.sB_b = 0; p.sC_b = 0; }  // one outer entry
 
     p.a_kfast = cols_fast(p.m, p.sA_m, p.k, p.sA_k);
     p.b_kfast = !cols_fast(p.k, p.sB_k, p.n, p.sB_n);
@@ -294,9 +319,12 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
                         : vector_width(p.A, p.sA_m, p.m, p.sA_k, p.sA_b, p.batch);
     p.vec_b = p.b_kfast ? vector_width(p.B, p.sB_k, p.k, p.sB_n, p.sB_b, p.batch)
                         : vector_width(p.B, p.sB_n, p.n, p.sB_k, p.sB_b, p.batch);
+    // The inner batch stride moves every tile base as well.
+    if (p.sA_i % 4) p.vec_a = 1;
+    if (p.sB_i % 4) p.vec_b = 1;
 
     p.c_vec4 = p.sC_n == 1 && p.n % 4 == 0 && p.C % 16 == 0 && p.sC_m % 4 == 0 &&
-               (p.batch == 1 || p.sC_b % 4 == 0);
+               (p.batch == 1 || p.sC_b % 4 == 0) && p.sC_i % 4 == 0;
     p.col_vec4 = p.c_vec4 && p.col_add && p.sL_n == 1 && p.col_add % 16 == 0 &&
                  (p.batch == 1 || p.sL_b % 4 == 0);
 

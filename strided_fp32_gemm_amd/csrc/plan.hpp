@@ -22,6 +22,13 @@ struct GemmArgs {
     float beta = 0.0f;
     uintptr_t row_add = 0; int64_t sR_batch = 0, sR_row = 0;
     uintptr_t col_add = 0; int64_t sL_batch = 0, sL_col = 0;
+    // Two batch levels: batch = outer * inner, flat index b = o*inner + i.
+    // Operand X of batch entry (o, i) starts at X + o*sX_batch + (i/gX)*sX_inner
+    // (gC = 1).  inner = 1 is the single-level product.
+    int64_t inner = 1;
+    int64_t sA_inner = 0, gA = 1;
+    int64_t sB_inner = 0, gB = 1;
+    int64_t sC_inner = 0;
 };
 
 enum class Family : int { Auto = 0, Mfma = 1, Wave = 2, Generic = 3 };
@@ -182,6 +189,25 @@ constexpr void tile_coords(const TileMap &map, int w, int &b, int &tm, int &tn) 
     tn = int(col);
 }
 
+// Two batch levels: flat batch index b = o*inner + i; operand X of entry b
+// starts at o*sX_outer + (i / gX)*sX_inner (gC = 1).  ia / ib are the inner
+// indices of A's and B's entries, ic = i that of C's.
+struct BatchSplit {
+    Divisor inner, gA, gB;
+};
+
+constexpr BatchSplit make_batch_split(int64_t inner, int64_t gA, int64_t gB) {
+    return BatchSplit{make_divisor(uint32_t(inner)), make_divisor(uint32_t(gA)), make_divisor(uint32_t(gB))};
+}
+
+constexpr void batch_entry(const BatchSplit &s, uint32_t b, uint32_t &o, uint32_t &ia, uint32_t &ib,
+                           uint32_t &ic) {
+    o = divide(b, s.inner);
+    ic = b - o * s.inner.d;
+    ia = divide(ic, s.gA);
+    ib = divide(ic, s.gB);
+}
+
 // Everything a launch needs, in kernel terms: A is m x k, B is k x n, C is
 // m x n, each with a batch stride, and "fast" names the contiguous axis.
 struct Plan {
@@ -200,6 +226,8 @@ struct Plan {
     uintptr_t row_add = 0, col_add = 0;   // per-row / per-column terms (kernel terms, after any rewrite)
     int64_t sR_b = 0, sR_m = 0, sL_b = 0, sL_n = 0;
     bool col_vec4 = false;     // column term read 4 at a time (with c_vec4)
+    int64_t inner = 1;         // second batch level (kernel terms, after any rewrite)
+    int64_t sA_i = 0, gA = 1, sB_i = 0, gB = 1, sC_i = 0;
     uintptr_t A = 0, B = 0, C = 0;
     int64_t sA_b = 0, sA_m = 0, sA_k = 0;
     int64_t sB_b = 0, sB_k = 0, sB_n = 0;

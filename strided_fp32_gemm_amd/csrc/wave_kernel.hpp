@@ -45,10 +45,12 @@ __global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
     tile_coords(p.map, blockIdx.x, b, tm, tn);
     const int i0 = tm * WM, j0 = tn * WN;
 
+    uint32_t bo, ba, bb, bc;
+    batch_entry(p.split, uint32_t(b), bo, ba, bb, bc);
     const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc(p.A + (long long)b * p.sA_b + (long long)i0 * p.sA_m);
+        make_rsrc(p.A + (long long)bo * p.sA_b + (long long)ba * p.sA_i + (long long)i0 * p.sA_m);
     const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc(p.B + (long long)b * p.sB_b + (long long)j0 * p.sB_n);
+        make_rsrc(p.B + (long long)bo * p.sB_b + (long long)bb * p.sB_i + (long long)j0 * p.sB_n);
     const unsigned m_left = unsigned(p.m - i0), n_left = unsigned(p.n - j0);
     const unsigned K = unsigned(p.k);
     const unsigned sAm = unsigned(p.sA_m), sAk = unsigned(p.sA_k);
@@ -136,8 +138,8 @@ __global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
     // Epilogue: lane (lr, lh) of block (a, c) holds C[a*16 + lr][c*16 + 4*lh + r]
     // (epilogue_value; the general epilogue's vector terms come through
     // their own buffer resources, out-of-range convention as for C).
-    const __amdgpu_buffer_rsrc_t rC =
-        make_rsrc(p.C + (long long)b * p.sC_b + (long long)i0 * p.sC_m + (long long)j0 * p.sC_n);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(p.C + (long long)bo * p.sC_b + (long long)bc * p.sC_i +
+                                                 (long long)i0 * p.sC_m + (long long)j0 * p.sC_n);
     const unsigned sCm = unsigned(p.sC_m), sCn = unsigned(p.sC_n);
     const float alpha = p.alpha;
     const bool accumulate = p.accumulate != 0;

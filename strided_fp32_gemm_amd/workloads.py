@@ -34,10 +34,13 @@ ROOT_SEED = 2024
 
 # Benchmark workloads.
 WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
-             "linear_bwd_dx", "linear_bwd_dw", "linear_xT", "linear_bias", "sqdist")
+             "linear_bwd_dx", "linear_bwd_dw", "linear_xT", "linear_bias", "sqdist",
+             "attn_qk_gqa", "attn_pv_gqa")
 # Entry point each workload goes through: "plain" (sgemm_strided_batched),
-# "ex" (sgemm_strided_batched_ex) or "dist" (sgemm_pairwise_sqdist).
-KINDS = {"linear_bias": "ex", "sqdist": "dist"}
+# "ex" (sgemm_strided_batched_ex), "dist" (sgemm_pairwise_sqdist) or
+# "batched2" (sgemm_strided_batched2).
+KINDS = {"linear_bias": "ex", "sqdist": "dist", "attn_qk_gqa": "batched2",
+         "attn_pv_gqa": "batched2"}
 
 
 def kind(name: str) -> str:
@@ -47,7 +50,7 @@ def kind(name: str) -> str:
 # Children of the root seed, in spawn order (the two halves of the linear
 # layer's backward pass share one draw of dy, W and x).
 SEED_NAMES = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
-              "linear_bwd", "linear_xT", "linear_bias", "sqdist")
+              "linear_bwd", "linear_xT", "linear_bias", "sqdist", "attn_qk_gqa", "attn_pv_gqa")
 
 
 @dataclasses.dataclass
@@ -333,6 +336,110 @@ def sqdist() -> DistProblem:
                        Operand(Y, (0, 512, 1)), Operand(D, (4096 * 1024, 1024, 1)))
 
 
+@dataclasses.dataclass
+class Operand2:
+    """A flat float32 host storage plus the (outer, inner, row, col) strides
+    of a two-level batch of matrices over it, and the group divisor of the
+    inner level (entry i of the inner level reads matrix i // group)."""
+    storage: np.ndarray
+    strides: tuple
+    group: int = 1
+
+
+@dataclasses.dataclass
+class Problem2:
+    """One sgemm_strided_batched2 call: C[o,i] <- alpha * A[o, i//gA] @
+    B[o, i//gB] (+C[o,i]) for o < nb_outer, i < nb_inner."""
+    name: str
+    nb_outer: int
+    nb_inner: int
+    m: int
+    n: int
+    k: int
+    alpha: float
+    accumulate: bool
+    A: Operand2
+    B: Operand2
+    C: Operand2
+    notes: str = ""
+
+    @property
+    def batch(self) -> int:
+        return self.nb_outer * self.nb_inner
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.m * self.n * self.k
+
+    def call_args(self, a, b, c):
+        """Positional arguments of sgemm_strided_batched2 (and of the
+        oracle's two-level product) with the storages replaced by a, b, c."""
+        (ao, ai, ar, ac), (bo, bi, br, bc) = self.A.strides, self.B.strides
+        return [self.nb_outer, self.nb_inner, self.m, self.n, self.k, self.alpha,
+                a, ao, ai, self.A.group, ar, ac, b, bo, bi, self.B.group, br, bc,
+                int(self.accumulate), c, *self.C.strides]
+
+
+def layout2(nb_outer: int, count: int, rows: int, cols: int, order: str, transposed: bool = False):
+    """Storage size and (outer, inner, row, col) strides of nb_outer x count
+    matrices of rows x cols.  order "heads" stores [outer][count][r][c]
+    (head-major); "tokens" stores [outer][r][count][c] (a [sequence][token]
+    [head][dim] buffer, rows = tokens).  `transposed` reads the stored
+    matrices transposed: the stored matrix is cols x rows and the row and
+    column strides are exchanged."""
+    sr, sc = (cols, rows) if transposed else (rows, cols)
+    per = sr * count * sc
+    if order == "heads":
+        st = (per, sr * sc, sc, 1)
+    elif order == "tokens":
+        st = (per, sc, count * sc, 1)
+    else:
+        raise ValueError(order)
+    if transposed:
+        st = (st[0], st[1], st[3], st[2])
+    return per * nb_outer, st
+
+
+# SmolLM2-360M, the model the rvllm post runs: 15 query heads share 5
+# key/value heads (3 per group), head_dim 64.
+GQA_Q_HEADS, GQA_KV_HEADS, GQA_HEAD_DIM = 15, 5, 64
+GQA_SEQS, GQA_TOKENS = 8, 512
+
+
+def attn_qk_gqa() -> Problem2:
+    """S = (1/8) Q K^T straight from the token-major projections: Q
+    [8][512][15][64] and K [8][512][5][64] N(0,1), three query heads per KV
+    head (gB = 3), S written head-major [8][15][512][512].  The same work as
+    attn_qk, without the transposing copies and with 5 K heads instead of 15."""
+    gq, gk = _gens("attn_qk_gqa", 2)
+    no, h, hk, t, d = GQA_SEQS, GQA_Q_HEADS, GQA_KV_HEADS, GQA_TOKENS, GQA_HEAD_DIM
+    nq, sq = layout2(no, h, t, d, "tokens")
+    nk, sk = layout2(no, hk, d, t, "tokens", transposed=True)
+    ns, ss = layout2(no, h, t, t, "heads")
+    Q = _f32(gq.normal(0.0, 1.0, nq))
+    K = _f32(gk.normal(0.0, 1.0, nk))
+    S = np.zeros(ns, np.float32)
+    return Problem2("attn_qk_gqa", no, h, t, t, d, 1.0 / math.sqrt(d), False,
+                    Operand2(Q, sq), Operand2(K, sk, h // hk), Operand2(S, ss))
+
+
+def attn_pv_gqa() -> Problem2:
+    """O = P V written token-major: P [8][15][512][512] i.i.d. U[0, 1/512]
+    (as attn_pv), V [8][512][5][64] N(0,1) shared by 3 query heads each
+    (gB = 3), O [8][512][15][64] -- the layout the output projection reads,
+    with no transposing copy."""
+    gp, gv = _gens("attn_pv_gqa", 2)
+    no, h, hk, t, d = GQA_SEQS, GQA_Q_HEADS, GQA_KV_HEADS, GQA_TOKENS, GQA_HEAD_DIM
+    n_p, sp = layout2(no, h, t, t, "heads")
+    nv, sv = layout2(no, hk, t, d, "tokens")
+    n_o, so = layout2(no, h, t, d, "tokens")
+    P = _f32(gp.uniform(0.0, 1.0 / t, n_p))
+    V = _f32(gv.normal(0.0, 1.0, nv))
+    O = np.zeros(n_o, np.float32)
+    return Problem2("attn_pv_gqa", no, h, t, d, t, 1.0, False,
+                    Operand2(P, sp), Operand2(V, sv, h // hk), Operand2(O, so))
+
+
 BUILDERS = {
     "square64": square64,
     "linear_xWt": linear_xWt,
@@ -345,6 +452,8 @@ BUILDERS = {
     "linear_xT": linear_xT,
     "linear_bias": linear_bias,
     "sqdist": sqdist,
+    "attn_qk_gqa": attn_qk_gqa,
+    "attn_pv_gqa": attn_pv_gqa,
 }
 
 
@@ -412,3 +521,33 @@ def random_problem(seed: int, batch: int, m: int, n: int, k: int, *,
         C = _f32(gc.uniform(-1.0, 1.0, max(per_c * batch, 1)))
     return Problem(name, batch, m, n, k, alpha, accumulate,
                    Operand(A, sa), Operand(B, sb), Operand(C, sc))
+
+
+def random_problem2(seed: int, nb_outer: int, nb_inner: int, m: int, n: int, k: int, *,
+                    gA: int = 1, gB: int = 1, a_order: str = "tokens", a_trans: bool = False,
+                    b_order: str = "tokens", b_trans: bool = False, c_order: str = "heads",
+                    c_trans: bool = False, alpha: float = 1.0, accumulate: bool = False, dist: str = "normal",
+                    name: str = "random2") -> Problem2:
+    """Random two-level problem: A holds ceil(nb_inner/gA) matrices per outer
+    entry, B ceil(nb_inner/gB), C nb_inner, each laid out by layout2 with the
+    given order and transposition.  dist as for random_problem."""
+    ss = np.random.SeedSequence([ROOT_SEED, 2, seed])
+    ga, gb, gc = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3)]
+
+    def draw(g, count):
+        count = max(count, 1)
+        if dist == "uniform":
+            return _f32(g.uniform(-1.0, 1.0, count))
+        if dist == "normal":
+            return _f32(g.normal(0.0, 1.0, count))
+        if dist == "int":
+            return _f32(g.integers(-3, 4, count))
+        raise ValueError(dist)
+
+    na, sa = layout2(nb_outer, -(-nb_inner // gA), m, k, a_order, a_trans)
+    nb, sb = layout2(nb_outer, -(-nb_inner // gB), k, n, b_order, b_trans)
+    nc, sc = layout2(nb_outer, nb_inner, m, n, c_order, c_trans)
+    A, B = draw(ga, na), draw(gb, nb)
+    C = _f32(gc.integers(-3, 4, max(nc, 1))) if dist == "int" else _f32(gc.uniform(-1.0, 1.0, max(nc, 1)))
+    return Problem2(name, nb_outer, nb_inner, m, n, k, alpha, accumulate,
+                    Operand2(A, sa, gA), Operand2(B, sb, gB), Operand2(C, sc))

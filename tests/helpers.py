@@ -41,3 +41,10 @@ def column_major_strides(ld: int):
     """(row, col) element strides of a column-major matrix with leading
     dimension `ld`: element (r, c) sits at r + c*ld."""
     return (1, ld)
+
+
+def view4(storage: np.ndarray, shape, strides) -> np.ndarray:
+    """Read-only 4-D numpy view of a flat float32 storage under element
+    strides (two batch levels, then row and column)."""
+    return as_strided(storage, tuple(int(s) for s in shape), tuple(4 * int(s) for s in strides),
+                      writeable=False)

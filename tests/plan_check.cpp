@@ -1,4 +1,4 @@
-// Host check of the tile-order arithmetic in plan.hpp (built with g++ by
+// Host check of the tile-order and batch-split arithmetic in plan.hpp (built with g++ by
 // test_plan_host.py; no GPU).  Exits 0 and prints "ok" when every case holds.
 #include <cstdint>
 #include <cstdio>
@@ -55,6 +55,20 @@ static void check_map(int batch, int tiles_m, int tiles_n) {
     }
 }
 
+// Two batch levels: the flat index b splits into (outer, inner) entries, the
+// inner entry of A and B divided by their groups, as plain division does.
+static void check_split(int64_t inner, int64_t gA, int64_t gB, uint32_t b) {
+    const BatchSplit s = make_batch_split(inner, gA, gB);
+    uint32_t o, ia, ib, ic;
+    batch_entry(s, b, o, ia, ib, ic);
+    const int64_t wo = b / inner, wc = b % inner;
+    if (o != wo || ic != wc || ia != wc / gA || ib != wc / gB) {
+        if (fails++ < 10)
+            std::printf("split b %u inner %lld groups %lld,%lld -> (%u,%u,%u,%u)\n", b, (long long)inner,
+                        (long long)gA, (long long)gB, o, ia, ib, ic);
+    }
+}
+
 int main() {
     std::mt19937_64 rng(12345);
     const uint32_t top = 0x7fffffffu;
@@ -79,6 +93,17 @@ int main() {
     for (auto &s : shapes) check_map(s[0], s[1], s[2]);
     for (int i = 0; i < 200; ++i)
         check_map(int(rng() % 9) + 1, int(rng() % 40) + 1, int(rng() % 40) + 1);
+    const int64_t splits[][3] = {{1, 1, 1}, {16, 1, 4}, {16, 4, 1}, {32, 8, 8}, {12, 5, 7},
+                                 {7, 7, 3}, {64, 64, 1}, {3, 2, 2}, {40, 40, 40}, {1000, 1, 999}};
+    for (auto &t : splits) {
+        for (uint32_t b = 0; b < 4096; ++b) check_split(t[0], t[1], t[2], b);
+        for (int i = 0; i < 256; ++i) check_split(t[0], t[1], t[2], uint32_t(rng() % (uint64_t(top) + 1)));
+    }
+    for (int i = 0; i < 2000; ++i) {
+        const int64_t inner = int64_t(rng() % 100000) + 1;
+        check_split(inner, int64_t(rng() % inner) + 1, int64_t(rng() % inner) + 1,
+                    uint32_t(rng() % (uint64_t(top) + 1)));
+    }
     if (fails) {
         std::printf("%d failures\n", fails);
         return 1;

@@ -219,3 +219,26 @@ def test_extended_entry_points_validate_before_the_device():
     assert status_of(lambda: dist(PC + 4, 24)) == -4                      # workspace inside D
     assert sg.sgemm_status_string(-8).startswith("SGEMM_ERR_WORKSPACE")
 
+
+
+def test_two_level_batch_validates_before_the_device():
+    """Two batch levels with groups: sizes, groups, strides, C's distinctness
+    across both levels and overlap with the inputs are checked before any
+    device call (no GPU here)."""
+    def b2(no=2, ni=4, gA=1, gB=2, sA=(256, 64, 8, 1), sB=(128, 64, 1, 8), sC=(512, 128, 16, 1),
+           A=PA, B=PB, C=PC):
+        return sg.sgemm_strided_batched2(no, ni, 8, 16, 8, 1.0, A, sA[0], sA[1], gA, sA[2], sA[3],
+                                         B, sB[0], sB[1], gB, sB[2], sB[3], 0,
+                                         C, sC[0], sC[1], sC[2], sC[3])
+    assert status_of(lambda: b2(ni=0)) == -1
+    assert status_of(lambda: b2(gA=0)) == -1
+    assert status_of(lambda: b2(no=-1)) == -1
+    assert status_of(lambda: b2(sB=(128, -64, 1, 8))) == -2
+    assert status_of(lambda: b2(sC=(512, 0, 16, 1))) == -4          # every head writes one block
+    assert status_of(lambda: b2(sC=(256, 128, 16, 1))) == -4        # sequences overlap heads
+    assert status_of(lambda: b2(C=PA + 4 * 100)) == -4              # C inside A
+    assert status_of(lambda: b2(no=1 << 40, ni=1 << 30)) == -5      # batch overflows int64
+    assert status_of(lambda: b2(sA=(1 << 61, 64, 8, 1), no=8)) == -5
+    b2(no=0)                                                        # empty: nothing to do
+    # Groups larger than the inner count are accepted (every entry maps to the first).
+    b2(no=0, gB=1 << 40)
