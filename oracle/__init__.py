@@ -21,7 +21,9 @@ elements.  Sums are formed in fp64 in ascending p and rounded to fp32 once.
 The general epilogue (``ref_sgemm_ex``) adds beta * C_old (not read when
 beta == 0), a per-row term r[b,i] and a per-column term c[b,j]; ``ref_sqnorms``
 and ``ref_sqdist`` are squared Euclidean norms and distances from their plain
-definitions.
+definitions; ``ref_sgemm_batched2`` takes two batch levels with grouped inputs,
+and ``ref_attention`` is scaled dot-product attention (scores, softmax, times
+V) over the same two levels.
 """
 from __future__ import annotations
 
@@ -47,7 +49,7 @@ _lib = None
 def build(src: str = _SRC, out: str = _LIB_PATH, extra_flags=()) -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-           *extra_flags, src, "-o", out + ".tmp"]
+           *extra_flags, src, "-lm", "-o", out + ".tmp"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out
@@ -99,6 +101,14 @@ def _bind(lib):
         _fptr, _i64, _i64, _i64, _i64, _i64,
         _fptr, _i64, _i64, _i64, _i64, _i64,
         _int,
+        _fptr, _i64, _i64, _i64, _i64,
+    ]
+    lib.oracle_attention.restype = _int
+    lib.oracle_attention.argtypes = [
+        _i64, _i64, _i64, _i64, _i64, _f32, _int,
+        _fptr, _i64, _i64, _i64, _i64,
+        _fptr, _i64, _i64, _i64, _i64, _i64,
+        _fptr, _i64, _i64, _i64, _i64,
         _fptr, _i64, _i64, _i64, _i64,
     ]
     lib.oracle_num_threads.restype = _int
@@ -352,6 +362,33 @@ def ref_sgemm_batched2(nb_outer, nb_inner, m, n, k, alpha,
     if rc != 0:
         raise RuntimeError(f"oracle_sgemm_batched2 returned {rc}")
     return C
+
+
+def ref_attention(nb_outer, nb_inner, tq, tk, d, alpha, causal,
+                  Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+                  K, sK_outer, sK_inner, g, sK_row, sK_col,
+                  V, sV_outer, sV_inner, sV_row, sV_col,
+                  O, sO_outer, sO_inner, sO_row, sO_col, lib=None):
+    """O[o,i] <- softmax(alpha * Q[o,i] K[o,i//g]^T (causal: query q sees keys
+    j <= q + tk - tq)) V[o,i//g], row by row in fp64; writes O in place."""
+    lib = lib or _get_lib()
+    Q, K, V = _as_storage(Q, "Q"), _as_storage(K, "K"), _as_storage(V, "V")
+    O = _as_storage(O, "O", writable=True)
+    if min(nb_outer, nb_inner, tq, tk, d) < 0 or g < 1:
+        raise ValueError("negative size or group below 1")
+    kv = -(-nb_inner // g) if nb_inner else 0
+    _check_view(Q, "Q", (nb_outer, nb_inner, tq, d), (sQ_outer, sQ_inner, sQ_row, sQ_col))
+    _check_view(K, "K", (nb_outer, kv, tk, d), (sK_outer, sK_inner, sK_row, sK_col))
+    _check_view(V, "V", (nb_outer, kv, tk, d), (sV_outer, sV_inner, sV_row, sV_col))
+    _check_view(O, "O", (nb_outer, nb_inner, tq, d), (sO_outer, sO_inner, sO_row, sO_col))
+    rc = lib.oracle_attention(nb_outer, nb_inner, tq, tk, d, float(alpha), int(bool(causal)),
+                              _ptr(Q), sQ_outer, sQ_inner, sQ_row, sQ_col,
+                              _ptr(K), sK_outer, sK_inner, g, sK_row, sK_col,
+                              _ptr(V), sV_outer, sV_inner, sV_row, sV_col,
+                              _ptr(O), sO_outer, sO_inner, sO_row, sO_col)
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention returned {rc}")
+    return O
 
 
 def num_threads(lib=None) -> int:

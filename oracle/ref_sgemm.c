@@ -31,12 +31,15 @@
  *
  * The general epilogue (any beta, a per-row and a per-column term) and the
  * squared norms and distances follow the same rules: every term is formed in
- * fp64 and the element is rounded to fp32 once.
+ * fp64 and the element is rounded to fp32 once.  So does attention (scores,
+ * softmax and the product with V, all in fp64, exp from the C library).
  *
- * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared ... -lm (no fast-math).
  */
+#include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -226,6 +229,83 @@ int oracle_sgemm_batched2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t
                             accumulate_beta(accumulate), Cb, 0, sC_row, sC_col, NULL, 0, 0, NULL, 0, 0, 0);
         }
     return 0;
+}
+
+/*
+ * Scaled dot-product attention over two batch levels, one query row at a
+ * time, in the three steps the rvllm post uses (sections "Matmuls go to
+ * cuBLAS" and "The kernels"): scores s_j = alpha * <Q[q,:], K[j,:]> (the
+ * 1/sqrt(head_dim) scale rides in alpha), a softmax over the visible keys
+ * taken as max, then the sum of exp(s_j - max), then the division, and the
+ * probabilities times V.  With `causal`, query q of tq sees keys
+ * j <= q + (tk - tq): the queries are the last tq positions of a context of
+ * tk (a prefill with tq = tk sees j <= q; one decode query sees every key);
+ * this is the attention mask the post adds before its softmax.
+ *
+ *   O[o,i,q,c] = sum_j softmax_j(s)[j] * V[o, i/g, j, c]
+ *
+ * Q[o,i] and O[o,i] are tq x d, K[o, i/g] is tk x d and V[o, i/g] tk x d,
+ * each addressed by (outer, inner, row, col) strides; g query heads share
+ * one key/value head.  Every step runs in fp64 (exp of fp64 arguments) and
+ * O is rounded to fp32 once.  Returns 0, or -1 for a negative size, a group
+ * below 1, tk = 0 with queries to answer, or causal with tq > tk (a query
+ * that would see no key).
+ */
+int oracle_attention(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                     float alpha, int causal,
+                     const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row, int64_t sQ_col,
+                     const float *K, int64_t sK_outer, int64_t sK_inner, int64_t g,
+                     int64_t sK_row, int64_t sK_col,
+                     const float *V, int64_t sV_outer, int64_t sV_inner, int64_t sV_row, int64_t sV_col,
+                     float *O, int64_t sO_outer, int64_t sO_inner, int64_t sO_row, int64_t sO_col)
+{
+    if (nb_outer < 0 || nb_inner < 0 || tq < 0 || tk < 0 || d < 0 || g < 1)
+        return -1;
+    const int64_t rows = nb_outer * nb_inner * tq;
+    if (rows == 0)
+        return 0;
+    if (tk == 0 || (causal && tq > tk))
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t w = 0; w < rows; ++w) {
+        const int64_t o = w / (nb_inner * tq), i = (w / tq) % nb_inner, q = w % tq;
+        const float *Qr = Q + o * sQ_outer + i * sQ_inner + q * sQ_row;
+        const float *Kb = K + o * sK_outer + (i / g) * sK_inner;
+        const float *Vb = V + o * sV_outer + (i / g) * sV_inner;
+        float *Or = O + o * sO_outer + i * sO_inner + q * sO_row;
+        const int64_t seen = causal ? q + (tk - tq) + 1 : tk;   /* keys 0 .. seen-1 */
+        double *s = (double *)malloc((size_t)seen * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        for (int64_t j = 0; j < seen; ++j) {
+            double dot = 0.0;
+            for (int64_t p = 0; p < d; ++p)
+                dot += (double)Qr[p * sQ_col] * (double)Kb[j * sK_row + p * sK_col];
+            s[j] = (double)alpha * dot;
+        }
+        double mx = s[0];
+        for (int64_t j = 1; j < seen; ++j)
+            if (s[j] > mx) mx = s[j];
+        double z = 0.0;
+        for (int64_t j = 0; j < seen; ++j) {
+            s[j] = exp(s[j] - mx);
+            z += s[j];
+        }
+        for (int64_t j = 0; j < seen; ++j)
+            s[j] /= z;
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < seen; ++j)
+                acc += s[j] * (double)Vb[j * sV_row + c * sV_col];
+            Or[c * sO_col] = (float)acc;
+        }
+        free(s);
+    }
+    return bad ? -1 : 0;
 }
 
 /*

@@ -535,9 +535,148 @@ def pin_batched2_gqa_row_folding(lib):
     assert np.array_equal(S1, S2)
 
 
+# ------------------------------------------------------------------ attention
+
+def _attn(lib, Q, K, V, alpha, causal, g=1, order="heads"):
+    """Run the oracle's attention on logical [outer][head][token][dim] arrays
+    stored head-major or token-major ([outer][token][head][dim]); returns O as
+    a logical [outer][head][tq][dim] float32 array."""
+    def store(X):
+        no, h, t, d = X.shape
+        if order == "heads":
+            return np.ascontiguousarray(X, np.float32).ravel(), (h * t * d, t * d, d, 1)
+        return (np.ascontiguousarray(X.transpose(0, 2, 1, 3), np.float32).ravel(),
+                (t * h * d, d, h * d, 1))
+    no, h, tq, d = Q.shape
+    tk = K.shape[2]
+    q, sq = store(Q)
+    k, sk = store(K)
+    v, sv = store(V)
+    o, so = store(np.zeros((no, h, tq, d), np.float32))
+    oracle.ref_attention(no, h, tq, tk, d, alpha, causal, q, *sq, k, sk[0], sk[1], g, sk[2], sk[3],
+                         v, *sv, o, *so, lib=lib)
+    if order == "heads":
+        return o.reshape(no, h, tq, d)
+    return o.reshape(no, tq, h, d).transpose(0, 2, 1, 3)
+
+
+def _visible(tq, tk, causal):
+    """mask[q, j]: key j is seen by query q (the queries are the last tq of tk
+    positions)."""
+    if not causal:
+        return np.ones((tq, tk), bool)
+    return np.arange(tk)[None, :] <= np.arange(tq)[:, None] + (tk - tq)
+
+
+def pin_attention_closed_forms(lib):
+    """Closed forms of softmax attention: equal scores (Q = 0, or alpha = 0)
+    weight every visible key alike, so each output row is the mean of the
+    visible V rows; a query that sees one key returns that V row exactly; a
+    key whose score leads by 40 or more takes all the weight (e^-40 is below
+    fp32 resolution), so the output is that key's V row.  Causal and not, decode
+    (tq < tk) and prefill, one and several KV groups, both layouts."""
+    rng = np.random.default_rng(21)
+    for no, h, g, tq, tk, d, causal, order in ((1, 1, 1, 7, 7, 5, False, "heads"),
+                                               (2, 4, 2, 7, 7, 3, True, "tokens"),
+                                               (1, 3, 3, 3, 8, 4, True, "heads"),
+                                               (2, 2, 1, 1, 9, 6, True, "tokens")):
+        hk = h // g
+        V = rng.standard_normal((no, hk, tk, d)).astype(np.float32)
+        K = rng.standard_normal((no, hk, tk, d)).astype(np.float32)
+        Qr = rng.standard_normal((no, h, tq, d)).astype(np.float32)
+        mask = _visible(tq, tk, causal)
+        Vh = V[:, np.arange(h) // g].astype(np.float64)                  # [no][h][tk][d]
+        mean = (mask[None, None, :, :, None] * Vh[:, :, None]).sum(3) / mask.sum(1)[None, None, :, None]
+        for Q, alpha in ((np.zeros_like(Qr), 0.7), (Qr, 0.0)):
+            O = _attn(lib, Q, K, V, alpha, causal, g, order)
+            tol = 4 * np.spacing(np.float32(np.abs(V).max()))
+            assert np.abs(O - mean).max() <= tol, (no, h, g, tq, tk, causal, order)
+        if causal and tq == tk:
+            O = _attn(lib, Qr, K, V, 0.5, True, g, order)
+            assert np.array_equal(O[:, :, 0], V[:, np.arange(h) // g, 0])
+    # One key of one row: every query sees exactly that V row.
+    V1 = rng.standard_normal((2, 2, 1, 5)).astype(np.float32)
+    K1 = rng.standard_normal((2, 2, 1, 5)).astype(np.float32)
+    Q1 = rng.standard_normal((2, 2, 4, 5)).astype(np.float32)
+    O = _attn(lib, Q1, K1, V1, 3.0, False)
+    assert np.array_equal(O, np.broadcast_to(V1, O.shape))
+    # A dominant key: K = c I, Q[q] = e_pick[q], alpha 0.5 -> score c/2 for
+    # the picked key, 0 for the rest; causal picks stay visible (pick[q] <= q).
+    # c = 4000 puts the lead far past exp's range, so only a softmax that
+    # subtracts the true row maximum stays finite.
+    d = tk = tq = 8
+    pick = np.array([0, 1, 0, 2, 4, 3, 6, 1])
+    Q = np.eye(d, dtype=np.float32)[pick][None, None]
+    V = rng.standard_normal((1, 1, tk, d)).astype(np.float32)
+    for c in (80.0, 4000.0):
+        K = (c * np.eye(tk, d, dtype=np.float32))[None, None]
+        for causal in (False, True):
+            for order in ("heads", "tokens"):
+                O = _attn(lib, Q, K, V, 0.5, causal, 1, order)
+                assert np.array_equal(O[0, 0], V[0, 0, pick]), (c, causal, order)
+
+
+def pin_attention_invariants(lib):
+    """Invariants of the definition: adding the same amount to every score of
+    a row changes nothing (an extra dimension with Q = 1 and K = 1e4 shifts
+    the scores by alpha*1e4, far past exp's range); permuting the keys (K and
+    V rows together) changes nothing without a mask; one decode query equals
+    the last row of the causal prefill over the same context; grouped KV heads
+    equal each KV head repeated for its query heads (same bits)."""
+    rng = np.random.default_rng(22)
+    no, h, g, t, d = 2, 4, 2, 9, 6
+    hk = h // g
+    Q = rng.standard_normal((no, h, t, d)).astype(np.float32)
+    K = rng.standard_normal((no, hk, t, d)).astype(np.float32)
+    V = rng.standard_normal((no, hk, t, d)).astype(np.float32)
+    for causal in (False, True):
+        base = _attn(lib, Q, K, V, 0.25, causal, g)
+        Qs = np.concatenate([Q, np.ones((no, h, t, 1), np.float32)], 3)
+        Ks = np.concatenate([K, np.full((no, hk, t, 1), 1e4, np.float32)], 3)
+        Vs = np.concatenate([V, np.zeros((no, hk, t, 1), np.float32)], 3)
+        shifted = _attn(lib, Qs, Ks, Vs, 0.25, causal, g)[..., :d]
+        assert np.all(np.isfinite(shifted))
+        assert np.abs(shifted - base).max() <= 1e-6 * np.abs(V).max(), causal
+        rep = _attn(lib, Q, np.repeat(K, g, 1), np.repeat(V, g, 1), 0.25, causal, 1)
+        assert np.array_equal(rep, base), causal
+    perm = rng.permutation(t)
+    Op = _attn(lib, Q, K[:, :, perm], V[:, :, perm], 0.25, False, g)
+    assert np.abs(Op - _attn(lib, Q, K, V, 0.25, False, g)).max() <= 1e-6 * np.abs(V).max()
+    prefill = _attn(lib, Q, K, V, 0.25, True, g, "tokens")
+    for last in (t, 5):
+        dec = _attn(lib, Q[:, :, last - 1:last], K[:, :, :last], V[:, :, :last], 0.25, True, g, "tokens")
+        full = prefill if last == t else _attn(lib, Q[:, :, :last], K[:, :, :last], V[:, :, :last],
+                                               0.25, True, g, "tokens")
+        assert np.array_equal(dec[:, :, 0], full[:, :, last - 1]), last
+
+
+def pin_attention_numpy_float64(lib):
+    """Against numpy's float64 route (matmul, exp, sum) on random data in
+    both layouts with grouped heads: the oracle rounds once, so it must sit
+    within one fp32 spacing of the float64 result."""
+    rng = np.random.default_rng(23)
+    for no, h, g, tq, tk, d, causal, order in ((2, 6, 3, 13, 13, 16, True, "tokens"),
+                                               (1, 2, 1, 5, 17, 8, True, "heads"),
+                                               (3, 4, 4, 11, 7, 12, False, "tokens")):
+        hk = h // g
+        Q = rng.standard_normal((no, h, tq, d)).astype(np.float32)
+        K = rng.standard_normal((no, hk, tk, d)).astype(np.float32)
+        V = rng.standard_normal((no, hk, tk, d)).astype(np.float32)
+        alpha = 1.0 / np.sqrt(d)
+        O = _attn(lib, Q, K, V, alpha, causal, g, order)
+        Kh = K[:, np.arange(h) // g].astype(np.float64)
+        Vh = V[:, np.arange(h) // g].astype(np.float64)
+        S = np.float64(np.float32(alpha)) * (Q.astype(np.float64) @ Kh.transpose(0, 1, 3, 2))
+        S = np.where(_visible(tq, tk, causal), S, -np.inf)
+        P = np.exp(S - S.max(-1, keepdims=True))
+        ref = (P / P.sum(-1, keepdims=True)) @ Vh
+        assert np.all(np.abs(O - ref) <= np.spacing(np.abs(ref).astype(np.float32))), (no, h, tq, tk)
+
+
 PINS = [pin_all_ones, pin_identity, pin_k_zero, pin_golden_transpose_trace,
         pin_golden_column_major, pin_blas_linear_mapping, pin_blas_rowmajor_trick,
         pin_exact_bruteforce, pin_numpy_float64, pin_stride_swap, pin_transpose_identity,
         pin_batch_slices, pin_accumulate, pin_order_and_entries, pin_nan_and_canaries,
         pin_epilogue_bruteforce, pin_epilogue_closed_forms, pin_sqnorms, pin_sqdist,
-        pin_batched2_bthd_gqa, pin_batched2_gqa_row_folding]
+        pin_batched2_bthd_gqa, pin_batched2_gqa_row_folding, pin_attention_closed_forms,
+        pin_attention_invariants, pin_attention_numpy_float64]

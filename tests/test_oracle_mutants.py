@@ -53,6 +53,17 @@ MUTANTS = {
     "kv_group_ignored": [("B + o * sB_outer + (i / gB) * sB_inner", "B + o * sB_outer + (i / 1) * sB_inner")],
     "group_of_the_wrong_operand": [("B + o * sB_outer + (i / gB) * sB_inner", "B + o * sB_outer + (i / gA) * sB_inner")],
     "batch_levels_swapped_in_C": [("C + o * sC_outer + i * sC_inner", "C + i * sC_outer + o * sC_inner")],
+    "mask_off_by_one": [("causal ? q + (tk - tq) + 1 : tk", "causal ? (q + (tk - tq) + 2 < tk ? q + (tk - tq) + 2 : tk) : tk")],
+    "mask_top_left": [("causal ? q + (tk - tq) + 1 : tk", "causal ? q + 1 : tk")],
+    "no_max_subtraction": [("s[j] = exp(s[j] - mx);", "s[j] = exp(s[j]);")],
+    "softmax_not_normalised": [("s[j] /= z;", "s[j] /= 1.0;")],
+    "scores_without_alpha": [("s[j] = (double)alpha * dot;", "s[j] = dot;")],
+    "softmax_max_of_first_key": [("if (s[j] > mx) mx = s[j];", "if (0) mx = s[j];")],
+    "attention_V_transposed": [("Vb[j * sV_row + c * sV_col]", "Vb[c * sV_row + j * sV_col]")],
+    "attention_K_at_query_row": [("Kb[j * sK_row + p * sK_col]", "Kb[q * sK_row + p * sK_col]")],
+    "attention_kv_group_ignored_in_K": [("K + o * sK_outer + (i / g) * sK_inner", "K + o * sK_outer + (i % g) * sK_inner")],
+    "attention_kv_group_ignored_in_V": [("V + o * sV_outer + (i / g) * sV_inner", "V + o * sV_outer + (i % g) * sV_inner")],
+    "attention_last_dim_skipped": [("for (int64_t p = 0; p < d; ++p)", "for (int64_t p = 0; p < d - 1; ++p)")],
 }
 
 # The brute-force pin at full size is slow; mutants see a smaller sweep.
