@@ -42,7 +42,7 @@ METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
 DEFAULT_WORKLOAD = "square4096_acc"
 KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/" + f for f in (
     "mfma_kernel.hpp", "persist_kernel.hpp", "wave_kernel.hpp", "kernels.hpp", "kernels.hip",
-    "plan.hpp", "plan.cpp")]
+    "plan.hpp", "plan.cpp", "buffer.hpp", "attn_kernel.hip", "attention.hpp", "attention.cpp")]
 
 
 def kernel_sources_sha256() -> str:
@@ -73,11 +73,41 @@ def traffic_record(workload: str, kernel: str):
         return None
 
 
+def cpu_baseline_attention(p, seconds: float) -> dict:
+    """The oracle's attention on the first H (sequence, head) pairs of the
+    same call (whole heads, every query row), H chosen so the run takes
+    roughly `seconds`."""
+    import oracle
+    threads = oracle.num_threads()
+    out = p.O.storage.copy()
+    (ko, ki, kr, kc) = p.K.strides
+
+    def run(heads):
+        no, ni = (1, heads) if heads <= p.nb_inner else (heads // p.nb_inner, p.nb_inner)
+        t0 = time.perf_counter()
+        oracle.ref_attention(no, ni, p.tq, p.tk, p.d, p.alpha, p.causal, p.Q.storage, *p.Q.strides,
+                             p.K.storage, ko, ki, p.g, kr, kc, p.V.storage, *p.V.strides,
+                             out, *p.O.strides)
+        return no * ni, time.perf_counter() - t0
+
+    total = p.nb_outer * p.nb_inner
+    heads, t = run(1)
+    while t < seconds / 8 and heads < total:
+        heads, t = run(min(total, heads * 4) if heads * 4 <= p.nb_inner
+                       else min(total, max(p.nb_inner, heads * 4) // p.nb_inner * p.nb_inner))
+    flops = 4.0 * p.d * p.visible_pairs * heads
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"all {p.tq} query rows of the first {heads} (sequence, head) pairs "
+                      f"({flops / 1e9:.2f} GFLOP in {t:.1f} s)"}
+
+
 def cpu_baseline(p, seconds: float) -> dict:
     """The oracle on rows 0..R-1 of batch 0 of the same product, R chosen so
     the run takes roughly `seconds`."""
     import oracle
     from strided_fp32_gemm_amd import workloads as wl
+    if wl.kind(p.name) == "attention":
+        return cpu_baseline_attention(p, seconds)
     threads = oracle.num_threads()
     kind = wl.kind(p.name)
     out = (p.D if kind == "dist" else p.C).storage.copy()
@@ -140,6 +170,12 @@ def _step_fn(p, dev, stream):
                                       sY[0], sY[2], sY[1], 0, dD.data_ptr(), *p.D.strides, num_cus=0)
         info["kernel"] += "_vec (after 2 sqnorms launches)"
         return (lambda: sg.sgemm_pairwise_sqdist(*args, stream=stream)), info, (dX, dY, dD, ws)
+    if kind == "attention":
+        dq, dk, dv, do = (torch.from_numpy(x.storage).to(dev) for x in (p.Q, p.K, p.V, p.O))
+        args = p.call_args(dq, dk, dv, do)
+        info = sg.sgemm_attention_describe(*p.call_args(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                                        do.data_ptr()))
+        return (lambda: sg.sgemm_attention(*args, stream=stream)), info, (dq, dk, dv, do)
     dA, dB = torch.from_numpy(p.A.storage).to(dev), torch.from_numpy(p.B.storage).to(dev)
     dC = torch.from_numpy(p.C.storage).to(dev)
     if kind == "batched2":
@@ -226,6 +262,13 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
 def _config(p, info) -> dict:
     from strided_fp32_gemm_amd import workloads as wl
 
+    if wl.kind(p.name) == "attention":
+        return {"workload": p.name, "op": "softmax(alpha Q K^T) V, fused", "nb_outer": p.nb_outer,
+                "nb_inner": p.nb_inner, "tq": p.tq, "tk": p.tk, "d": p.d, "g": p.g, "alpha": p.alpha,
+                "causal": bool(p.causal),
+                "strides": {"Q": list(p.Q.strides), "K": list(p.K.strides), "V": list(p.V.strides),
+                            "O": list(p.O.strides)},
+                "flops_per_step": p.flops, "kernel": info["kernel"], "workgroups": info["workgroups"]}
     c = {"workload": p.name, "batch": p.batch, "m": p.m, "n": p.n, "k": p.k}
     if wl.kind(p.name) == "batched2":
         c.update({"nb_outer": p.nb_outer, "nb_inner": p.nb_inner, "gA": p.A.group, "gB": p.B.group,

@@ -263,6 +263,74 @@ int sgemm_plan_describe2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t 
                          float *C, int64_t sC_outer, int64_t sC_inner, int64_t sC_row,
                          int64_t sC_col, int path, int num_cus, sgemm_plan_info *info);
 
+/*
+ * Fused scaled dot-product attention over two batch levels (the three-step
+ * attention of the rvllm post, section "Matmuls go to cuBLAS": scores as a
+ * strided batched product with the 1/sqrt(head_dim) scale in alpha, a
+ * softmax, the probabilities times V; done in one pass so the scores never
+ * reach memory, the fusion its section "What's basic about it" names):
+ *
+ *     O[o,i,q,:] = sum_j softmax_j(alpha * <Q[o,i,q,:], K[o,i/g,j,:]>) V[o,i/g,j,:]
+ *
+ * for o < nb_outer, i < nb_inner (e.g. sequence and query head), q < tq,
+ * over the keys j < tk, or with causal != 0 over j <= q + tk - tq (the
+ * queries are the last tq positions of the context: a prefill with tq = tk
+ * sees j <= q, one decode query sees every key).  Each operand X is addressed
+ * as X + o*sX_outer + h*sX_inner + row*sX_row + c*sX_col, where h = i for Q
+ * and O and h = i/g for K and V (g query heads share a key/value head; a g
+ * at least nb_inner maps every query head to the first).  Q and O are
+ * tq x d, K and V are tk x d.  A [sequence][token][head][dim] buffer is read
+ * as it is (row stride = heads*dim).
+ *
+ * Sizes: nb_outer, tq, tk, d >= 0, nb_inner and g >= 1
+ * (SGEMM_ERR_INVALID_SIZE); tk = 0 with queries to answer, or causal with
+ * tq > tk, is SGEMM_ERR_INVALID_SIZE (a query would see no key); d above 256
+ * is SGEMM_ERR_UNSUPPORTED.  Strides in elements, >= 0.  O must give every
+ * output its own element and must not overlap Q, K or V (SGEMM_ERR_C_ALIAS).
+ * Pointers are device pointers owned by the caller; no workspace, nothing is
+ * allocated.  Arithmetic is fp32 (matrix cores for d = 64 with unit column
+ * strides and 16-byte aligned rows, a 64-bit generic kernel otherwise); the
+ * order of every sum is fixed, so results are reproducible bit for bit.
+ * Enqueued on `stream` without synchronising.  Returns an sgemm_status.
+ */
+int sgemm_attention(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                    float alpha, int causal,
+                    const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row, int64_t sQ_col,
+                    const float *K, int64_t sK_outer, int64_t sK_inner, int64_t g,
+                    int64_t sK_row, int64_t sK_col,
+                    const float *V, int64_t sV_outer, int64_t sV_inner, int64_t sV_row, int64_t sV_col,
+                    float *O, int64_t sO_outer, int64_t sO_inner, int64_t sO_row, int64_t sO_col,
+                    void *stream);
+
+/* sgemm_attention with the kernel forced: SGEMM_PATH_AUTO, SGEMM_PATH_MFMA
+ * (SGEMM_ERR_UNSUPPORTED if the matrix-core kernel cannot serve the call) or
+ * SGEMM_PATH_GENERIC; SGEMM_PATH_WAVE is SGEMM_ERR_INVALID_PATH.  Returns an
+ * sgemm_status. */
+int sgemm_attention_path(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                         float alpha, int causal,
+                         const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row,
+                         int64_t sQ_col,
+                         const float *K, int64_t sK_outer, int64_t sK_inner, int64_t g,
+                         int64_t sK_row, int64_t sK_col,
+                         const float *V, int64_t sV_outer, int64_t sV_inner, int64_t sV_row,
+                         int64_t sV_col,
+                         float *O, int64_t sO_outer, int64_t sO_inner, int64_t sO_row, int64_t sO_col,
+                         int path, void *stream);
+
+/* The plan of a sgemm_attention_path call (validated the same way, no
+ * device access): tile_m = query rows per workgroup.  Returns an
+ * sgemm_status. */
+int sgemm_attention_describe(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                             float alpha, int causal,
+                             const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row,
+                             int64_t sQ_col,
+                             const float *K, int64_t sK_outer, int64_t sK_inner, int64_t g,
+                             int64_t sK_row, int64_t sK_col,
+                             const float *V, int64_t sV_outer, int64_t sV_inner, int64_t sV_row,
+                             int64_t sV_col,
+                             float *O, int64_t sO_outer, int64_t sO_inner, int64_t sO_row,
+                             int64_t sO_col, int path, sgemm_plan_info *info);
+
 /* Static description of a status code (never NULL). */
 const char *sgemm_status_string(int status);
 

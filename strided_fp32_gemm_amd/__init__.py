@@ -19,6 +19,9 @@ from ._binding import (  # noqa: F401
     PATH_WAVE,
     SgemmError,
     load,
+    sgemm_attention,
+    sgemm_attention_describe,
+    sgemm_attention_path,
     sgemm_last_error,
     sgemm_pairwise_sqdist,
     sgemm_plan_describe,

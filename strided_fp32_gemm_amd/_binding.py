@@ -30,7 +30,8 @@ STATUS = {
 # Every symbol include/sgemm_strided.h declares.
 EXPORTS = ("sgemm_strided_batched", "sgemm_strided_batched_path", "sgemm_strided_batched_ex",
            "sgemm_strided_batched_ex_path", "sgemm_strided_batched2", "sgemm_strided_batched2_path",
-           "sgemm_sqnorms", "sgemm_pairwise_sqdist",
+           "sgemm_sqnorms", "sgemm_pairwise_sqdist", "sgemm_attention", "sgemm_attention_path",
+           "sgemm_attention_describe",
            "sgemm_plan_describe", "sgemm_plan_describe2", "sgemm_status_string", "sgemm_last_error")
 
 
@@ -88,6 +89,12 @@ _B2_ARGS = [_i64, _i64, _i64, _i64, _i64, _f32,
             _int,
             _vp, _i64, _i64, _i64, _i64]
 
+_ATTN_ARGS = [_i64, _i64, _i64, _i64, _i64, _f32, _int,
+              _vp, _i64, _i64, _i64, _i64,
+              _vp, _i64, _i64, _i64, _i64, _i64,
+              _vp, _i64, _i64, _i64, _i64,
+              _vp, _i64, _i64, _i64, _i64]
+
 _lib = None
 
 
@@ -113,6 +120,12 @@ def load(path: str = LIB_PATH):
     lib.sgemm_strided_batched2.argtypes = _B2_ARGS + [_vp]
     lib.sgemm_strided_batched2_path.restype = _int
     lib.sgemm_strided_batched2_path.argtypes = _B2_ARGS + [_int, _vp]
+    lib.sgemm_attention.restype = _int
+    lib.sgemm_attention.argtypes = _ATTN_ARGS + [_vp]
+    lib.sgemm_attention_path.restype = _int
+    lib.sgemm_attention_path.argtypes = _ATTN_ARGS + [_int, _vp]
+    lib.sgemm_attention_describe.restype = _int
+    lib.sgemm_attention_describe.argtypes = _ATTN_ARGS + [_int, ctypes.POINTER(PlanInfo)]
     lib.sgemm_sqnorms.restype = _int
     lib.sgemm_sqnorms.argtypes = [_i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp]
     lib.sgemm_pairwise_sqdist.restype = _int
@@ -271,6 +284,57 @@ def sgemm_strided_batched2_path(nb_outer, nb_inner, m, n, k, alpha,
                     B, sB_outer, sB_inner, gB, sB_row, sB_col, accumulate,
                     C, sC_outer, sC_inner, sC_row, sC_col)
     _check(load().sgemm_strided_batched2_path(*args, int(path), _stream(stream)))
+
+
+def _attn_list(nb_outer, nb_inner, tq, tk, d, alpha, causal,
+               Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+               K, sK_outer, sK_inner, g, sK_row, sK_col,
+               V, sV_outer, sV_inner, sV_row, sV_col,
+               O, sO_outer, sO_inner, sO_row, sO_col):
+    return [int(nb_outer), int(nb_inner), int(tq), int(tk), int(d), float(alpha), int(bool(causal)),
+            _ptr(Q), int(sQ_outer), int(sQ_inner), int(sQ_row), int(sQ_col),
+            _ptr(K), int(sK_outer), int(sK_inner), int(g), int(sK_row), int(sK_col),
+            _ptr(V), int(sV_outer), int(sV_inner), int(sV_row), int(sV_col),
+            _ptr(O), int(sO_outer), int(sO_inner), int(sO_row), int(sO_col)]
+
+
+def sgemm_attention(nb_outer, nb_inner, tq, tk, d, alpha, causal,
+                    Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+                    K, sK_outer, sK_inner, g, sK_row, sK_col,
+                    V, sV_outer, sV_inner, sV_row, sV_col,
+                    O, sO_outer, sO_inner, sO_row, sO_col, stream=None) -> None:
+    """O <- softmax(alpha Q K^T [causal]) V over two batch levels, fused,
+    through the C ABI (K and V head i//g for query head i)."""
+    args = _attn_list(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer, sQ_inner, sQ_row,
+                      sQ_col, K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer, sV_inner, sV_row,
+                      sV_col, O, sO_outer, sO_inner, sO_row, sO_col)
+    _check(load().sgemm_attention(*args, _stream(stream)))
+
+
+def sgemm_attention_path(nb_outer, nb_inner, tq, tk, d, alpha, causal,
+                         Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+                         K, sK_outer, sK_inner, g, sK_row, sK_col,
+                         V, sV_outer, sV_inner, sV_row, sV_col,
+                         O, sO_outer, sO_inner, sO_row, sO_col, path=PATH_AUTO, stream=None) -> None:
+    """sgemm_attention with the kernel forced (PATH_AUTO, PATH_MFMA, PATH_GENERIC)."""
+    args = _attn_list(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer, sQ_inner, sQ_row,
+                      sQ_col, K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer, sV_inner, sV_row,
+                      sV_col, O, sO_outer, sO_inner, sO_row, sO_col)
+    _check(load().sgemm_attention_path(*args, int(path), _stream(stream)))
+
+
+def sgemm_attention_describe(nb_outer, nb_inner, tq, tk, d, alpha, causal,
+                             Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+                             K, sK_outer, sK_inner, g, sK_row, sK_col,
+                             V, sV_outer, sV_inner, sV_row, sV_col,
+                             O, sO_outer, sO_inner, sO_row, sO_col, path=PATH_AUTO) -> dict:
+    """The plan of a sgemm_attention_path call (no device access)."""
+    info = PlanInfo()
+    args = _attn_list(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer, sQ_inner, sQ_row,
+                      sQ_col, K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer, sV_inner, sV_row,
+                      sV_col, O, sO_outer, sO_inner, sO_row, sO_col)
+    _check(load().sgemm_attention_describe(*args, int(path), ctypes.byref(info)))
+    return info.as_dict()
 
 
 def sgemm_sqnorms(batch, count, length, X, sX_batch, sX_item, sX_elem, out, sO_batch, sO_item,

@@ -16,6 +16,7 @@
 #include <cstring>
 #include <string>
 
+#include "attention.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
 
@@ -138,9 +139,104 @@ int pack2(int64_t nb_outer, int64_t nb_inner, int64_t m, int64_t n, int64_t k, f
     return SGEMM_OK;
 }
 
+sgemm::AttnCall pack_attention(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                               float alpha, int causal, const float *Q, int64_t sQ_outer,
+                               int64_t sQ_inner, int64_t sQ_row, int64_t sQ_col, const float *K,
+                               int64_t sK_outer, int64_t sK_inner, int64_t g, int64_t sK_row,
+                               int64_t sK_col, const float *V, int64_t sV_outer, int64_t sV_inner,
+                               int64_t sV_row, int64_t sV_col, float *O, int64_t sO_outer,
+                               int64_t sO_inner, int64_t sO_row, int64_t sO_col) {
+    sgemm::AttnCall c;
+    c.nb_outer = nb_outer; c.nb_inner = nb_inner; c.tq = tq; c.tk = tk; c.d = d; c.g = g;
+    c.alpha = alpha; c.causal = causal;
+    c.Q = reinterpret_cast<uintptr_t>(Q); c.K = reinterpret_cast<uintptr_t>(K);
+    c.V = reinterpret_cast<uintptr_t>(V); c.O = reinterpret_cast<uintptr_t>(O);
+    const int64_t sq[4] = {sQ_outer, sQ_inner, sQ_row, sQ_col}, sk[4] = {sK_outer, sK_inner, sK_row, sK_col},
+                  sv[4] = {sV_outer, sV_inner, sV_row, sV_col}, so[4] = {sO_outer, sO_inner, sO_row, sO_col};
+    for (int a = 0; a < 4; ++a) { c.sQ[a] = sq[a]; c.sK[a] = sk[a]; c.sV[a] = sv[a]; c.sO[a] = so[a]; }
+    return c;
+}
+
+bool attention_path_ok(int path) {
+    return path == SGEMM_PATH_AUTO || path == SGEMM_PATH_MFMA || path == SGEMM_PATH_GENERIC;
+}
+
+int plan_attention(const sgemm::AttnCall &c, int path, sgemm::AttnPlan &plan) {
+    if (!attention_path_ok(path)) return fail(SGEMM_ERR_INVALID_PATH, "attention runs on AUTO, MFMA or GENERIC");
+    std::string why;
+    int st = sgemm::validate_attention(c, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    st = sgemm::make_attention_plan(c, static_cast<sgemm::AttnPath>(path), plan, why);
+    return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
+}
+
 }  // namespace
 
 extern "C" {
+
+int sgemm_attention_path(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                         float alpha, int causal, const float *Q, int64_t sQ_outer, int64_t sQ_inner,
+                         int64_t sQ_row, int64_t sQ_col, const float *K, int64_t sK_outer,
+                         int64_t sK_inner, int64_t g, int64_t sK_row, int64_t sK_col, const float *V,
+                         int64_t sV_outer, int64_t sV_inner, int64_t sV_row, int64_t sV_col, float *O,
+                         int64_t sO_outer, int64_t sO_inner, int64_t sO_row, int64_t sO_col, int path,
+                         void *stream) {
+    sgemm::AttnPlan plan;
+    int st = plan_attention(pack_attention(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer,
+                                           sQ_inner, sQ_row, sQ_col, K, sK_outer, sK_inner, g, sK_row,
+                                           sK_col, V, sV_outer, sV_inner, sV_row, sV_col, O, sO_outer,
+                                           sO_inner, sO_row, sO_col),
+                            path, plan);
+    if (st != SGEMM_OK) return st;
+    std::string why;
+    st = sgemm::launch_attention(plan, static_cast<hipStream_t>(stream), why);
+    return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
+}
+
+int sgemm_attention(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d, float alpha,
+                    int causal, const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row,
+                    int64_t sQ_col, const float *K, int64_t sK_outer, int64_t sK_inner, int64_t g,
+                    int64_t sK_row, int64_t sK_col, const float *V, int64_t sV_outer, int64_t sV_inner,
+                    int64_t sV_row, int64_t sV_col, float *O, int64_t sO_outer, int64_t sO_inner,
+                    int64_t sO_row, int64_t sO_col, void *stream) {
+    return sgemm_attention_path(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer, sQ_inner,
+                                sQ_row, sQ_col, K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer,
+                                sV_inner, sV_row, sV_col, O, sO_outer, sO_inner, sO_row, sO_col,
+                                SGEMM_PATH_AUTO, stream);
+}
+
+int sgemm_attention_describe(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                             float alpha, int causal, const float *Q, int64_t sQ_outer,
+                             int64_t sQ_inner, int64_t sQ_row, int64_t sQ_col, const float *K,
+                             int64_t sK_outer, int64_t sK_inner, int64_t g, int64_t sK_row,
+                             int64_t sK_col, const float *V, int64_t sV_outer, int64_t sV_inner,
+                             int64_t sV_row, int64_t sV_col, float *O, int64_t sO_outer,
+                             int64_t sO_inner, int64_t sO_row, int64_t sO_col, int path,
+                             sgemm_plan_info *info) {
+    if (!info) return fail(SGEMM_ERR_NULL_POINTER, "info is NULL");
+    sgemm::AttnPlan plan;
+    int st = plan_attention(pack_attention(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer,
+                                           sQ_inner, sQ_row, sQ_col, K, sK_outer, sK_inner, g, sK_row,
+                                           sK_col, V, sV_outer, sV_inner, sV_row, sV_col, O, sO_outer,
+                                           sO_inner, sO_row, sO_col),
+                            path, plan);
+    if (st != SGEMM_OK) return st;
+    std::memset(info, 0, sizeof *info);
+    info->path = plan.empty ? SGEMM_PATH_AUTO
+                            : (plan.path == sgemm::AttnPath::Mfma ? SGEMM_PATH_MFMA : SGEMM_PATH_GENERIC);
+    if (!plan.empty && plan.path == sgemm::AttnPath::Mfma) {
+        info->tile_m = plan.waves * 16; info->tile_n = 64; info->tile_k = 64;
+        info->vec_a = 4; info->vec_b = 4;
+    } else if (!plan.empty) {
+        info->tile_m = 4; info->tile_n = 1; info->tile_k = 1;
+        info->vec_a = 1; info->vec_b = 1;
+    }
+    info->waves = plan.empty ? 0 : plan.waves;
+    info->launches = plan.empty ? 0 : 1;
+    info->workgroups = plan.empty ? 0 : plan.workgroups;
+    std::strncpy(info->kernel, plan.kernel_name.c_str(), sizeof info->kernel - 1);
+    return SGEMM_OK;
+}
 
 int sgemm_strided_batched_path(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
                                const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,

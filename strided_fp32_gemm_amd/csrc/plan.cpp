@@ -7,6 +7,7 @@
 // (section "Safety": check every size a kernel depends on, then launch) is
 // what validate() and the buffer-range checks below implement.
 #include "plan.hpp"
+#include "extent.hpp"
 
 #include <algorithm>
 #include <cmath>
@@ -17,33 +18,6 @@
 namespace sgemm {
 
 namespace {
-
-bool mul64(int64_t x, int64_t y, int64_t &r) { return !__builtin_mul_overflow(x, y, &r); }
-bool add64(int64_t x, int64_t y, int64_t &r) { return !__builtin_add_overflow(x, y, &r); }
-
-// Largest element offset of a [e0, e1, e2] view with strides s*, or -1 on
-// overflow.  Extents are >= 1 here.
-int64_t last_offset(int64_t e0, int64_t s0, int64_t e1, int64_t s1, int64_t e2, int64_t s2) {
-    int64_t a, b, c, t, r;
-    if (!mul64(e0 - 1, s0, a) || !mul64(e1 - 1, s1, b) || !mul64(e2 - 1, s2, c)) return -1;
-    if (!add64(a, b, t) || !add64(t, c, r)) return -1;
-    return r;
-}
-
-// Same for a [e0, e1, e2, e3] view.
-int64_t last_offset4(int64_t e0, int64_t s0, int64_t e1, int64_t s1, int64_t e2, int64_t s2, int64_t e3,
-                     int64_t s3) {
-    int64_t head = last_offset(e0, s0, e1, s1, e2, s2), tail, r;
-    if (head < 0 || !mul64(e3 - 1, s3, tail) || !add64(head, tail, r)) return -1;
-    return r;
-}
-
-bool ranges_overlap(uintptr_t p, int64_t last_p, uintptr_t q, int64_t last_q) {
-    uintptr_t p_end = p + 4u * (uintptr_t)(last_p + 1);
-    uintptr_t q_end = q + 4u * (uintptr_t)(last_q + 1);
-    return p < q_end && q < p_end;
-}
-
 
 // Width (in floats) of the global loads along an operand's fast axis: 4
 // (16-byte loads) when the fast axis is contiguous, its extent a multiple of
@@ -138,19 +112,12 @@ int validate(const GemmArgs &a, std::string &why) {
         why = "an operand's extent times its strides overflows int64";
         return kErrUnsupported;
     }
-    // C must address every output at its own element: sorted by stride, each
-    // axis of extent > 1 has to step past everything the smaller axes reach.
-    struct Axis { int64_t extent, stride; } ax[4] = {
-        {outer, a.sC_batch}, {a.inner, a.sC_inner}, {a.m, a.sC_row}, {a.n, a.sC_col}};
-    std::sort(ax, ax + 4, [](const Axis &x, const Axis &y) { return x.stride < y.stride; });
-    int64_t reach = 0;
-    for (const Axis &x : ax) {
-        if (x.extent <= 1) continue;
-        if (x.stride <= reach) {
-            why = "C's strides map two outputs to the same element";
-            return kErrAlias;
-        }
-        reach += (x.extent - 1) * x.stride;
+    // C must address every output at its own element.
+    const int64_t c_ext[4] = {outer, a.inner, a.m, a.n};
+    const int64_t c_str[4] = {a.sC_batch, a.sC_inner, a.sC_row, a.sC_col};
+    if (!distinct_axes(c_ext, c_str)) {
+        why = "C's strides map two outputs to the same element";
+        return kErrAlias;
     }
     if (a.k > 0 && (ranges_overlap(a.C, lastC, a.A, lastA) || ranges_overlap(a.C, lastC, a.B, lastB))) {
         why = "C's address range overlaps A or B";

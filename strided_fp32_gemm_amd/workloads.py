@@ -35,12 +35,12 @@ ROOT_SEED = 2024
 # Benchmark workloads.
 WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
              "linear_bwd_dx", "linear_bwd_dw", "linear_xT", "linear_bias", "sqdist",
-             "attn_qk_gqa", "attn_pv_gqa")
+             "attn_qk_gqa", "attn_pv_gqa", "attn_fused", "attn_fused_causal")
 # Entry point each workload goes through: "plain" (sgemm_strided_batched),
 # "ex" (sgemm_strided_batched_ex), "dist" (sgemm_pairwise_sqdist) or
-# "batched2" (sgemm_strided_batched2).
+# "batched2" (sgemm_strided_batched2) or "attention" (sgemm_attention).
 KINDS = {"linear_bias": "ex", "sqdist": "dist", "attn_qk_gqa": "batched2",
-         "attn_pv_gqa": "batched2"}
+         "attn_pv_gqa": "batched2", "attn_fused": "attention", "attn_fused_causal": "attention"}
 
 
 def kind(name: str) -> str:
@@ -50,7 +50,8 @@ def kind(name: str) -> str:
 # Children of the root seed, in spawn order (the two halves of the linear
 # layer's backward pass share one draw of dy, W and x).
 SEED_NAMES = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
-              "linear_bwd", "linear_xT", "linear_bias", "sqdist", "attn_qk_gqa", "attn_pv_gqa")
+              "linear_bwd", "linear_xT", "linear_bias", "sqdist", "attn_qk_gqa", "attn_pv_gqa",
+              "attn_fused")
 
 
 @dataclasses.dataclass
@@ -440,6 +441,80 @@ def attn_pv_gqa() -> Problem2:
                     Operand2(P, sp), Operand2(V, sv, h // hk), Operand2(O, so))
 
 
+@dataclasses.dataclass
+class AttnProblem:
+    """One sgemm_attention call: O[o,i] <- softmax(alpha Q[o,i] K[o,i//g]^T,
+    causal or not) V[o,i//g] for o < nb_outer, i < nb_inner; Q, O are
+    tq x d, K, V are tk x d.  Strides are (outer, inner, row, col)."""
+    name: str
+    nb_outer: int
+    nb_inner: int
+    tq: int
+    tk: int
+    d: int
+    g: int
+    alpha: float
+    causal: bool
+    Q: Operand2
+    K: Operand2
+    V: Operand2
+    O: Operand2
+
+    @property
+    def batch(self) -> int:
+        return self.nb_outer * self.nb_inner
+
+    @property
+    def visible_pairs(self) -> int:
+        """(query, key) pairs the definition sums over, per (o, i)."""
+        if not self.causal:
+            return self.tq * self.tk
+        shift = self.tk - self.tq
+        return sum(min(q + shift + 1, self.tk) for q in range(self.tq))
+
+    @property
+    def flops(self) -> int:
+        """The two products' multiply-adds over the visible pairs (2*d each
+        for the scores and for P V)."""
+        return 4 * self.d * self.batch * self.visible_pairs
+
+    def call_args(self, q, k, v, o):
+        """Positional arguments of sgemm_attention (and of the oracle's
+        attention) with the storages replaced by q, k, v, o."""
+        (ko, ki, kr, kc) = self.K.strides
+        return [self.nb_outer, self.nb_inner, self.tq, self.tk, self.d, self.alpha, int(self.causal),
+                q, *self.Q.strides, k, ko, ki, self.g, kr, kc, v, *self.V.strides, o, *self.O.strides]
+
+
+def _attn_fused(name: str, causal: bool) -> AttnProblem:
+    """The whole attention of one layer, fused: Q [8][512][15][64], K and V
+    [8][512][5][64] token-major N(0,1), three query heads per KV head, alpha
+    1/8, O [8][512][15][64] token-major (zero-filled)."""
+    gq, gk, gv = _gens("attn_fused", 3)
+    no, h, hk, t, d = GQA_SEQS, GQA_Q_HEADS, GQA_KV_HEADS, GQA_TOKENS, GQA_HEAD_DIM
+    nq, sq = layout2(no, h, t, d, "tokens")
+    nk, sk = layout2(no, hk, t, d, "tokens")
+    Q = _f32(gq.normal(0.0, 1.0, nq))
+    K = _f32(gk.normal(0.0, 1.0, nk))
+    V = _f32(gv.normal(0.0, 1.0, nk))
+    O = np.zeros(nq, np.float32)
+    return AttnProblem(name, no, h, t, t, d, h // hk, 1.0 / math.sqrt(d), causal,
+                       Operand2(Q, sq), Operand2(K, sk), Operand2(V, sk), Operand2(O, sq))
+
+
+def attn_fused() -> AttnProblem:
+    """Scores, softmax and P V in one launch over the attn_qk / attn_pv sizes
+    (8 sequences x 15 query heads x 512 tokens, head_dim 64) with 5 KV heads;
+    no mask."""
+    return _attn_fused("attn_fused", False)
+
+
+def attn_fused_causal() -> AttnProblem:
+    """attn_fused with the causal mask of a prefill (query q sees keys <= q);
+    the same draw of Q, K, V."""
+    return _attn_fused("attn_fused_causal", True)
+
+
 BUILDERS = {
     "square64": square64,
     "linear_xWt": linear_xWt,
@@ -454,6 +529,8 @@ BUILDERS = {
     "sqdist": sqdist,
     "attn_qk_gqa": attn_qk_gqa,
     "attn_pv_gqa": attn_pv_gqa,
+    "attn_fused": attn_fused,
+    "attn_fused_causal": attn_fused_causal,
 }
 
 
@@ -551,3 +628,23 @@ def random_problem2(seed: int, nb_outer: int, nb_inner: int, m: int, n: int, k: 
     C = _f32(gc.integers(-3, 4, max(nc, 1))) if dist == "int" else _f32(gc.uniform(-1.0, 1.0, max(nc, 1)))
     return Problem2(name, nb_outer, nb_inner, m, n, k, alpha, accumulate,
                     Operand2(A, sa, gA), Operand2(B, sb, gB), Operand2(C, sc))
+
+
+def random_attention(seed: int, nb_outer: int, nb_inner: int, tq: int, tk: int, d: int, *,
+                     g: int = 1, causal: bool = False, order: str = "tokens", alpha: float = None,
+                     scale: float = 1.0, o_fill: float = 0.0, name: str = "random_attn") -> AttnProblem:
+    """Random attention problem: Q, K, V N(0, scale^2) stored head-major or
+    token-major (layout2), ceil(nb_inner/g) KV heads, O filled with o_fill;
+    alpha defaults to 1/sqrt(d)."""
+    ss = np.random.SeedSequence([ROOT_SEED, 3, seed])
+    gq, gk, gv = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3)]
+    hk = -(-nb_inner // g)
+    nq, sq = layout2(nb_outer, nb_inner, tq, d, order)
+    nk, sk = layout2(nb_outer, hk, tk, d, order)
+    Q = _f32(gq.normal(0.0, scale, max(nq, 1)))
+    K = _f32(gk.normal(0.0, scale, max(nk, 1)))
+    V = _f32(gv.normal(0.0, 1.0, max(nk, 1)))
+    O = np.full(max(nq, 1), o_fill, np.float32)
+    a = 1.0 / math.sqrt(d) if alpha is None else alpha
+    return AttnProblem(name, nb_outer, nb_inner, tq, tk, d, g, a, causal,
+                       Operand2(Q, sq), Operand2(K, sk), Operand2(V, sk), Operand2(O, sq))

@@ -242,3 +242,46 @@ def test_two_level_batch_validates_before_the_device():
     b2(no=0)                                                        # empty: nothing to do
     # Groups larger than the inner count are accepted (every entry maps to the first).
     b2(no=0, gB=1 << 40)
+
+
+def test_attention_validates_and_plans_before_the_device():
+    """Fused attention rejects bad sizes, strides, pointers, aliasing and
+    paths with a status before any device call, and plans the matrix-core
+    kernel only for d = 64 with unit column strides and aligned rows."""
+    def args(no=2, h=6, tq=32, tk=32, d=64, causal=0, g=3, sQ=None, sK=None, sO=None,
+             Q=PA, K=PB, V=PB + (1 << 24), O=PC):
+        sQ = sQ or (tq * h * d, d, h * d, 1)
+        sK = sK or (tk * 2 * d, d, 2 * d, 1)
+        sO = sO or sQ
+        return [no, h, tq, tk, d, 0.125, causal, Q, *sQ, K, sK[0], sK[1], g, sK[2], sK[3],
+                V, *sK, O, *sO]
+
+    def run(**kw):
+        path = kw.pop("path", 0)
+        return sg.sgemm_attention_path(*args(**kw), path=path)
+
+    def plan(**kw):
+        path = kw.pop("path", 0)
+        return sg.sgemm_attention_describe(*args(**kw), path=path)
+
+    assert status_of(lambda: run(h=0)) == -1
+    assert status_of(lambda: run(g=0)) == -1
+    assert status_of(lambda: run(tk=0)) == -1                       # a query with no key
+    assert status_of(lambda: run(tq=40, tk=32, causal=1)) == -1     # causal, first queries see nothing
+    assert status_of(lambda: run(d=300, sQ=(0, 300, 300, 1), sK=(0, 300, 300, 1))) == -5
+    assert status_of(lambda: run(sK=(0, 64, -128, 1))) == -2
+    assert status_of(lambda: run(Q=None)) == -3
+    assert status_of(lambda: run(O=PA + 4 * 64)) == -4              # O inside Q
+    assert status_of(lambda: run(sO=(0, 64, 384, 1))) == -4         # sequences collide in O
+    assert status_of(lambda: run(path=2)) == -7                     # no wavefront family here
+    assert status_of(lambda: run(d=32, sQ=(32 * 192, 32, 192, 1), sK=(32 * 64, 32, 64, 1), path=1)) == -5
+    run(no=0)                                                        # nothing to do
+    run(tq=0, tk=0)
+    assert plan()["kernel"] == "attn_mfma_d64_w8"
+    assert plan(causal=1)["kernel"] == "attn_mfma_d64_w8_causal"
+    assert plan()["workgroups"] == 2 * 6 * 1
+    assert plan(path=3)["kernel"] == "attn_generic"
+    assert plan(d=32, sQ=(32 * 192, 32, 192, 1), sK=(32 * 64, 32, 64, 1))["kernel"] == "attn_generic"
+    assert plan(sQ=(32 * 6 * 66, 66, 6 * 66, 1))["kernel"] == "attn_generic"     # rows 8-byte aligned only
+    assert plan(Q=PA + 8)["kernel"] == "attn_generic"
+    assert plan(sK=(32 * 2 * 128, 128, 256, 2))["kernel"] == "attn_generic"     # column stride 2
