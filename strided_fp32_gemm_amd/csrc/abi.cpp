@@ -402,6 +402,10 @@ int describe(const sgemm::GemmArgs &a, int path, int num_cus, sgemm_plan_info *i
         const sgemm::PersistCfg &t = sgemm::kPersistTiles[plan.tile];
         info->tile_m = t.bm; info->tile_n = t.bn; info->tile_k = t.kmax;
         info->waves = t.waves();
+    } else if (plan.tile >= 0 && plan.strip) {
+        const sgemm::StripCfg &t = sgemm::kStripTiles[plan.tile];
+        info->tile_m = t.rows; info->tile_n = int(std::min<int64_t>(plan.n, INT32_MAX)); info->tile_k = t.kmax;
+        info->waves = t.waves;
     } else if (plan.tile >= 0 && plan.family == sgemm::Family::Wave) {
         const sgemm::WaveCfg &t = sgemm::kWaveTiles[plan.tile];
         info->tile_m = t.bm; info->tile_n = t.bn; info->tile_k = 16;

@@ -168,15 +168,24 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
             f32x4 sacc[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) sacc[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            // K fragments of step group j (head dimensions 16*lh + 4*j + e),
+            // read one group ahead; the four accumulators take turns.
+            f32x4 kf[2][4];
+            auto read_k = [&](int j, f32x4 (&dst)[4]) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    dst[kb] = *reinterpret_cast<const f32x4 *>(Kl + (16 * kb + lq) * kPitch + 16 * lh + 4 * j);
+            };
+            read_k(0, kf[0]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                if (j + 1 < 4) read_k(j + 1, kf[(j + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const f32x4 kf =
-                        *reinterpret_cast<const f32x4 *>(Kl + (16 * kb + lq) * kPitch + 16 * lh + 4 * j);
+                for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sacc[kb] = mfma16(kf[e], qf[j][e], sacc[kb]);
-                }
+                    for (int kb = 0; kb < 4; ++kb) sacc[kb] = mfma16(kf[j & 1][kb][e], qf[j][e], sacc[kb]);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // Last key of this block the lane's query sees, relative to the
             // lane's first key (kv0 + 4*lh); >= 63 when the block is all visible.
@@ -209,15 +218,27 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
             l = l * corr + ls;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) oacc[nb] *= corr;
-            // O^T += V^T P^T over the 64 keys of this block.
+            // O^T += V^T P^T over the 64 keys of this block; the V values of
+            // 16-key group kb are read one group ahead.
+            float vf[2][4][4];   // [buffer][r][nb]: V[kv0 + 16*kb + 4*lh + r][16*nb + lq]
+            auto read_v = [&](int kb, float (&dst)[4][4]) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float *vrow = Vl + (16 * kb + 4 * lh + r) * kPitch + lq;
+                    for (int nb = 0; nb < 4; ++nb)
+                        dst[r][nb] = Vl[(16 * kb + 4 * lh + r) * kPitch + 16 * nb + lq];
+            };
+            read_v(0, vf[0]);
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) oacc[nb] = mfma16(vrow[16 * nb], x[kb][r], oacc[nb]);
-                }
+            for (int kb = 0; kb < 4; ++kb) {
+                if (kb + 1 < 4) read_v(kb + 1, vf[(kb + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) oacc[nb] = mfma16(vf[kb & 1][r][nb], x[kb][r], oacc[nb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if (t + 1 < nblocks) {
             put((t + 1) & 1);
@@ -232,7 +253,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
         const f32x4 v = oacc[nb] / l;
-        store4(rO, qok ? (unsigned(qrow) * sOr + unsigned(16 * nb + 4 * lh)) * 4u : kOutOfRange, v);
+        store4_device(rO, qok ? (unsigned(qrow) * sOr + unsigned(16 * nb + 4 * lh)) * 4u : kOutOfRange, v);
     }
 }
 

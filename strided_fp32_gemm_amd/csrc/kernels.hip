@@ -256,6 +256,8 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         if (p.persist)
             persist_table().f[p.tile][p.a_kfast][p.b_kfast][p.accumulate != 0](
                 a, unsigned(p.workgroups), stream);
+        else if (p.strip)
+            launch_strip(a, p.tile, p.accumulate != 0, unsigned(p.workgroups), stream);
         else if (p.family == Family::Wave)
             wave_table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4](
                 a, unsigned(p.workgroups), stream);

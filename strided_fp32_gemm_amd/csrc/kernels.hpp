@@ -93,6 +93,9 @@ void fill_persist_0(PersistTable &);
 void fill_persist_1(PersistTable &);
 void fill_persist_2(PersistTable &);
 
+// Strip kernel (kStripTiles[tile]); a.map has one tile column per batch entry.
+void launch_strip(const MfmaArgs &a, int tile, bool accumulate, unsigned grid, hipStream_t stream);
+
 // Squared norms of batch x count vectors of length len (see sgemm_sqnorms).
 int launch_sqnorms(long long batch, long long count, long long len, const float *X, long long sX_b,
                    long long sX_i, long long sX_e, float *out, long long sO_b, long long sO_i,

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kPersistTiles[P].wgm * kPersistTiles[P].wgn * 64) v
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = ACC ? __builtin_fmaf(alpha, acc[x][e], beta * old[x][e]) : alpha * acc[x][e];
-        store4(t.rC, offset(t, x / TN, x % TN), o);
+        store4_device(t.rC, offset(t, x / TN, x % TN), o);
     };
 
     static_assert(G >= NB && G >= 3, "one store per k group; the other work needs 3 groups");

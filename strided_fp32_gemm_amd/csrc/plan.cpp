@@ -228,6 +228,31 @@ bool persist_serves(const Plan &p, const PersistCfg &t) {
            !p.col_add;
 }
 
+// The strip kernel needs A and B contiguous along k with 16-byte loads,
+// 16-byte C stores, k <= 64 and no vector terms; offsets within one batch
+// entry are 32-bit (the whole of A's, B's and C's slices from one base).
+bool strip_serves(const Plan &p, const StripCfg &t) {
+    return p.a_kfast && p.b_kfast && p.vec_a == 4 && p.vec_b == 4 && p.c_vec4 && p.k >= 1 &&
+           p.k <= t.kmax && !p.row_add && !p.col_add && fits_buffer(p.m, p.sA_m, p.k, 1) &&
+           fits_buffer(p.n, p.sB_n, p.k, 1) && fits_buffer(p.m, p.sC_m, p.n, 1);
+}
+
+// Strip launch: batch * ceil(m / rows) workgroups, each multiplying its rows
+// by all of B (k padded to 64) and writing its rows of C; a CU holds as many
+// as LDS and its 32 wavefront slots allow.
+double strip_cost(const Plan &p, const StripCfg &t, int num_cus) {
+    const double kFlopPerCuCycle = 256.0, kStoreBytesPerCycle = 11.0, kFill = 3000.0;
+    double wgs = double(p.batch) * double((p.m + t.rows - 1) / t.rows);
+    double cus = double(std::max(num_cus, 1));
+    double slots = std::min(std::floor(160.0 * 1024.0 / StripCfg::lds_bytes()), std::floor(32.0 / t.waves));
+    double occ = std::max(1.0, std::min(slots, std::ceil(wgs / cus)));
+    double rounds = std::ceil(wgs / (cus * occ));
+    double npad = double((p.n + StripCfg::kBlockCols - 1) / StripCfg::kBlockCols) * StripCfg::kBlockCols;
+    double compute = occ * t.rows * npad * 2.0 * t.kmax / kFlopPerCuCycle / t.rate;
+    double epilogue = occ * t.rows * double(p.n) * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
+    return rounds * std::max(compute, epilogue) + kFill;
+}
+
 }  // namespace
 
 int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::string &why) {
@@ -315,17 +340,20 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
             if (std::strcmp(force, kPersistTiles[t].name) == 0 && persist_serves(p, kPersistTiles[t]) &&
                 tile_fits(p, kPersistTiles[t].bm, kPersistTiles[t].bn))
                 force_known = true;
+        for (int t = 0; t < kNumStripTiles; ++t)
+            if (std::strcmp(force, kStripTiles[t].name) == 0 && strip_serves(p, kStripTiles[t]))
+                force_known = true;
         if (!force_known || family != Family::Auto) force = nullptr;
     }
 
     int best = -1;
-    bool best_wave = false, best_persist = false;
+    bool best_wave = false, best_persist = false, best_strip = false;
     double best_cost = 0;
     auto consider = [&](int t, bool wave, bool persist, int bm, int bn, double cost) {
         int64_t wgs = p.batch * ((p.m + bm - 1) / bm) * ((p.n + bn - 1) / bn);
         if (wgs > i32max || !tile_fits(p, bm, bn)) return;
         if (best < 0 || cost < best_cost) {
-            best = t; best_wave = wave; best_persist = persist; best_cost = cost;
+            best = t; best_wave = wave; best_persist = persist; best_strip = false; best_cost = cost;
         }
     };
     if (small_enough && family != Family::Generic) {
@@ -339,13 +367,31 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
                 int64_t tiles = p.batch * ((p.m + c.bm - 1) / c.bm) * ((p.n + c.bn - 1) / c.bn);
                 consider(t, false, true, c.bm, c.bn, persist_cost(p, c, num_cus, persist_grid(p, c, num_cus, tiles)));
             }
+            for (int t = 0; t < kNumStripTiles; ++t) {
+                const StripCfg &c = kStripTiles[t];
+                if (!allowed(c.name) || !strip_serves(p, c)) continue;
+                const int64_t wgs = p.batch * ((p.m + c.rows - 1) / c.rows);
+                const double cost = strip_cost(p, c, num_cus);
+                if (wgs <= i32max && (best < 0 || cost < best_cost)) {
+                    best = t; best_wave = false; best_persist = false; best_strip = true; best_cost = cost;
+                }
+            }
         }
         if (family != Family::Mfma)
             for (int t = 0; t < kNumWaveTiles; ++t)
                 if (allowed(kWaveTiles[t].name))
                     consider(t, true, false, kWaveTiles[t].bm, kWaveTiles[t].bn, wave_cost(p, kWaveTiles[t], num_cus));
     }
-    if (best >= 0) {
+    if (best >= 0 && best_strip) {
+        const StripCfg &c = kStripTiles[best];
+        p.family = Family::Mfma;
+        p.tile = best;
+        p.strip = true;
+        p.tiles_m = (p.m + c.rows - 1) / c.rows;
+        p.tiles_n = 1;
+        p.workgroups = p.batch * p.tiles_m;
+        p.kernel_name = std::string("strip_") + c.name + "_ak_bk" + (p.accumulate ? "_acc" : "");
+    } else if (best >= 0) {
         int bm = best_wave ? kWaveTiles[best].bm : best_persist ? kPersistTiles[best].bm : kTiles[best].bm;
         int bn = best_wave ? kWaveTiles[best].bn : best_persist ? kPersistTiles[best].bn : kTiles[best].bn;
         const char *name = best_wave ? kWaveTiles[best].name

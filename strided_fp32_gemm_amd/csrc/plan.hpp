@@ -128,6 +128,26 @@ inline constexpr PersistCfg kPersistTiles[kNumPersistTiles] = {
     {64, 128, 64, 2, 4, "p64x128k64", 0.59},
 };
 
+// Short-k strip kernel: a workgroup of `waves` wavefronts owns `rows` = 16 *
+// waves * (1 or 2) rows of C across all n columns; each wavefront keeps its rows of A
+// (k <= kmax, k-contiguous) in registers and streams B (k-contiguous) in
+// 64-column blocks through LDS.
+struct StripCfg {
+    int rows, waves, kmax;
+    const char *name;
+    double rate;   // sustained fraction of the matrix-core peak (fitted)
+    static constexpr int kBlockCols = 64;
+    static constexpr int lds_bytes() { return 2 * kBlockCols * (64 + 4) * 4; }
+};
+
+constexpr int kNumStripTiles = 4;
+inline constexpr StripCfg kStripTiles[kNumStripTiles] = {
+    {64, 4, 64, "s64k64", 0.67},
+    {128, 8, 64, "s128k64", 0.71},
+    {128, 4, 64, "s128r2k64", 0.63},   // two 16-row sub-strips per wavefront
+    {64, 2, 64, "s64r2k64", 0.62},
+};
+
 // Division by a launch constant as a multiply and a shift (Granlund and
 // Montgomery, "Division by invariant integers using multiplication", 1994):
 // for 1 <= d < 2^31 take l = ceil(log2 d) and m = ceil(2^(31+l) / d), which
@@ -216,6 +236,7 @@ struct Plan {
     Family family = Family::Generic;
     int tile = -1;             // index into kTiles / kPersistTiles (MFMA) or kWaveTiles (WAVE)
     bool persist = false;      // MFMA family, persistent short-k kernel (tile indexes kPersistTiles)
+    bool strip = false;        // MFMA family, short-k strip kernel (tile indexes kStripTiles)
     bool a_kfast = true, b_kfast = false;
     int vec_a = 1, vec_b = 1;
     bool c_vec4 = false;       // C rows take 16-byte stores

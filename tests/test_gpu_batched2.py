@@ -119,10 +119,11 @@ def test_two_levels_integer_bitwise(path):
         assert np.array_equal(got, ref), (path, no, ni, m, n, k, layout)
 
 
-@pytest.mark.parametrize("tile", ["p64x64k64", "p128x64k64", "p64x128k64"])
+@pytest.mark.parametrize("tile", ["p64x64k64", "p128x64k64", "p64x128k64", "s64k64", "s128k64", "s128r2k64"])
 def test_two_levels_persistent(tile, monkeypatch):
     """Each persistent short-k tile, forced, with the tile list crossing
-    sequences and heads (grid capped so each workgroup visits many tiles)."""
+    sequences and heads (grid capped so each workgroup visits many tiles),
+    and each strip tile on the score layouts it serves."""
     monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
     monkeypatch.setenv("SGEMM_PERSIST_WGS", "13")
     for no, ni, m, n, k, layout, gB in [(3, 6, 200, 136, 64, "qk", 3), (2, 4, 64, 64, 32, "qk", 2),
@@ -131,7 +132,10 @@ def test_two_levels_persistent(tile, monkeypatch):
         for acc in (False, True):
             p = problem(no + ni + m + n + k, no, ni, m, n, k, layout, 1, gB, alpha=-1.25,
                         accumulate=acc)
-            assert describe(p)["kernel"].startswith("persist_" + tile), describe(p)
+            if tile.startswith("s") and not (layout.startswith("qk")):
+                continue   # the strip kernel serves k-contiguous A and B only
+            assert describe(p)["kernel"].startswith(("persist_", "strip_")) and tile in describe(p)["kernel"], \
+                describe(p)
             got, ref = out(p, gpu_call(p)), out(p, oracle_call(p))
             e = err_ratio(p, got, ref)
             assert e <= TOL, (tile, no, ni, m, n, k, layout, acc, e)

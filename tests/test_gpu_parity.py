@@ -226,6 +226,29 @@ def test_persistent_tile(tile, wgs, monkeypatch):
                 assert e <= TOL, (tile, wgs, m, n, k, a_major, b_major, acc, e)
 
 
+@pytest.mark.parametrize("tile", ["s64k64", "s128k64", "s128r2k64", "s64r2k64"])
+def test_strip_tile(tile, monkeypatch):
+    """Each short-k strip tile, forced, on ragged shapes with k in 4..64 and
+    A, B both contiguous along k (the only layout it serves), accumulating
+    and not; its k order is that of the other 16x16 kernels, so it must give
+    the persistent kernel's bits."""
+    shapes = [(3, 300, 260, 64), (5, 132, 68, 40), (2, 64, 64, 4), (9, 128, 192, 60), (1, 4, 8, 12),
+              (2, 77, 1000, 64)]
+    for batch, m, n, k in shapes:
+        for acc in (False, True):
+            p = wl.random_problem(m * 5 + n + k, batch, m, n, k, a_major="row", b_major="col",
+                                  dist="normal", alpha=0.375, accumulate=acc)
+            monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+            info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
+            assert info["kernel"].startswith("strip_" + tile), info
+            got = gpu_call(p)
+            monkeypatch.setenv("SGEMM_FORCE_TILE", "p64x64k64")
+            assert sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))["kernel"].startswith("persist_")
+            assert np.array_equal(got, gpu_call(p)), (tile, batch, m, n, k, acc)
+            e = err_ratio(p, out(p, got), out(p, oracle_call(p)))
+            assert e <= TOL, (tile, m, n, k, acc, e)
+
+
 def test_column_major_output():
     """C stored column-major is served as C^T = B^T A^T."""
     for a_major, b_major in LAYOUTS:
