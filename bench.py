@@ -3,10 +3,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one call of sgemm_strided_batched (validation, planning and the
-kernel launch) over the workload's inputs, which are resident in device
-memory before timing starts.  W untimed steps, then exactly K timed steps
-bracketed by device synchronisation; rank 0 prints one JSON line.
+A step is one call of the workload's entry point (validation, planning and
+the kernel launch) over its inputs, which are resident in device memory
+before timing starts.  W untimed steps, then exactly K timed steps bracketed
+by device synchronisation; rank 0 prints one JSON line.  Without --warmup, W
+is as many steps as fill 0.3 s (at least 5), so that the clock has ramped up
+before a short kernel is timed; the line reports the W used.
 
 Default workload: the large square product, 4 x 4096^3 with A read
 transposed, alpha 0.5 and accumulation into C.  `--workload all` prints one
@@ -38,6 +40,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+WARMUP_SECONDS = 0.3              # default warm-up: the clock ramps up within it
 METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
 DEFAULT_WORKLOAD = "square4096_acc"
 KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/" + f for f in (
@@ -203,25 +206,48 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     step, info, keep = _step_fn(p, dev, stream)
-    for _ in range(warmup):
-        step()
+    if warmup is None:
+        # Warm up for WARMUP_SECONDS of device time (at least 5 steps).
+        warmup = 0
+        t_warm = time.perf_counter()
+        while warmup < 5 or time.perf_counter() - t_warm < WARMUP_SECONDS:
+            for _ in range(5):
+                step()
+            warmup += 5
+            torch.cuda.synchronize(dev)
+    else:
+        for _ in range(warmup):
+            step()
     torch.cuda.synchronize(dev)
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # Timed region: K steps back to back, one pair of HIP events on the launch
+    # stream around all of them (the mean launch duration is their span / K;
+    # an event pair per launch would add its own timestamp work to each).
+    first = torch.cuda.Event(enable_timing=True)
+    last = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    for i in range(steps):
+    first.record(stream)
+    for _ in range(steps):
+        step()
+    last.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    mean_ms = first.elapsed_time(last) / steps
+
+    # Spread of single launches, from an untimed pass with an event pair each.
+    probes = min(steps, 50)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(probes)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(probes)]
+    for i in range(probes):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
     flops = float(p.flops)
     value = flops * steps / wall / 1e12
-    mean_ms = statistics.fmean(launch_ms)
     achieved = flops / (mean_ms * 1e-3) / 1e12
     traffic = traffic_record(name, info["kernel"])
     line = {
@@ -294,7 +320,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before timing (default: as many as fill 0.3 s, at least 5)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the CPU oracle baseline (0 skips it)")
@@ -307,7 +334,7 @@ def main() -> int:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         return 2
-    if args.steps < 1 or args.warmup < 0:
+    if args.steps < 1 or (args.warmup is not None and args.warmup < 0):
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
     import torch
