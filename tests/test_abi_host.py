@@ -171,14 +171,26 @@ def test_tile_map_example_shape_is_planned():
     assert (-(-rows // 4), -(-cols // 4)) == (int(g["tile_rows"]), int(g["tile_columns"]))
 
 
-def test_persistent_tile_serves_short_k_only(monkeypatch):
-    """The persistent short-k kernel takes the attention-score shape (k = 64,
-    16-byte loads and stores) with one workgroup per LDS-resident pair of
-    slabs on each CU, and is never used where it cannot serve: k above its
-    slab depth, element loads, or C rows without 16-byte stores."""
+def test_short_k_kernels_serve_short_k_only(monkeypatch):
+    """The attention-score shape (k = 64, A and B contiguous along k) goes to
+    the strip kernel, 128 rows per workgroup across all 512 columns; with B
+    contiguous along n the persistent kernel takes it (one workgroup per
+    LDS-resident pair of slabs on each CU).  Neither is used where it cannot
+    serve: k above 64, element loads, or C rows without 16-byte stores."""
     qk = _cfg_plan("attn_qk")
-    assert qk["kernel"].startswith("persist_p64x64k64"), qk
-    assert qk["tile_k"] == 64 and qk["workgroups"] == 2 * 256
+    assert qk["kernel"] == "strip_s128k64_ak_bk", qk
+    assert qk["tile_m"] == 128 and qk["tile_k"] == 64 and qk["workgroups"] == 120 * 4
+    bn = plan(120, 512, 512, 64, (512 * 64, 64, 1), (512 * 64, 512, 1), (512 * 512, 512, 1))
+    assert bn["kernel"].startswith("persist_p64x64k64"), bn
+    assert bn["workgroups"] == 2 * 256
+    for tile in ("s64k64", "s128k64"):
+        monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+        assert not plan(120, 512, 512, 64, (512 * 64, 64, 1), (512 * 64, 512, 1),
+                        (512 * 512, 512, 1))["kernel"].startswith("strip_")     # B n-fast
+        assert not plan(120, 512, 512, 68, (512 * 68, 68, 1), (512 * 68, 1, 68),
+                        (512 * 512, 512, 1))["kernel"].startswith("strip_")     # k above 64
+        assert not plan(120, 512, 510, 64, (512 * 64, 64, 1), (510 * 64, 1, 64),
+                        (512 * 510, 510, 1))["kernel"].startswith("strip_")     # C rows not 16-byte
     monkeypatch.setenv("SGEMM_FORCE_TILE", "p64x64k64")
     ok = plan(120, 512, 512, 64, (512 * 64, 64, 1), (512 * 64, 1, 64), (512 * 512, 512, 1))
     assert ok["kernel"].startswith("persist_"), ok
