@@ -319,6 +319,47 @@ def test_canaries_nan_and_gaps(path):
     assert np.array_equal(np.isnan(g), mask)
 
 
+def test_offsets_beyond_32_bits():
+    """Operands whose rows or batch entries lie more than 2 GiB apart.  Rows
+    that far apart exceed a workgroup's 32-bit buffer window, so the planner
+    takes the 64-bit generic kernel; batch entries that far apart only move
+    each workgroup's 64-bit base, so the matrix-core kernel still serves.
+    Both match the oracle run on compact copies of the same logical values."""
+    far = (1 << 29) + 128                      # floats: 2 GiB + 512 bytes
+    rng = np.random.default_rng(77)
+    for (batch, m, n, k, where, family) in ((1, 5, 40, 70, "A rows", "generic"),
+                                            (2, 33, 20, 16, "C batch", "mfma")):
+        A = rng.standard_normal((batch, m, k)).astype(np.float32)
+        B = rng.standard_normal((batch, k, n)).astype(np.float32)
+        if where == "A rows":
+            sa = (0, far, 1)
+            dA = torch.zeros((m - 1) * far + k, device="cuda")
+            dA.as_strided((m, k), (far, 1)).copy_(torch.from_numpy(A[0]))
+            sc = (m * n, n, 1)
+            dC = torch.zeros(batch * m * n, device="cuda")
+        else:
+            sa = (m * k, k, 1)
+            dA = torch.from_numpy(A.ravel()).cuda()
+            sc = (far, n, 1)
+            dC = torch.zeros(far + m * n, device="cuda")
+        dB = torch.from_numpy(B.ravel()).cuda()
+        sb = (k * n, n, 1)
+        args = [batch, m, n, k, 1.5, dA, *sa, dB, *sb, 0, dC, *sc]
+        info = sg.sgemm_plan_describe(*[a.data_ptr() if isinstance(a, torch.Tensor) else a for a in args])
+        assert info["kernel"].startswith(family), info
+        sg.sgemm_strided_batched(*args, stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        got = dC.as_strided((batch, m, n), sc).cpu().numpy()
+        ref = np.zeros(batch * m * n, np.float32)
+        oracle.ref_sgemm(batch, m, n, k, 1.5, A.ravel(), m * k, k, 1, B.ravel(), k * n, n, 1, 0,
+                         ref, m * n, n, 1)
+        scale = k * np.abs(A).max() * np.abs(B).max()
+        e = np.abs(got.astype(np.float64) - ref.reshape(batch, m, n)).max() / scale
+        assert e <= TOL, (where, e)
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+
+
 def test_determinism_repeated_calls():
     p = wl.random_problem(47, 4, 300, 260, 500, a_major="col", b_major="col", dist="normal")
     first = gpu_call(p)
