@@ -24,8 +24,9 @@
 //    of bank conflicts); the next block's global loads are in flight while
 //    the current one is multiplied; one barrier per block.
 //  - Weights are exp2(s * alpha*log2(e) - running max), with v_exp_f32.  The
-//    row maximum needs two cross-lane steps per key block; the row sum stays
-//    per lane until the end.
+//    row maximum needs two lane swaps per key block (v_permlane16_swap,
+//    v_permlane32_swap: vector instructions, no LDS round trip); the row sum
+//    stays per lane until the end.
 //  - Causal: a workgroup pairs an early and a late block of query rows (one
 //    per half of its wavefronts) so that workgroups carry equal work; it
 //    stops at the last key its queries see, and a wavefront skips the blocks
@@ -60,6 +61,26 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine the four lanes l%16 + 16*h (h = 0..3) of a wavefront with `op`,
+// leaving the result in all four: lanes swap 16-lane rows (v_permlane16_swap:
+// row 0 with 1, 2 with 3), then 32-lane halves (v_permlane32_swap), both plain
+// vector instructions.  A self-swap returns this lane's value and its
+// partner's in some order, so op(r[0], r[1]) is the pair's result in both
+// lanes; the association is (row 0 op row 1) op (row 2 op row 3).
+// (The two results are copied to scalars before the bit casts: a bit cast of
+// a subscripted vector element reads the vector's first element.)
+template <typename Op>
+__device__ __forceinline__ float across_rows(float v, Op op) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned a0 = r16[0], a1 = r16[1];
+    v = op(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+    const unsigned w = __builtin_bit_cast(unsigned, v);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    const unsigned b0 = r32[0], b1 = r32[1];
+    return op(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
@@ -202,8 +223,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
                     x[kb][r] = 16 * kb + r <= lim ? v : -INFINITY;
                     mt = fmaxf(mt, x[kb][r]);
                 }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = across_rows(mt, [](float x, float y) { return fmaxf(x, y); });
             const float mnew = fmaxf(m, mt);
             const float corr = exp2_fast(m - mnew);
             m = mnew;
@@ -248,8 +268,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
     }
 
     // The four lanes of a query hold disjoint key subsets of its sum.
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = across_rows(l, [](float x, float y) { return x + y; });
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
         const f32x4 v = oacc[nb] / l;
