@@ -36,6 +36,16 @@
  * results.  No atomics are used.  alpha scales the fresh product only; with
  * accumulate != 0 the stored C is added once per element.  With
  * accumulate == 0 the stored C is never read.
+ *
+ * Entry points:
+ *   sgemm_strided_batched[_path]       the product (optionally + C)
+ *   sgemm_strided_batched_ex[_path]    + beta*C + per-row and per-column terms
+ *   sgemm_strided_batched2[_path]      two batch levels, grouped inputs (KV heads)
+ *   sgemm_sqnorms, sgemm_pairwise_sqdist   squared norms, squared distances
+ *   sgemm_attention[_path]             softmax(alpha Q K^T) V, fused, over two batch levels
+ *   sgemm_plan_describe[2], sgemm_attention_describe   the launch a call would make
+ *   sgemm_status_string, sgemm_last_error   status text
+ * The _path variants force a kernel family (tests, sweeps).
  */
 #ifndef SGEMM_STRIDED_H
 #define SGEMM_STRIDED_H

@@ -5,9 +5,12 @@
 over a batch, with every operand given by a pointer and (batch, row, col)
 element strides; a transposed operand is the same memory with its row and
 column strides exchanged (StaleyNET "GPU Implementation", section "The
-matrix product").  The computation runs in hand-written HIP kernels behind a
-C ABI (include/sgemm_strided.h); this package only marshals arguments.
-PyTorch is used for device memory and streams.
+matrix product").  Around it: a general epilogue (beta, per-row and
+per-column terms), squared norms and distances, two batch levels with
+grouped inputs, and fused attention softmax(alpha Q K^T) V.  The computation
+runs in hand-written HIP kernels behind a C ABI (include/sgemm_strided.h);
+this package only marshals arguments.  PyTorch is used for device memory and
+streams.
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
