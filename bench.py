@@ -21,7 +21,8 @@ The JSON line carries:
              launch stream, against the MI355X dense fp32 matrix peak
              (157.3 TFLOP/s); `traffic` is the HBM bytes per launch measured
              by rocprofv3 counters, when a committed record for the current
-             kernel sources exists, else null
+             kernel sources exists, else null; `achieved_tb_per_s` is the
+             algorithmic bytes per launch over the same mean duration
   cpu_baseline  the CPU oracle timed on a bounded slice of the same workload
              (a block of rows of batch 0), as TFLOP/s, with its thread count.
 """
@@ -76,6 +77,18 @@ def traffic_record(workload: str, kernel: str):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_attention(p, seconds: float) -> dict:
     """The oracle's attention on the first H (sequence, head) pairs of the
     same call (whole heads, every query row), H chosen so the run takes
@@ -101,7 +114,7 @@ def cpu_baseline_attention(p, seconds: float) -> dict:
     flops = 4.0 * p.d * p.visible_pairs * heads
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"all {p.tq} query rows of the first {heads} (sequence, head) pairs "
-                      f"({flops / 1e9:.2f} GFLOP in {t:.1f} s)"}
+                      f"({flops / 1e9:.2f} GFLOP in {t:.1f} s)", "cpu_model": cpu_model()}
 
 
 def cpu_baseline(p, seconds: float) -> dict:
@@ -152,7 +165,7 @@ def cpu_baseline(p, seconds: float) -> dict:
     flops = 2.0 * rows * p.n * p.k
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of batch 0 ({rows}x{p.n}x{p.k}, "
-                      f"{flops / 1e9:.1f} GFLOP in {t:.1f} s)"}
+                      f"{flops / 1e9:.1f} GFLOP in {t:.1f} s)", "cpu_model": cpu_model()}
 
 
 def _step_fn(p, dev, stream):
@@ -250,6 +263,7 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
     value = flops * steps / wall / 1e12
     achieved = flops / (mean_ms * 1e-3) / 1e12
     traffic = traffic_record(name, info["kernel"])
+    alg_bytes = wl.algorithmic_bytes(p)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -272,6 +286,8 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
             "traffic": traffic,
+            "algorithmic_bytes": alg_bytes,
+            "achieved_tb_per_s": round(alg_bytes / (mean_ms * 1e-3) / 1e12, 3),
             "kernel": info["kernel"],
             "launch_ms_mean": round(mean_ms, 5),
             "launch_ms_median": round(statistics.median(launch_ms), 5),

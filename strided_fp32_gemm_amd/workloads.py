@@ -538,6 +538,32 @@ def workload(name: str):
     return BUILDERS[name]()
 
 
+def algorithmic_bytes(p) -> int:
+    """Bytes one call must move at least: every input element read once and
+    every output element written once (plus C read when it is accumulated).
+    A batch-stride-0 operand counts once."""
+    if isinstance(p, AttnProblem):
+        kv = -(-p.nb_inner // p.g)
+        return 4 * p.nb_outer * (2 * p.nb_inner * p.tq * p.d + 2 * kv * p.tk * p.d)
+    if isinstance(p, DistProblem):
+        ny = 1 if p.Y.strides[0] == 0 else p.batch
+        return 4 * (p.batch * p.m * p.k + ny * p.n * p.k + p.batch * p.m * p.n)
+    if isinstance(p, Problem2):
+        na, nb = -(-p.nb_inner // p.A.group), -(-p.nb_inner // p.B.group)
+        a = p.nb_outer * na * p.m * p.k
+        b = p.nb_outer * nb * p.k * p.n
+        return 4 * (a + b + p.batch * p.m * p.n * (2 if p.accumulate else 1))
+    a = (1 if p.A.strides[0] == 0 else p.batch) * p.m * p.k
+    b = (1 if p.B.strides[0] == 0 else p.batch) * p.k * p.n
+    c = p.batch * p.m * p.n * (2 if p.beta_value != 0 else 1)
+    vec = 0
+    if p.row is not None:
+        vec += (1 if p.row.strides[0] == 0 else p.batch) * p.m
+    if p.col is not None:
+        vec += (1 if p.col.strides[0] == 0 else p.batch) * p.n
+    return 4 * (a + b + c + vec)
+
+
 # ---------------------------------------------------------------------------
 # Parametric problems for parity tests.
 # ---------------------------------------------------------------------------
