@@ -149,8 +149,8 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
 
     // LDS tiles: A as [BM][BK+pad] (k fast) or [BK][BM+pad] (m fast);
     //            B as [BN][BK+pad] (k fast) or [BK][BN+pad] (n fast).
-    constexpr int A_R = AK ? BM : BK, A_F = AK ? BK : BM, A_PAD = cfg.pad(AK);
-    constexpr int B_R = BKF ? BN : BK, B_F = BKF ? BK : BN, B_PAD = cfg.pad(BKF);
+    constexpr int A_R = AK ? BM : BK, A_F = AK ? BK : BM, A_PAD = cfg.pad(AK, cfg.a_blocks());
+    constexpr int B_R = BKF ? BN : BK, B_F = BKF ? BK : BN, B_PAD = cfg.pad(BKF, cfg.b_blocks());
     constexpr int A_LD = A_F + A_PAD, B_LD = B_F + B_PAD;
     constexpr int A_SIZE = A_R * A_LD, B_SIZE = B_R * B_LD;
     static_assert(4 * (A_SIZE + B_SIZE) == cfg.buffer_lds_bytes(AK, BKF), "LDS carve-up");

@@ -46,16 +46,33 @@ struct TileCfg {
     // is full (fitted to tile sweeps on MI355X).
     double rate;
     constexpr int waves() const { return wgm * wgn; }
-    // Padding of an LDS tile row: 4 floats on a k-fast tile; on an m- or
-    // n-fast tile 8 (32-wide blocks) or 4 (16-wide blocks), which spreads the
-    // lane groups that read different k rows over distinct banks.
-    constexpr int pad(bool kfast) const { return kfast ? 4 : (mf == 32 ? 8 : 4); }
+    // Padding (floats) of an LDS tile row, chosen so that the fragment reads
+    // and the staging writes meet no bank conflict.  gfx950's LDS has 64
+    // banks of 4 bytes; a 16-byte read serves the lanes in four groups of
+    // 16, {0-3, 12-15, 20-23, 24-27}, {4-11, 16-19, 28-31} and the same two
+    // shifted by 32; 8- and 4-byte reads serve 32 consecutive lanes, 16-byte
+    // writes 8 (measured per lane pair with the bank-conflict counter).
+    // `blocks` is the operand's count of MF-wide blocks per wavefront.
+    //  * 32-wide blocks: 4 on a k-fast tile, 8 on an m- or n-fast one (lane
+    //    halves 4 rows apart land 32 banks apart).
+    //  * 16-wide blocks, k-fast: 8, so the 16 rows a read group touches
+    //    start on distinct 4-bank quads.
+    //  * 16-wide blocks, m- or n-fast, read 4 (2) blocks per 16-byte (8-byte)
+    //    load: 0 (8), so the lane quarters 4 rows apart stay on the same
+    //    (opposite) half of the banks; single-float reads: 4.
+    constexpr int pad(bool kfast, int blocks) const {
+        if (mf == 32) return kfast ? 4 : 8;
+        if (kfast) return 8;
+        return blocks == 4 ? 0 : blocks == 2 ? 8 : 4;
+    }
+    constexpr int a_blocks() const { return bm / wgm / mf; }
+    constexpr int b_blocks() const { return bn / wgn / mf; }
     // LDS bytes of one buffer of the A and B tiles, each stored
     // [slow][fast + pad]; the main loop double-buffers them unless the whole
     // k extent fits one slice.
     constexpr int buffer_lds_bytes(bool a_kfast, bool b_kfast) const {
-        return 4 * ((a_kfast ? bm * (bk + pad(true)) : bk * (bm + pad(false))) +
-                    (b_kfast ? bn * (bk + pad(true)) : bk * (bn + pad(false))));
+        return 4 * ((a_kfast ? bm * (bk + pad(true, a_blocks())) : bk * (bm + pad(false, a_blocks()))) +
+                    (b_kfast ? bn * (bk + pad(true, b_blocks())) : bk * (bn + pad(false, b_blocks()))));
     }
     // LDS bytes of the staged epilogue: every wavefront's (bm/wgm) x (bn/wgn)
     // sub-tile of C, rows padded by 4 floats.
