@@ -134,8 +134,15 @@ struct Mfma<16> {
     static __device__ __forceinline__ int row(int r, int lh) { return 4 * lh + r; }
 };
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedLdsRead = 0x100, kSchedLdsWrite = 0x200;
+
+// The 16-byte-load layouts are held to two wavefronts per SIMD (at most 256
+// registers per lane), the occupancy at which two workgroups share a CU; the
+// register file otherwise tips some of them to one.
 template <int T, bool AK, bool BKF, bool AV4, bool BV4>
-__global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma(MfmaArgs p) {
+__global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64)
+__attribute__((amdgpu_waves_per_eu(AV4 && BV4 ? 2 : 1))) void sgemm_mfma(MfmaArgs p) {
     constexpr TileCfg cfg = kTiles[T];
     constexpr int BM = cfg.bm, BN = cfg.bn, BK = cfg.bk, MF = cfg.mf;
     constexpr int NT = cfg.wgm * cfg.wgn * 64;
@@ -275,75 +282,108 @@ __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64) void sgemm_mfma
 #pragma unroll
         for (int c = 0; c < TN; ++c) acc[a][c] = acc_t{};
 
-    // One k slice from LDS buffer `buf`: fragments of group g+1 are read
-    // while the matrix-core instructions of group g run, and hook(g) slots
-    // other work of the step in after group g's products.
-    auto multiply = [&](int buf, auto &&hook) {
-        const float *As = smem + buf * (A_SIZE + B_SIZE);
-        const float *Bs = As + A_SIZE;
-        f32x4 af[2][TM], bf[2][TN];
-        read_frags(As, Bs, 0, af[0], bf[0]);
+    // Fragments of two k groups: the products of group g run from one set
+    // while the next group's fragments land in the other.
+    f32x4 af[2][TM], bf[2][TN];
+    auto products = [&](int set) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (g + 1 < G) read_frags(As, Bs, g + 1, af[(g + 1) & 1], bf[(g + 1) & 1]);
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int a = 0; a < TM; ++a)
 #pragma unroll
-                for (int a = 0; a < TM; ++a)
-#pragma unroll
-                    for (int c = 0; c < TN; ++c)
-                        acc[a][c] = M::op(af[g & 1][a][q], bf[g & 1][c][q], acc[a][c]);
-            hook(g);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+                for (int c = 0; c < TN; ++c) acc[a][c] = M::op(af[set][a][q], bf[set][c][q], acc[a][c]);
     };
+    static_assert(G >= 2 && G % 2 == 0, "a slice holds an even number (>= 2) of k groups");
+    // Per k group: LDS reads of one group's fragments, products, and (once
+    // per slice) the slice's global loads and LDS writes.
+    constexpr int kFragReads = (A_IL ? 4 : AK ? TM : 4 * TM) + (B_IL ? 4 : BKF ? TN : 4 * TN);
+    constexpr int kProducts = 4 * TM * TN;
+    constexpr int kProductsPerRead = kProducts / (2 * kFragReads) > 0 ? kProducts / (2 * kFragReads) : 1;
+    constexpr int kGlobalLoads = LoaderA::kSlots * (AV4 ? 1 : 4) + LoaderB::kSlots * (BV4 ? 1 : 4);
+    constexpr int kLdsWrites = LoaderA::kSlots + LoaderB::kSlots;
 
     const int KT = (p.k + BK - 1) / BK;
     if (KT > 0) {
-        LoaderA la0;
-        LoaderB lb0;
-        {
-            // Two register sets: while slice kt is multiplied, slice kt+1 is
-            // landing in one set and slice kt+2 is being requested into the
-            // other, so two slices of loads are in flight per workgroup.  The
-            // loop runs pairs of steps so the sets alternate statically, and
-            // nothing in its body is conditional: a step only conditional on
-            // the slice count would give the accumulators two incoming paths
-            // at the loop's end, and the compiler reconciles those with
-            // register copies on every iteration.  Requests past the end of k
-            // read zeros, and moving them to the idle buffer is harmless (the
-            // loop only runs when k has at least two slices, so both buffers
-            // exist).  An odd last slice, already in buffer 0, is multiplied
-            // after the loop; with a single slice that is the only step and
-            // buffer 1 is never touched.
-            LoaderA la1;
-            LoaderB lb1;
-            issue(la0, lb0, 0u);
-            issue(la1, lb1, unsigned(BK));
-            put(la0, lb0, 0);
-            __syncthreads();
-            // A step requests slice kt+2 after the first k group's products
-            // and moves slice kt+1 (requested a step ago) into the other
-            // buffer after the last group's: that buffer was last read for
-            // slice kt-1, before the previous barrier.
-            auto step = [&](int kt, int buf, LoaderA &la_next, LoaderB &lb_next, LoaderA &la_free,
-                            LoaderB &lb_free) {
-                multiply(buf, [&](int g) {
+        LoaderA la0, la1;
+        LoaderB lb0, lb1;
+        // Two register sets: while slice kt is multiplied, slice kt+1 is
+        // landing in one set and slice kt+2 is being requested into the
+        // other, so two slices of loads are in flight per workgroup.  The
+        // loop runs pairs of steps so the sets alternate statically, and
+        // nothing in its body is conditional: a step only conditional on the
+        // slice count would give the accumulators two incoming paths at the
+        // loop's end, and the compiler reconciles those with register copies
+        // on every iteration.  Requests past the end of k read zeros, and
+        // moving them to the idle buffer is harmless (the loop only runs when
+        // k has at least two slices, so both buffers exist).  An odd last
+        // slice, already in buffer 0, is multiplied after the loop; with a
+        // single slice that is the only step and buffer 1 is never touched.
+        issue(la0, lb0, 0u);
+        issue(la1, lb1, unsigned(BK));
+        put(la0, lb0, 0);
+        __syncthreads();
+        read_frags(smem, smem + A_SIZE, 0, af[0], bf[0]);
+        // Slice kt from LDS buffer `buf`.  After group 0's products the
+        // requests for slice kt+2 go out; after group G-2's, slice kt+1
+        // (requested a step ago) is written into the other buffer and the
+        // slice's one barrier follows.  That buffer was last read for slice
+        // kt-1 before the previous barrier, which also waited for this
+        // wavefront's reads.  Each group reads the next group's fragments
+        // while its products run; the last group reads group 0 of slice kt+1
+        // from the other buffer, made visible by the barrier, so the next
+        // step starts on fragments already in registers.
+        auto step = [&](int kt, int buf, bool last, LoaderA &la_next, LoaderB &lb_next, LoaderA &la_free,
+                        LoaderB &lb_free) __attribute__((always_inline)) {
+            const float *As = smem + buf * (A_SIZE + B_SIZE);
+            const float *An = smem + (buf ^ 1) * (A_SIZE + B_SIZE);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (g + 1 < G) read_frags(As, As + A_SIZE, g + 1, af[(g + 1) & 1], bf[(g + 1) & 1]);
+                else if (!last) read_frags(An, An + A_SIZE, 0, af[0], bf[0]);
+                products(g & 1);
+                if (!last) {
                     if (g == 0) issue(la_free, lb_free, unsigned(kt + 2) * BK);
-                    if (g == G - 1) put(la_next, lb_next, buf ^ 1);
-                });
-                __syncthreads();
-            };
-            int kt = 0;
-            for (; kt + 1 < KT; kt += 2) {
-                step(kt, 0, la1, lb1, la0, lb0);
-                step(kt + 1, 1, la0, lb0, la1, lb1);
+                    if (g == G - 2) put(la_next, lb_next, buf ^ 1);
+                }
+                // Instruction order of the group (scheduling-group barriers):
+                // one fragment read per P products over the first half, then
+                // each global load and each LDS write after one product.  Left
+                // to itself the compiler issues the reads late in the group
+                // and in bursts that fill the LDS queue, where a wavefront
+                // stalls with products still to issue.
+                if (g + 1 < G || !last) {
+#pragma unroll
+                    for (int i = 0; i < kFragReads; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedLdsRead, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kProductsPerRead, 0);
+                    }
+                }
+                if (!last && g == 0) {
+#pragma unroll
+                    for (int i = 0; i < kGlobalLoads; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    }
+                }
+                if (!last && g == G - 2) {
+#pragma unroll
+                    for (int i = 0; i < kLdsWrites; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedLdsWrite, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    }
+                }
+                if (!last && g == G - 2) __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (kt < KT) {
-                multiply(0, [](int) {});
-                __syncthreads();
-            }
+        };
+        int kt = 0;
+        for (; kt + 1 < KT; kt += 2) {
+            step(kt, 0, false, la1, lb1, la0, lb0);
+            step(kt + 1, 1, false, la0, lb0, la1, lb1);
         }
+        if (kt < KT) step(kt, 0, true, la1, lb1, la0, lb0);
+        // The staged epilogue reuses the main loop's buffers.
+        __syncthreads();
     }
 
     // Epilogue (epilogue_value): C = alpha*acc, or one fused multiply-add
