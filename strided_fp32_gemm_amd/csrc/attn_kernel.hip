@@ -20,9 +20,11 @@
 //    LDS reads.  The key sum of P V follows the score layout.  Both orders are
 //    fixed, so results are reproducible bit for bit.
 //  - Keys arrive in blocks of 64, K and V staged through double-buffered LDS
-//    (row pitch 68 floats: the 16-byte K reads and the 4-byte V reads are free
-//    of bank conflicts); the next block's global loads are in flight while
-//    the current one is multiplied; one barrier per block.
+//    (row pitch 68 floats: the 4-byte V reads are free of bank conflicts; the
+//    16-byte K reads take two cycles per 16-lane group instead of one, which
+//    no row pitch avoids with this head-dimension order, but LDS time stays a
+//    small fraction of the matrix-core time); the next block's global loads
+//    are in flight while the current one is multiplied; one barrier per block.
 //  - Weights are exp2(s * alpha*log2(e) - running max), with v_exp_f32.  The
 //    row maximum needs two lane swaps per key block (v_permlane16_swap,
 //    v_permlane32_swap: vector instructions, no LDS round trip); the row sum

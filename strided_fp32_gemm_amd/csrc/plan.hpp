@@ -154,7 +154,7 @@ struct StripCfg {
     const char *name;
     double rate;   // sustained fraction of the matrix-core peak (fitted)
     static constexpr int kBlockCols = 64;
-    static constexpr int lds_bytes() { return 2 * kBlockCols * (64 + 4) * 4; }
+    static constexpr int lds_bytes() { return 2 * kBlockCols * (64 + 8) * 4; }
 };
 
 constexpr int kNumStripTiles = 4;

@@ -27,8 +27,9 @@ namespace {
 
 constexpr int kSK = 64;                    // k held per row
 constexpr int kSN = StripCfg::kBlockCols;  // columns per LDS block
-constexpr int kSPitch = kSK + 4;           // LDS row pitch (floats): conflict-free 16-byte reads
+constexpr int kSPitch = kSK + 8;           // LDS row pitch (floats): conflict-free 16-byte reads
 constexpr int kSBlock = kSN * kSPitch;
+static_assert(2 * kSBlock * 4 == StripCfg::lds_bytes(), "two B blocks fill the planned LDS");
 
 template <int NW, int RW, bool ACC>
 __global__ __launch_bounds__(NW * 64) void sgemm_strip(MfmaArgs p) {
