@@ -45,8 +45,9 @@ WARMUP_SECONDS = 0.3              # default warm-up: the clock ramps up within i
 METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
 DEFAULT_WORKLOAD = "square4096_acc"
 KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/" + f for f in (
-    "mfma_kernel.hpp", "persist_kernel.hpp", "wave_kernel.hpp", "kernels.hpp", "kernels.hip",
-    "plan.hpp", "plan.cpp", "buffer.hpp", "attn_kernel.hip", "attention.hpp", "attention.cpp")]
+    "mfma_kernel.hpp", "persist_kernel.hpp", "wave_kernel.hpp", "strip_kernel.hip", "kernels.hpp",
+    "kernels.hip", "plan.hpp", "plan.cpp", "buffer.hpp", "extent.hpp", "attn_kernel.hip", "attention.hpp",
+    "attention.cpp")]
 
 
 def kernel_sources_sha256() -> str:
