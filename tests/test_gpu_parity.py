@@ -188,8 +188,9 @@ def test_every_tile(tile, monkeypatch):
     shapes in all four transpose cases, with 16-byte loads (aligned shape)
     and element loads (padded lines), accumulating and not."""
     monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+    # k slices of 32: 3, 3, 2, 7, 2, 1 (the main loop never runs), 4 and 5.
     shapes = [(2, 300, 260, 96, 0), (2, 150, 190, 70, 3), (1, 33, 520, 40, 1), (3, 70, 100, 200, 0),
-              (2, 64, 96, 64, 0)]
+              (2, 64, 96, 64, 0), (2, 100, 90, 20, 0), (1, 70, 80, 128, 0), (1, 130, 140, 160, 2)]
     for batch, m, n, k, pad in shapes:
         for a_major, b_major in LAYOUTS:
             for acc in (False, True):
