@@ -46,9 +46,9 @@ __global__ __launch_bounds__(kPersistTiles[P].wgm * kPersistTiles[P].wgn * 64) v
     constexpr int G = KM / 16;
     static_assert(WM % 16 == 0 && WN % 16 == 0 && KM % 16 == 0, "tile shape");
 
-    // LDS slab: A as [BM][KM+4] (k fast) or [KM][BM+4]; B likewise.  Two slabs.
-    constexpr int A_R = AK ? BM : KM, A_F = AK ? KM : BM, A_PAD = 4;
-    constexpr int B_R = BKF ? BN : KM, B_F = BKF ? KM : BN, B_PAD = 4;
+    // LDS slab: A as [BM][KM+pad] (k fast) or [KM][BM+pad]; B likewise.  Two slabs.
+    constexpr int A_R = AK ? BM : KM, A_F = AK ? KM : BM, A_PAD = PersistCfg::pad(AK);
+    constexpr int B_R = BKF ? BN : KM, B_F = BKF ? KM : BN, B_PAD = PersistCfg::pad(BKF);
     constexpr int A_LD = A_F + A_PAD, B_LD = B_F + B_PAD;
     constexpr int A_SIZE = A_R * A_LD, B_SIZE = B_R * B_LD;
     static_assert(4 * (A_SIZE + B_SIZE) == cfg.slab_bytes(AK, BKF), "LDS carve-up");

@@ -131,10 +131,15 @@ struct PersistCfg {
     const char *name;
     double rate;   // sustained fraction of the matrix-core peak (fitted)
     constexpr int waves() const { return wgm * wgn; }
-    // LDS bytes of one slab: A and B stored [slow][fast + 4].
+    // Row padding (floats) of a slab: 8 on a k-fast operand (its 16-byte
+    // fragment reads of 16 rows then start on distinct bank quads within
+    // each of gfx950's 16-lane read groups), 4 on an m- or n-fast one (its
+    // single-float reads, 32 lanes at a time, land on distinct banks).
+    static constexpr int pad(bool kfast) { return kfast ? 8 : 4; }
+    // LDS bytes of one slab: A and B stored [slow][fast + pad].
     constexpr int slab_bytes(bool a_kfast, bool b_kfast) const {
-        return 4 * ((a_kfast ? bm * (kmax + 4) : kmax * (bm + 4)) +
-                    (b_kfast ? bn * (kmax + 4) : kmax * (bn + 4)));
+        return 4 * ((a_kfast ? bm * (kmax + pad(true)) : kmax * (bm + pad(false))) +
+                    (b_kfast ? bn * (kmax + pad(true)) : kmax * (bn + pad(false))));
     }
 };
 
