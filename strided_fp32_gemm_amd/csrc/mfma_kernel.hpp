@@ -298,9 +298,13 @@ __attribute__((amdgpu_waves_per_eu(AV4 && BV4 ? 2 : 1))) void sgemm_mfma(MfmaArg
     // per slice) the slice's global loads and LDS writes.
     constexpr int kFragReads = (A_IL ? 4 : AK ? TM : 4 * TM) + (B_IL ? 4 : BKF ? TN : 4 * TN);
     constexpr int kProducts = 4 * TM * TN;
-    constexpr int kProductsPerRead = kProducts / (2 * kFragReads) > 0 ? kProducts / (2 * kFragReads) : 1;
     constexpr int kGlobalLoads = LoaderA::kSlots * (AV4 ? 1 : 4) + LoaderB::kSlots * (BV4 ? 1 : 4);
     constexpr int kLdsWrites = LoaderA::kSlots + LoaderB::kSlots;
+    // Spacing in products: the fragment reads spread over the first 3/8 of
+    // the group's products, the LDS writes over half of them (measured
+    // against denser spacings on the 4 x 4096^3 product: 1.5% faster).
+    constexpr int kProductsPerRead = 3 * kProducts / (8 * kFragReads) > 0 ? 3 * kProducts / (8 * kFragReads) : 1;
+    constexpr int kProductsPerWrite = kProducts / (2 * kLdsWrites) > 0 ? kProducts / (2 * kLdsWrites) : 1;
 
     const int KT = (p.k + BK - 1) / BK;
     if (KT > 0) {
@@ -346,8 +350,9 @@ __attribute__((amdgpu_waves_per_eu(AV4 && BV4 ? 2 : 1))) void sgemm_mfma(MfmaArg
                     if (g == G - 2) put(la_next, lb_next, buf ^ 1);
                 }
                 // Instruction order of the group (scheduling-group barriers):
-                // one fragment read per P products over the first half, then
-                // each global load and each LDS write after one product.  Left
+                // the fragment reads spaced over the first products, then each
+                // global load after one product, then the LDS writes spaced
+                // over the following products.  Left
                 // to itself the compiler issues the reads late in the group
                 // and in bursts that fill the LDS queue, where a wavefront
                 // stalls with products still to issue.
@@ -369,7 +374,7 @@ __attribute__((amdgpu_waves_per_eu(AV4 && BV4 ? 2 : 1))) void sgemm_mfma(MfmaArg
 #pragma unroll
                     for (int i = 0; i < kLdsWrites; ++i) {
                         __builtin_amdgcn_sched_group_barrier(kSchedLdsWrite, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kProductsPerWrite, 0);
                     }
                 }
                 if (!last && g == G - 2) __syncthreads();
