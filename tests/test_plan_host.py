@@ -1,7 +1,9 @@
 """Host-side arithmetic of the planner, compiled with g++ (no GPU): the
 multiply-shift division by launch constants and the tile order built on it
 (every tile id maps to one in-range tile, exactly once, in the documented
-order)."""
+order), the two-level batch split, and the LDS row pads (every kernel's
+fragment reads and staging writes free of bank conflicts under gfx950's
+lane groups)."""
 import os
 import shutil
 import subprocess
@@ -13,7 +15,7 @@ CSRC = os.path.join(os.path.dirname(HERE), "strided_fp32_gemm_amd", "csrc")
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
-def test_tile_order_arithmetic(tmp_path):
+def test_planner_host_arithmetic(tmp_path):
     exe = tmp_path / "plan_check"
     subprocess.run(["g++", "-O2", "-std=c++17", "-Wall", "-I", CSRC,
                     os.path.join(HERE, "plan_check.cpp"), "-o", str(exe)], check=True)
