@@ -24,9 +24,12 @@
 //    16-byte aligned, extent a multiple of 4) or element loads (any stride,
 //    any alignment).  Straight-line load code lets the compiler keep every
 //    load of the next k slice in flight while the matrix cores work.
-//  - LDS is double buffered (one barrier per k step) and the fragments of
-//    the next 8-deep k group are read from LDS while the current group's
-//    matrix-core instructions run.
+//  - LDS is double buffered (one barrier per k step, placed before the
+//    step's last k group) and the fragments of the next k group are read
+//    from LDS while the current group's matrix-core instructions run; the
+//    last group reads the first fragments of the next slice, so no step
+//    starts by waiting on LDS.  Scheduling-group barriers space the LDS
+//    reads, global loads and LDS writes among the products.
 //  - Loads and stores go through buffer resources.  A lane outside the
 //    matrix gets an offset beyond the resource's range, so the hardware
 //    returns zero for its load and drops its store: no branch and no access
