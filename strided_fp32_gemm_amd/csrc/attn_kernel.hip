@@ -46,6 +46,7 @@
 
 #include "attention.hpp"
 #include "buffer.hpp"
+#include "kernels.hpp"
 
 namespace sgemm {
 
@@ -333,9 +334,8 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs p) {
 
 template <int NW>
 void launch_mfma_attention(const AttnArgs &a, unsigned grid, hipStream_t s) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_mfma_d64<NW>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    (void)attr;
+    static std::atomic<unsigned long long> lds_set{0};
+    allow_dynamic_lds(reinterpret_cast<const void *>(&attn_mfma_d64<NW>), kLdsBytes, lds_set);
     hipLaunchKernelGGL(attn_mfma_d64<NW>, dim3(grid), dim3(NW * 64), kLdsBytes, s, a);
 }
 

@@ -3,11 +3,25 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <string>
 
 #include "plan.hpp"
 
 namespace sgemm {
+
+// Raises kernel `fn`'s dynamic LDS limit to `bytes` on the current device,
+// once per device: `done` holds one bit per device id below 64 (a larger id
+// sets the attribute on every launch).  A failure leaves the bit clear; the
+// launch then fails and reports through hipGetLastError.
+inline void allow_dynamic_lds(const void *fn, int bytes, std::atomic<unsigned long long> &done) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_acq_rel);
+}
 
 // The general epilogue's extra terms: C <- alpha*acc + beta*C_old + row[i] +
 // col[j], the vectors at row + b*sR_b + i*sR_m and col + b*sL_b + j*sL_n.

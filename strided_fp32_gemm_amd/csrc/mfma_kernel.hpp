@@ -530,10 +530,9 @@ void launch_mfma(const MfmaArgs &a, unsigned grid, hipStream_t s) {
     const long long slices = (a.k + cfg.bk - 1) / cfg.bk;
     const int lds = cfg.lds_bytes(AK, BKF, slices);
     // Allow this kernel the largest dynamic LDS any of its launches asks for.
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&sgemm_mfma<T, AK, BKF, AV4, BV4>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, cfg.lds_bytes(AK, BKF, 2));
-    (void)attr;
+    static std::atomic<unsigned long long> lds_set{0};
+    allow_dynamic_lds(reinterpret_cast<const void *>(&sgemm_mfma<T, AK, BKF, AV4, BV4>), cfg.lds_bytes(AK, BKF, 2),
+                      lds_set);
     hipLaunchKernelGGL((sgemm_mfma<T, AK, BKF, AV4, BV4>), dim3(grid), dim3(nt), lds, s, a);
 }
 

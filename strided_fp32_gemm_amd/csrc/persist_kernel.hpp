@@ -243,10 +243,8 @@ void launch_persist(const MfmaArgs &a, unsigned grid, hipStream_t s) {
     constexpr PersistCfg cfg = kPersistTiles[P];
     constexpr int nt = cfg.wgm * cfg.wgn * 64;
     constexpr int lds = 2 * cfg.slab_bytes(AK, BKF);
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&sgemm_persist<P, AK, BKF, ACC>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    (void)attr;
+    static std::atomic<unsigned long long> lds_set{0};
+    allow_dynamic_lds(reinterpret_cast<const void *>(&sgemm_persist<P, AK, BKF, ACC>), lds, lds_set);
     hipLaunchKernelGGL((sgemm_persist<P, AK, BKF, ACC>), dim3(grid), dim3(nt), lds, s, a);
 }
 
