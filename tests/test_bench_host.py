@@ -1,0 +1,37 @@
+"""bench.py's command-line contract on a host without a GPU: it measures one
+GPU only (any other count, by flag or by WORLD_SIZE, exits 2 with a message),
+rejects meaningless step counts, and without a visible GPU fails with a
+message instead of printing a number."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+def run(args, **env):
+    e = dict(os.environ)
+    e.update(env)
+    return subprocess.run([sys.executable, BENCH, *args], capture_output=True, text=True, timeout=300, env=e,
+                          cwd=ROOT)
+
+
+@pytest.mark.parametrize("args,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_is_refused(args, env):
+    r = run(args, **env)
+    assert r.returncode == 2, (r.returncode, r.stderr)
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("args", [["--steps", "0"], ["--warmup", "-1"]])
+def test_bad_step_counts_are_refused(args):
+    r = run(args)
+    assert r.returncode == 2 and r.stdout == "", (r.returncode, r.stderr)
+
+
+def test_no_gpu_is_an_error_not_a_number():
+    r = run(["--steps", "1"], HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    assert r.returncode != 0 and r.stdout == "", (r.returncode, r.stdout)
