@@ -140,12 +140,14 @@ struct Mfma<16> {
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedLdsRead = 0x100, kSchedLdsWrite = 0x200;
 
-// The 16-byte-load layouts are held to two wavefronts per SIMD (at most 256
-// registers per lane), the occupancy at which two workgroups share a CU; the
-// register file otherwise tips some of them to one.
+// The 16-byte-load layouts of the 16-wide-block tiles are held to two
+// wavefronts per SIMD (at most 256 registers per lane), the occupancy at
+// which two workgroups share a CU; the register file otherwise tips some of
+// them to one.  The 32-wide-block tiles are left alone: the largest hold more
+// accumulators than that cap allows without spilling.
 template <int T, bool AK, bool BKF, bool AV4, bool BV4>
 __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64)
-__attribute__((amdgpu_waves_per_eu(AV4 && BV4 ? 2 : 1))) void sgemm_mfma(MfmaArgs p) {
+__attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTiles[T].mf == 16 ? 2 : 1))) void sgemm_mfma(MfmaArgs p) {
     constexpr TileCfg cfg = kTiles[T];
     constexpr int BM = cfg.bm, BN = cfg.bn, BK = cfg.bk, MF = cfg.mf;
     constexpr int NT = cfg.wgm * cfg.wgn * 64;
