@@ -1,0 +1,73 @@
+"""Register budget of the compiled kernels (hipcc cross-compiles gfx950 device
+code on the CPU; no GPU): no kernel instantiation spills registers to scratch
+memory, and the 128 x 128 tile with 16-wide blocks keeps two wavefronts per
+SIMD on its 16-byte-load layouts (two workgroups per CU, the occupancy its
+schedule is built for).  A register cap on a tile whose accumulators do not
+fit it shows up here as scratch, long before a timing does."""
+import concurrent.futures as cf
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from strided_fp32_gemm_amd import build as b
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                                reason="hipcc not available")
+
+KERNEL_SOURCES = [s for s in b.SOURCES if s.endswith(".hip")]
+
+
+def kernel_stats(asm: str):
+    """(kernel symbol, scratch bytes, occupancy) for every kernel in one
+    device assembly file, from the compiler's per-function summary."""
+    out, name = [], None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            name = m.group(1)
+            scratch = occ = None
+            continue
+        m = re.match(r"^\s*; ScratchSize: (\d+)", line)
+        if m and name:
+            scratch = int(m.group(1))
+        m = re.match(r"^\s*; Occupancy: (\d+)", line)
+        if m and name:
+            occ = int(m.group(1))
+            out.append((name, scratch, occ))
+            name = None
+    return out
+
+
+@pytest.fixture(scope="module")
+def stats(tmp_path_factory):
+    tmp = tmp_path_factory.mktemp("asm")
+
+    def one(src):
+        path = tmp / (src + ".s")
+        r = subprocess.run([b._hipcc(), "-x", "hip", *b.common_flags(), "--cuda-device-only", "-S",
+                            os.path.join(b.CSRC, src), "-o", str(path)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return src, kernel_stats(path.read_text())
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        return dict(ex.map(one, KERNEL_SOURCES))
+
+
+def test_every_source_has_kernels(stats):
+    for src, ks in stats.items():
+        assert ks, f"no kernel summary found in {src}"
+
+
+def test_no_kernel_spills(stats):
+    spills = [(src, name, s) for src, ks in stats.items() for name, s, _ in ks if s]
+    assert not spills, spills
+
+
+def test_square_tile_keeps_two_wavefronts_per_simd(stats):
+    # sgemm_mfma<9, AK, BKF, AV4 = true, BV4 = true>: tile 9 is t128x128m16.
+    vec4 = [(n, occ) for n, _, occ in stats["mfma_t9.hip"] if n.endswith("Lb1ELb1EEEvNS_8MfmaArgsE")]
+    assert len(vec4) == 4, vec4
+    assert all(occ >= 2 for _, occ in vec4), vec4
