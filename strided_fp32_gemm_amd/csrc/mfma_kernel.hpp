@@ -140,14 +140,17 @@ struct Mfma<16> {
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedLdsRead = 0x100, kSchedLdsWrite = 0x200;
 
-// The 16-byte-load layouts of the 16-wide-block tiles are held to two
-// wavefronts per SIMD (at most 256 registers per lane), the occupancy at
-// which two workgroups share a CU; the register file otherwise tips some of
-// them to one.  The 32-wide-block tiles are left alone: the largest hold more
-// accumulators than that cap allows without spilling.
+// The 16-byte-load layouts of the 16-wide-block tiles whose LDS lets two
+// workgroups share a CU are held to two wavefronts per SIMD (at most 256
+// registers per lane); the register file otherwise tips some of them to one.
+// Other tiles are left alone: the cap would only make them spill (the 32-wide
+// tiles hold more accumulators, and one workgroup per CU gains nothing).
+template <int T, bool AK, bool BKF>
+constexpr bool kTwoPerSimd = kTiles[T].mf == 16 && 2 * kTiles[T].lds_bytes(AK, BKF, 2) <= 160 * 1024;
+
 template <int T, bool AK, bool BKF, bool AV4, bool BV4>
 __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64)
-__attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTiles[T].mf == 16 ? 2 : 1))) void sgemm_mfma(MfmaArgs p) {
+__attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTwoPerSimd<T, AK, BKF> ? 2 : 1))) void sgemm_mfma(MfmaArgs p) {
     constexpr TileCfg cfg = kTiles[T];
     constexpr int BM = cfg.bm, BN = cfg.bn, BK = cfg.bk, MF = cfg.mf;
     constexpr int NT = cfg.wgm * cfg.wgn * 64;
