@@ -96,7 +96,7 @@ def _child(lib_path):
     return _first_failing_pin(oracle.load_library(lib_path))
 
 
-def _verdict(tmp_path, edits):
+def _outcome(tmp_path, edits):
     """Name of the first pin that rejects the build, "crash:<rc>" if the
     mutant brings its process down (an index mutation can read outside its
     buffer), or None if every pin passes."""
@@ -104,19 +104,19 @@ def _verdict(tmp_path, edits):
     here = os.path.dirname(os.path.abspath(__file__))
     root = os.path.dirname(here)
     code = ("import sys; sys.path[:0] = [%r, %r]; import test_oracle_mutants as t; "
-            "print('VERDICT', t._child(%r))" % (here, root, lib_path))
+            "print('OUTCOME', t._child(%r))" % (here, root, lib_path))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600)
     if r.returncode != 0:
         return f"crash:{r.returncode}"
-    line = [l for l in r.stdout.splitlines() if l.startswith("VERDICT ")][-1]
+    line = [l for l in r.stdout.splitlines() if l.startswith("OUTCOME ")][-1]
     v = line.split(" ", 1)[1]
     return None if v == "None" else v
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(tmp_path, name):
-    assert _verdict(tmp_path, MUTANTS[name]) is not None, f"no pin rejects mutant {name}"
+    assert _outcome(tmp_path, MUTANTS[name]) is not None, f"no pin rejects mutant {name}"
 
 
 def test_pristine_copy_passes(tmp_path):
-    assert _verdict(tmp_path, []) is None
+    assert _outcome(tmp_path, []) is None
