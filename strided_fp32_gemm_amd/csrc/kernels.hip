@@ -172,7 +172,8 @@ const MfmaTable &table() {
         fill_tile_9(tab);
         fill_tile_10(tab);
         fill_tile_11(tab);
-        static_assert(kNumTiles == 12, "launch table covers every tile");
+        fill_tile_12(tab);
+        static_assert(kNumTiles == 13, "launch table covers every tile");
         return tab;
     }();
     return t;

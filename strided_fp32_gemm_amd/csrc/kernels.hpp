@@ -99,6 +99,7 @@ void fill_tile_8(MfmaTable &);
 void fill_tile_9(MfmaTable &);
 void fill_tile_10(MfmaTable &);
 void fill_tile_11(MfmaTable &);
+void fill_tile_12(MfmaTable &);
 void fill_wave_0(WaveTable &);
 void fill_wave_1(WaveTable &);
 void fill_wave_2(WaveTable &);

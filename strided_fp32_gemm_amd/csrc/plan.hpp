@@ -87,7 +87,7 @@ struct TileCfg {
 // The LDS-tiled (MFMA family) tile table.  Kernel instantiations are
 // generated from the same indices (one translation unit per tile), so the
 // order is part of the contract between planner and kernels.
-constexpr int kNumTiles = 12;
+constexpr int kNumTiles = 13;
 inline constexpr TileCfg kTiles[kNumTiles] = {
     {128, 128, 32, 2, 2, 32, "t128x128", 0.87},
     {128, 64, 32, 2, 2, 32, "t128x64", 0.89},
@@ -101,6 +101,7 @@ inline constexpr TileCfg kTiles[kNumTiles] = {
     {128, 128, 32, 2, 2, 16, "t128x128m16", 0.95},
     {128, 64, 32, 2, 2, 16, "t128x64m16", 0.88},
     {64, 128, 32, 2, 2, 16, "t64x128m16", 0.88},
+    {64, 32, 32, 4, 1, 16, "t64x32m16", 0.80},
 };
 
 // One tile of the direct wavefront kernel (WAVE family): a single

@@ -107,7 +107,7 @@ def _cfg_plan(name):
 
 
 @pytest.mark.parametrize("name,path,a_kfast,b_kfast,vec_b", [
-    ("square64", "wave", 1, 0, 4),
+    ("square64", "mfma", 1, 0, 4),
     ("linear_xWt", "mfma", 1, 1, 4),
     ("attn_qk", "mfma", 1, 1, 4),
     ("attn_pv", "mfma", 1, 0, 4),

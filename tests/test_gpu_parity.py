@@ -178,7 +178,7 @@ def test_tile_boundaries(mnk, path):
 
 
 TILE_NAMES = ["t128x128", "t128x64", "t64x128", "t64x64", "t256x128", "t128x160", "t128x80m16",
-              "t64x176m16", "t64x64m16", "t128x128m16", "t128x64m16", "t64x128m16",
+              "t64x176m16", "t64x64m16", "t128x128m16", "t128x64m16", "t64x128m16", "t64x32m16",
               "w32x32", "w32x64", "w64x32", "w64x64"]
 
 
