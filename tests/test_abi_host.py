@@ -297,3 +297,14 @@ def test_attention_validates_and_plans_before_the_device():
     assert plan(sQ=(32 * 6 * 66, 66, 6 * 66, 1))["kernel"] == "attn_generic"     # rows 8-byte aligned only
     assert plan(Q=PA + 8)["kernel"] == "attn_generic"
     assert plan(sK=(32 * 2 * 128, 128, 256, 2))["kernel"] == "attn_generic"     # column stride 2
+
+
+@pytest.mark.parametrize("name,tile", [("linear_bwd_dw", "t64x32m16"), ("linear_bwd_dx", "t64x64m16"),
+                                       ("attn_pv", "t64x64m16"), ("square4096_acc", "t128x128m16")])
+def test_measured_tile_choices(name, tile):
+    """The planner's cost model keeps the tile choices that measured fastest
+    on MI355X: dW (600 tiles of 64x64 on 256 CUs) moves to the 64x32 tile's
+    1200 workgroups, while dX and P.V stay on 64x64 and the 4 x 4096^3 product on
+    128x128 (no GPU: planning runs on the host)."""
+    p = _cfg_plan(name)
+    assert p["path_name"] == "mfma" and tile in p["kernel"], p
