@@ -24,7 +24,13 @@ The JSON line carries:
              kernel sources exists, else null; `achieved_tb_per_s` is the
              algorithmic bytes per launch over the same mean duration
   cpu_baseline  the CPU oracle timed on a bounded slice of the same workload
-             (a block of rows of batch 0), as TFLOP/s, with its thread count.
+             (a block of rows of batch 0), as TFLOP/s, with its thread count,
+             the host's logical CPUs and the CPUs the process may use
+  configs    (default run only) the other configurations of the workload
+             set, each timed in the same process after the headline: the
+             64^3 product, the linear layer, attention's Q K^T and P V, and
+             the spectrogram -- mean launch time, TFLOP/s, fraction of the
+             fp32 matrix peak, kernel, and the oracle on a slice of each.
 """
 from __future__ import annotations
 
@@ -44,15 +50,30 @@ PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 WARMUP_SECONDS = 0.3              # default warm-up: the clock ramps up within it
 METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
 DEFAULT_WORKLOAD = "square4096_acc"
-KERNEL_SOURCES = ["strided_fp32_gemm_amd/csrc/" + f for f in (
-    "mfma_kernel.hpp", "persist_kernel.hpp", "wave_kernel.hpp", "strip_kernel.hip", "kernels.hpp",
-    "kernels.hip", "plan.hpp", "plan.cpp", "buffer.hpp", "extent.hpp", "attn_kernel.hip", "attention.hpp",
-    "attention.cpp")]
+# The other configurations of the method's workload set, timed beside the
+# headline in the default run: the 64^3 product, the linear layer x W^T, the
+# attention scores Q K^T and the product P V, and the spectrogram.
+CONFIG_WORKLOADS = (("1", "square64"), ("2", "linear_xWt"), ("3a", "attn_qk"), ("3b", "attn_pv"),
+                    ("4", "spectrogram"))
+CONFIG_CPU_SECONDS = 1.5          # oracle slice per configuration (the headline's is --cpu-seconds)
+CONFIG_STEPS = 100                # timed launches per configuration
+
+
+def kernel_sources() -> list:
+    """Every source the library is built from (kernels, planner, ABI and
+    the public header), in a fixed order."""
+    csrc = os.path.join(ROOT, "strided_fp32_gemm_amd", "csrc")
+    files = sorted(os.path.join("strided_fp32_gemm_amd", "csrc", f) for f in os.listdir(csrc)
+                   if f.endswith((".hip", ".hpp", ".cpp", ".h")))
+    inc = os.path.join(ROOT, "include")
+    files += sorted(os.path.join("include", f) for f in os.listdir(inc) if f.endswith(".h"))
+    return files
 
 
 def kernel_sources_sha256() -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in kernel_sources():
+        h.update(rel.encode())
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -90,6 +111,17 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def host_cores(threads: int) -> dict:
+    """What the oracle ran on: its OpenMP thread count, the host's logical
+    CPUs and the CPUs this process may use."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cores": threads, "omp_max_threads": threads, "host_cpus": os.cpu_count(),
+            "usable_cpus": usable, "cpu_model": cpu_model()}
+
+
 def cpu_baseline_attention(p, seconds: float) -> dict:
     """The oracle's attention on the first H (sequence, head) pairs of the
     same call (whole heads, every query row), H chosen so the run takes
@@ -113,9 +145,9 @@ def cpu_baseline_attention(p, seconds: float) -> dict:
         heads, t = run(min(total, heads * 4) if heads * 4 <= p.nb_inner
                        else min(total, max(p.nb_inner, heads * 4) // p.nb_inner * p.nb_inner))
     flops = 4.0 * p.d * p.visible_pairs * heads
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", **host_cores(threads), "kind": "oracle",
             "sample": f"all {p.tq} query rows of the first {heads} (sequence, head) pairs "
-                      f"({flops / 1e9:.2f} GFLOP in {t:.1f} s)", "cpu_model": cpu_model()}
+                      f"({flops / 1e9:.2f} GFLOP in {t:.1f} s)"}
 
 
 def cpu_baseline(p, seconds: float) -> dict:
@@ -155,18 +187,39 @@ def cpu_baseline(p, seconds: float) -> dict:
                              int(p.accumulate), out, 0, p.C.s_row, p.C.s_col)
         return time.perf_counter() - t0
 
+    def run_entries(nb):
+        """The first nb whole batch entries of the call (plain products)."""
+        t0 = time.perf_counter()
+        oracle.ref_sgemm(nb, p.m, p.n, p.k, p.alpha, p.A.storage, *p.A.strides, p.B.storage, *p.B.strides,
+                         int(p.accumulate), out, *p.C.strides)
+        return time.perf_counter() - t0
+
     rows = min(p.m, threads)
     t = run(rows)
-    while t < 0.5 and rows < p.m:
+    while t < min(0.5, seconds / 4) and rows < p.m:
         rows = min(p.m, rows * 4)
         t = run(rows)
     if t < seconds and rows < p.m:
         rows = min(p.m, max(rows, int(rows * seconds / max(t, 1e-6)) // threads * threads))
         t = run(rows)
     flops = 2.0 * rows * p.n * p.k
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of batch 0 ({rows}x{p.n}x{p.k}, "
-                      f"{flops / 1e9:.1f} GFLOP in {t:.1f} s)", "cpu_model": cpu_model()}
+    sample = f"rows 0..{rows - 1} of batch 0 ({rows}x{p.n}x{p.k}"
+    if rows == p.m and t < seconds / 2:
+        # Small products: whole batch entries, then the whole call repeated.
+        nb, reps = 1, 1
+        if kind == "plain" and p.batch > 1:
+            nb = min(p.batch, max(1, int(seconds / max(t, 1e-6))))
+            t = run_entries(nb)
+        for _ in range(3):
+            if t >= seconds / 2:
+                break
+            reps = max(reps + 1, int(reps * seconds / max(t, 1e-6)))
+            t = sum(run_entries(nb) if kind == "plain" else run(rows) for _ in range(reps))
+        flops = 2.0 * rows * p.n * p.k * nb * reps
+        sample = f"batch entries 0..{nb - 1} ({nb} x {p.m}x{p.n}x{p.k}) x {reps} repetitions"
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", **host_cores(threads), "kind": "oracle",
+            "sample": f"{sample}, {flops / 1e9:.2f} GFLOP in {t:.2f} s)" if sample.startswith("rows")
+            else f"{sample} ({flops / 1e9:.2f} GFLOP in {t:.2f} s)"}
 
 
 def _step_fn(p, dev, stream):
@@ -211,7 +264,12 @@ def _step_fn(p, dev, stream):
     return (lambda: sg.sgemm_strided_batched(*args, stream=stream)), info, (dA, dB, dC)
 
 
-def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
+def measure(name: str, steps: int, warmup):
+    """Time `steps` launches of one workload (inputs resident in device
+    memory); returns the problem, its plan, the wall time of the timed region,
+    the mean launch time from one HIP event pair on the launch stream around
+    the timed launches, single-launch times from an untimed pass, and the
+    warm-up step count used."""
     import torch
     from strided_fp32_gemm_amd import workloads as wl
 
@@ -259,7 +317,37 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
         ends[i].record(stream)
     torch.cuda.synchronize(dev)
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    del keep
+    torch.cuda.empty_cache()
+    return p, info, wall, mean_ms, launch_ms, warmup
 
+
+def config_entry(label: str, name: str, cpu_seconds: float) -> dict:
+    """One configuration of the workload set: its kernel's mean launch time
+    and rate against the fp32 matrix peak, and the oracle beside it."""
+    from strided_fp32_gemm_amd import workloads as wl
+
+    p, info, _, mean_ms, launch_ms, warmup = measure(name, CONFIG_STEPS, None)
+    flops = float(p.flops)
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    alg_bytes = wl.algorithmic_bytes(p)
+    e = {"config": label, "workload": name, "kernel": info["kernel"], "workgroups": info["workgroups"],
+         "batch": p.batch, "m": p.m, "n": p.n, "k": p.k, "flops_per_launch": flops,
+         "steps": CONFIG_STEPS, "warmup": warmup,
+         "launch_ms_mean": round(mean_ms, 5), "launch_ms_median": round(statistics.median(launch_ms), 5),
+         "launch_ms_min": round(min(launch_ms), 5),
+         "tflops": round(achieved, 3), "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
+         "algorithmic_bytes": alg_bytes,
+         "achieved_tb_per_s": round(alg_bytes / (mean_ms * 1e-3) / 1e12, 3)}
+    if cpu_seconds > 0:
+        e["cpu_baseline"] = cpu_baseline(p, cpu_seconds)
+    return e
+
+
+def bench_one(name: str, steps: int, warmup, cpu_seconds: float) -> dict:
+    from strided_fp32_gemm_amd import workloads as wl
+
+    p, info, wall, mean_ms, launch_ms, warmup = measure(name, steps, warmup)
     flops = float(p.flops)
     value = flops * steps / wall / 1e12
     achieved = flops / (mean_ms * 1e-3) / 1e12
@@ -297,8 +385,6 @@ def bench_one(name: str, steps: int, warmup: int, cpu_seconds: float) -> dict:
     }
     if cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(p, cpu_seconds)
-    del keep
-    torch.cuda.empty_cache()
     return line
 
 
@@ -342,6 +428,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target duration of the CPU oracle baseline (0 skips it)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time the headline workload only (no per-configuration object)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the product, run 3 plain device copies of this many MiB "
                          "(calibrates the HBM byte counters; prints nothing else)")
@@ -371,8 +459,30 @@ def main() -> int:
     names = list(wl.WORKLOADS) if args.workload == "all" else [args.workload]
     for name in names:
         line = bench_one(name, args.steps, args.warmup, args.cpu_seconds)
+        if name == DEFAULT_WORKLOAD and args.workload != "all" and not args.no_configs:
+            line["configs"] = configs_object(line, min(args.cpu_seconds, CONFIG_CPU_SECONDS))
         print(json.dumps(line), flush=True)
     return 0
+
+
+def configs_object(headline: dict, cpu_seconds: float) -> dict:
+    """Every configuration of the workload set beside the headline (config
+    5), each timed in this same process, plus the attention pair together."""
+    out = {}
+    for label, name in CONFIG_WORKLOADS:
+        print(f"[bench] config {label}: {name}", file=sys.stderr, flush=True)
+        out[name] = config_entry(label, name, cpu_seconds)
+    qk, pv = out["attn_qk"], out["attn_pv"]
+    ms = qk["launch_ms_mean"] + pv["launch_ms_mean"]
+    fl = qk["flops_per_launch"] + pv["flops_per_launch"]
+    out["attn_qk_plus_pv"] = {"config": "3", "workload": "attn_qk + attn_pv",
+                              "launch_ms_mean": round(ms, 5), "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
+                              "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP32_MATRIX_TFLOPS, 4)}
+    r = headline["roofline"]
+    out["square4096_acc"] = {"config": "5", "workload": DEFAULT_WORKLOAD, "kernel": r["kernel"],
+                             "launch_ms_mean": r["launch_ms_mean"], "tflops": r["achieved"],
+                             "frac": r["frac"], "cpu_baseline": "see the line's cpu_baseline"}
+    return out
 
 
 if __name__ == "__main__":

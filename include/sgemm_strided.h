@@ -57,7 +57,18 @@ extern "C" {
 #endif
 
 /* Status codes.  Every non-zero status leaves C untouched and enqueues
- * nothing, except SGEMM_ERR_HIP, which reports a failed launch. */
+ * nothing, except SGEMM_ERR_HIP, which reports a failed launch.
+ *
+ * Why they exist: a launch whose sizes do not match what the kernel assumes
+ * reads or writes memory it must not, and nothing reports it, so every size,
+ * stride and pointer a kernel depends on is checked before the launch
+ * (StaleyNET "GPU Implementation", section "Safety").  The individual codes
+ * follow the failure modes kael book ch. 09 "CUDA backend" lists in section
+ * "Edge cases and pitfalls": a zero extent returns before any launch (a grid
+ * of zero blocks is itself an error), index arithmetic that would wrap is
+ * refused rather than run (-5), and faults inside a running kernel are not
+ * reported by the launch but by a later runtime call (-6 only covers what
+ * the runtime reports at launch time). */
 enum sgemm_status {
     SGEMM_OK = 0,
     SGEMM_ERR_INVALID_SIZE = -1,   /* batch, m, n or k < 0 */
@@ -341,11 +352,17 @@ int sgemm_attention_describe(int64_t nb_outer, int64_t nb_inner, int64_t tq, int
                              float *O, int64_t sO_outer, int64_t sO_inner, int64_t sO_row,
                              int64_t sO_col, int path, sgemm_plan_info *info);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL; an unknown code gets a
+ * generic text).  The checks behind the codes are those of StaleyNET "GPU
+ * Implementation", section "Safety" (sizes checked before every launch). */
 const char *sgemm_status_string(int status);
 
 /* Detail of the last non-OK status returned on the calling thread ("" if
- * none).  Valid until the next call on the same thread. */
+ * none): which argument failed which check, or the HIP runtime's message for
+ * SGEMM_ERR_HIP.  Valid until the next call on the same thread.  It never
+ * reports a fault inside a kernel that already started: such faults surface
+ * at the caller's next synchronising runtime call (kael book ch. 09 "CUDA
+ * backend", section "Edge cases and pitfalls", asynchronous errors). */
 const char *sgemm_last_error(void);
 
 #ifdef __cplusplus

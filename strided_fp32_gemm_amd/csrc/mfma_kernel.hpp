@@ -169,7 +169,7 @@ __attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTwoPerSimd<T, AK, BKF> ? 2 : 1
     constexpr int A_LD = A_F + A_PAD, B_LD = B_F + B_PAD;
     constexpr int A_SIZE = A_R * A_LD, B_SIZE = B_R * B_LD;
     static_assert(4 * (A_SIZE + B_SIZE) == cfg.buffer_lds_bytes(AK, BKF), "LDS carve-up");
-    constexpr int E_LD = WN + 4;  // staged-epilogue row pitch
+    constexpr int E_LD = cfg.epi_pitch(BKF);  // staged-epilogue row pitch
     // Dynamic LDS of cfg.lds_bytes(AK, BKF, slices) bytes: one A/B buffer
     // when the k extent is a single slice, two otherwise, and at least the
     // staged epilogue's footprint.

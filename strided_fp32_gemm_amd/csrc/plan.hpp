@@ -74,13 +74,26 @@ struct TileCfg {
         return 4 * ((a_kfast ? bm * (bk + pad(true, a_blocks())) : bk * (bm + pad(false, a_blocks()))) +
                     (b_kfast ? bn * (bk + pad(true, b_blocks())) : bk * (bn + pad(false, b_blocks()))));
     }
-    // LDS bytes of the staged epilogue: every wavefront's (bm/wgm) x (bn/wgn)
-    // sub-tile of C, rows padded by 4 floats.
-    constexpr int epilogue_lds_bytes() const { return 4 * waves() * (bm / wgm) * (bn / wgn + 4); }
+    // Row pitch (floats) of the staged epilogue, where each wavefront parks
+    // its (bm/wgm) x (bn/wgn) sub-tile of C before storing whole rows.  The
+    // row stores read it back with 16-byte LDS reads, 16 lanes per cycle in
+    // the groups above; with rows of 32 or 64 floats and no padding those
+    // groups cover 64 distinct banks.  The accumulators go in with 16-byte
+    // writes (four 16-wide blocks side by side: n-fast B tile with 4 blocks)
+    // or, on 32-wide blocks, with single-float writes of 32 consecutive
+    // columns: both free of conflicts at that pitch.  The single-float writes
+    // of the other 16-wide-block tiles put lane quarters 4 rows apart in one
+    // 32-lane cycle, so their rows keep 4 floats of padding.
+    constexpr int epi_pitch(bool b_kfast) const {
+        const int wn = bn / wgn;
+        return (mf == 32 || (!b_kfast && b_blocks() == 4)) ? wn : wn + 4;
+    }
+    // LDS bytes of the staged epilogue: every wavefront's sub-tile of C.
+    constexpr int epilogue_lds_bytes(bool b_kfast) const { return 4 * waves() * (bm / wgm) * epi_pitch(b_kfast); }
     // LDS a launch allocates for k-slice count `slices` (dynamic shared memory).
     constexpr int lds_bytes(bool a_kfast, bool b_kfast, long long slices) const {
         int loop = buffer_lds_bytes(a_kfast, b_kfast) * (slices > 1 ? 2 : 1);
-        return loop > epilogue_lds_bytes() ? loop : epilogue_lds_bytes();
+        return loop > epilogue_lds_bytes(b_kfast) ? loop : epilogue_lds_bytes(b_kfast);
     }
 };
 

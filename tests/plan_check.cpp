@@ -3,6 +3,8 @@
 // and prints "ok" when every case holds.
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <string>
 #include <random>
 #include <vector>
 
@@ -74,7 +76,7 @@ static void check_split(int64_t inner, int64_t gA, int64_t gB, uint32_t b) {
 // (measured per lane pair with the bank-conflict counter): 16-byte reads in four groups of 16,
 // 8- and 4-byte reads in halves of 32, 16-byte writes in runs of 8.  Two lanes of one group
 // conflict when they touch the same bank at different addresses.
-enum class Op { Read16, Read8, Read4, Write16 };
+enum class Op { Read16, Read8, Read4, Write16, Write4 };
 
 static int lane_group(Op op, int lane) {
     switch (op) {
@@ -84,7 +86,8 @@ static int lane_group(Op op, int lane) {
             return (lane >> 5) * 2 + (first ? 0 : 1);
         }
         case Op::Read8:
-        case Op::Read4: return lane >> 5;
+        case Op::Read4:
+        case Op::Write4: return lane >> 5;
         case Op::Write16: return lane >> 3;
     }
     return 0;
@@ -92,7 +95,7 @@ static int lane_group(Op op, int lane) {
 
 // Extra cycles one instruction spends on conflicts; addr[l] < 0 marks an idle lane.
 static int conflict_cycles(Op op, const long long addr[64]) {
-    const int width = op == Op::Read4 ? 1 : op == Op::Read8 ? 2 : 4;
+    const int width = (op == Op::Read4 || op == Op::Write4) ? 1 : op == Op::Read8 ? 2 : 4;
     int extra = 0;
     for (int g = 0; g < 8; ++g) {
         std::vector<long long> bank[64];
@@ -160,6 +163,37 @@ static void check_tiled_reads(const TileCfg &t, int layout, bool kfast, int bloc
     }
 }
 
+// Staged epilogue of the LDS-tiled kernel for one wavefront: the accumulators written at
+// (row of register r of block a, column of block c), then read back 16 bytes per lane along
+// whole rows.  Checked where the pitch has no padding (epi_pitch): 32-wide blocks, and 16-wide
+// blocks written 16 bytes at a time (an n-fast B tile with 4 blocks per wavefront).
+static void check_epilogue(const TileCfg &t, int layout, bool a_kfast, bool b_kfast) {
+    const int wm = t.bm / t.wgm, wn = t.bn / t.wgn, mf = t.mf, tm = wm / mf, tn = wn / mf;
+    const int ld = t.epi_pitch(b_kfast);
+    if (ld != wn) return;
+    const bool a_il = !a_kfast && mf == 16 && (tm == 2 || tm == 4);
+    const bool b_il = !b_kfast && mf == 16 && (tn == 2 || tn == 4);
+    auto arow = [&](int a, int i) { return a_il ? tm * i + a : a * mf + i; };
+    auto bcol = [&](int c, int j) { return b_il ? tn * j + c : c * mf + j; };
+    auto mrow = [&](int r, int lh) { return mf == 32 ? 8 * (r >> 2) + 4 * lh + (r & 3) : 4 * lh + r; };
+    const int regs = mf == 32 ? 16 : 4;
+    long long addr[64];
+    for (int a = 0; a < tm; ++a)
+        for (int c = 0; c < (b_il && tn == 4 ? 1 : tn); ++c)
+            for (int r = 0; r < regs; ++r) {
+                for (int l = 0; l < 64; ++l) addr[l] = (long long)arow(a, mrow(r, l / mf)) * ld + bcol(c, l % mf);
+                expect_free("epilogue write", t.name, layout, b_il && tn == 4 ? Op::Write16 : Op::Write4, addr);
+            }
+    const int per_row = wn / 4;
+    for (int i = 0; i < wm * wn / 4 / 64; ++i) {
+        for (int l = 0; l < 64; ++l) {
+            const int q = l + 64 * i;
+            addr[l] = (long long)(q / per_row) * ld + (q % per_row) * 4;
+        }
+        expect_free("epilogue read", t.name, layout, Op::Read16, addr);
+    }
+}
+
 static void check_lds_banks() {
     for (int i = 0; i < kNumTiles; ++i) {
         const TileCfg &t = kTiles[i];
@@ -172,6 +206,7 @@ static void check_lds_banks() {
             const int nt = t.waves() * 64;
             check_stage(t.name, layout, t.bm * t.bk / a_f, a_f, a_pad, nt);
             check_stage(t.name, layout, t.bn * t.bk / b_f, b_f, b_pad, nt);
+            check_epilogue(t, layout, ak, bk);
         }
     }
     // Persistent short-k kernel: 16-wide blocks, k groups of 16, single-float reads on m- or
@@ -202,7 +237,28 @@ static void check_lds_banks() {
     check_stage("strip", 0, StripCfg::kBlockCols, 64, pitch - 64, 8 * 64);
 }
 
-int main() {
+// `plan_check tiles BATCH ROWS COLUMNS EDGE`: the tile order of a launch over
+// EDGE x EDGE output tiles, one line per workgroup id w: "w b tm tn first_row
+// row_count first_column column_count", counts clipped at the matrix edge as
+// the kernels clip them (a row is stored when row - first_row < rows -
+// first_row).  The worked example of a tile decomposition is checked against
+// these lines by test_abi_host.py.
+static int print_tiles(int batch, int rows, int cols, int edge) {
+    const int tiles_m = (rows + edge - 1) / edge, tiles_n = (cols + edge - 1) / edge;
+    const TileMap map = make_tile_map(batch, tiles_m, tiles_n);
+    for (int w = 0; w < batch * tiles_m * tiles_n; ++w) {
+        int b, tm, tn;
+        tile_coords(map, w, b, tm, tn);
+        const int r0 = tm * edge, c0 = tn * edge;
+        const int rc = rows - r0 < edge ? rows - r0 : edge, cc = cols - c0 < edge ? cols - c0 : edge;
+        std::printf("%d %d %d %d %d %d %d %d\n", w, b, tm, tn, r0, rc, c0, cc);
+    }
+    return 0;
+}
+
+int main(int argc, char **argv) {
+    if (argc == 6 && std::string(argv[1]) == "tiles")
+        return print_tiles(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]));
     check_lds_banks();
     std::mt19937_64 rng(12345);
     const uint32_t top = 0x7fffffffu;

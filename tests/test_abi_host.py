@@ -8,13 +8,18 @@ touches a device.
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
+import numpy as np
 import pytest
 
 import strided_fp32_gemm_amd as sg
 from strided_fp32_gemm_amd import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.join(ROOT, "tests")
+CSRC = os.path.join(ROOT, "strided_fp32_gemm_amd", "csrc")
 HEADER = os.path.join(ROOT, "include", "sgemm_strided.h")
 
 # Fake, suitably aligned device addresses: the planner reads alignment only.
@@ -167,8 +172,44 @@ def test_tile_map_example_shape_is_planned():
     for path in (sg.PATH_WAVE, sg.PATH_MFMA, sg.PATH_GENERIC):
         p = plan(1, rows, cols, inner, (0, inner, 1), (0, cols, 1), (0, cols, 1), path=path)
         assert p["workgroups"] == 1
-    # The pages' own 4 x 4 decomposition of that shape: 2 x 3 tiles.
-    assert (-(-rows // 4), -(-cols // 4)) == (int(g["tile_rows"]), int(g["tile_columns"]))
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+@pytest.mark.parametrize("batches", [1, 3])
+def test_tile_order_on_the_worked_example(tmp_path, batches):
+    """The library's own tile-order code (plan.hpp's tile_coords, compiled
+    with g++) driven over the 4 x 4 decomposition of kael ch. 09 "Matmul"'s
+    worked example (rows 5, columns 9): 2 x 3 tiles per batch entry, each
+    output covered exactly once, and the page's tile 4 (first row (4 / 3) * 4,
+    first column (4 % 3) * 4) clipped to out[4][4..7].  The library visits the
+    tiles in its own order (grouped tile rows, column by column), so the
+    page's tile number is located by its (tile row, tile column); with 6
+    tiles per launch the XCD remap is off (6 is not a multiple of 8), and
+    with 3 batch entries (18 tiles) it is off too."""
+    from helpers import load_golden
+    g = load_golden("kael_tile_map.txt")
+    rows, cols, edge = int(g["rows"]), int(g["columns"]), 4
+    exe = tmp_path / "plan_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, os.path.join(HERE, "plan_check.cpp"), "-o",
+                    str(exe)], check=True)
+    r = subprocess.run([str(exe), "tiles", str(batches), str(rows), str(cols), str(edge)],
+                       capture_output=True, text=True, check=True, timeout=60)
+    lines = [tuple(int(t) for t in ln.split()) for ln in r.stdout.split("\n") if ln.strip()]
+    assert len(lines) == batches * int(g["tiles"])
+    assert [ln[0] for ln in lines] == list(range(len(lines)))
+    assert max(ln[2] for ln in lines) + 1 == int(g["tile_rows"])
+    assert max(ln[3] for ln in lines) + 1 == int(g["tile_columns"])
+    cover = np.zeros((batches, rows, cols), np.int64)
+    for _, b, tm, tn, r0, rc, c0, cc in lines:
+        assert (r0, c0) == (tm * edge, tn * edge)
+        cover[b, r0:r0 + rc, c0:c0 + cc] += 1
+    assert (cover == 1).all()
+    tile = int(g["tile"])
+    want = (tile // int(g["tile_columns"]), tile % int(g["tile_columns"]))
+    for b in range(batches):
+        (hit,) = [ln for ln in lines if ln[1] == b and (ln[2], ln[3]) == want]
+        assert hit[4:] == (int(g["tile4_first_row"]), int(g["tile4_row_count"]),
+                           int(g["tile4_first_column"]), int(g["tile4_column_count"]))
 
 
 def test_short_k_kernels_serve_short_k_only(monkeypatch):

@@ -35,3 +35,31 @@ def test_bad_step_counts_are_refused(args):
 def test_no_gpu_is_an_error_not_a_number():
     r = run(["--steps", "1"], HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
     assert r.returncode != 0 and r.stdout == "", (r.returncode, r.stdout)
+
+
+def test_traffic_record_hash_covers_every_built_source():
+    """The counter record bench.py reports as `roofline.traffic` is only
+    trusted while the hash of the library's sources matches the one it was
+    taken on; that hash must cover every file the build compiles and every
+    header those files include (directly or not), and the public header."""
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    from strided_fp32_gemm_amd import build
+    hashed = set(bench.kernel_sources())
+    csrc = os.path.join("strided_fp32_gemm_amd", "csrc")
+    todo = [os.path.join(csrc, f) for f in build.SOURCES]
+    seen = set()
+    while todo:
+        rel = todo.pop()
+        if rel in seen:
+            continue
+        seen.add(rel)
+        assert rel in hashed, rel
+        text = open(os.path.join(ROOT, rel)).read()
+        for inc in re.findall(r'#include\s+"([^"]+)"', text):
+            local = os.path.join(csrc, inc)
+            todo.append(local if os.path.exists(os.path.join(ROOT, local)) else os.path.join("include", inc))
+    assert os.path.join("include", "sgemm_strided.h") in seen
+    before = bench.kernel_sources_sha256()
+    assert before == bench.kernel_sources_sha256() and len(before) == 64

@@ -251,27 +251,21 @@ def test_pairwise_sqdist_workspace_errors():
     assert e.value.status == -4
 
 
-def _sample(rng, batch, m, n, count=3000):
-    idx = np.stack([rng.integers(0, batch, count), rng.integers(0, m, count), rng.integers(0, n, count)], 1)
-    corners = [(b, i, j) for b in {0, batch - 1} for i in {0, m - 1} for j in {0, n - 1}]
-    return np.concatenate([idx, np.array(corners)], 0).astype(np.int64)
-
-
 def test_linear_bias_full_size():
     """The bias-fused linear layer at full size, as the benchmark runs it:
-    sampled outputs against the oracle, and two calls give the same bits."""
+    every output against the oracle, and two calls give the same bits."""
     p = wl.workload("linear_bias")
     dA, dB, dC, dl = dev(p.A.storage), dev(p.B.storage), dev(p.C.storage), dev(p.col.storage)
     s = torch.cuda.current_stream()
     sg.sgemm_strided_batched_ex(*p.ex_call_args(dA, dB, dC, None, dl), stream=s)
     torch.cuda.synchronize()
     got = dC.cpu().numpy()
-    idx = _sample(np.random.default_rng(801), p.batch, p.m, p.n)
-    ref = oracle.ref_sgemm_ex_entries(p.batch, p.m, p.n, p.k, p.alpha, p.A.storage, p.A.strides,
-                                      p.B.storage, p.B.strides, p.beta_value, p.C.storage, p.C.strides,
-                                      idx, **_oracle_vec_args(p))
-    gv = view(got, p.batch, p.m, p.n, p.C.strides)[idx[:, 0], idx[:, 1], idx[:, 2]]
-    assert ex_err(p, gv, ref) <= TOL
+    ref = p.C.storage.copy()
+    oracle.ref_sgemm_ex(p.batch, p.m, p.n, p.k, p.alpha, p.A.storage, p.A.strides, p.B.storage,
+                        p.B.strides, p.beta_value, ref, p.C.strides, **_oracle_vec_args(p))
+    gv = view(got, p.batch, p.m, p.n, p.C.strides)
+    rv = view(ref, p.batch, p.m, p.n, p.C.strides)
+    assert ex_err(p, gv, rv) <= TOL
     dC2 = dev(p.C.storage)
     sg.sgemm_strided_batched_ex(*p.ex_call_args(dA, dB, dC2, None, dl), stream=s)
     torch.cuda.synchronize()
@@ -280,7 +274,7 @@ def test_linear_bias_full_size():
 
 def test_sqdist_full_size():
     """The distance table at full size (4 x 4096 vectors against a shared
-    1024-entry codebook, 512 features): sampled distances against the plain
+    1024-entry codebook, 512 features): every distance against the plain
     definition, and two calls give the same bits."""
     p = wl.workload("sqdist")
     dX, dY, dD = dev(p.X.storage), dev(p.Y.storage), dev(p.D.storage)
@@ -289,11 +283,12 @@ def test_sqdist_full_size():
     sg.sgemm_pairwise_sqdist(*p.call_args(dX, dY, dD, ws), stream=s)
     torch.cuda.synchronize()
     got = dD.cpu().numpy()
-    idx = _sample(np.random.default_rng(802), p.batch, p.m, p.n)
-    ref = oracle.ref_sqdist_entries(p.batch, p.m, p.n, p.k, p.X.storage, p.X.strides, p.Y.storage,
-                                    p.Y.strides, idx)
-    gv = view(got, p.batch, p.m, p.n, p.D.strides)[idx[:, 0], idx[:, 1], idx[:, 2]]
-    assert _dist_err(p.X.storage, p.Y.storage, p.k, gv, ref) <= TOL
+    ref = p.D.storage.copy()
+    oracle.ref_sqdist(p.batch, p.m, p.n, p.k, p.X.storage, p.X.strides, p.Y.storage, p.Y.strides,
+                      ref, p.D.strides)
+    gv = view(got, p.batch, p.m, p.n, p.D.strides)
+    rv = view(ref, p.batch, p.m, p.n, p.D.strides)
+    assert _dist_err(p.X.storage, p.Y.storage, p.k, gv, rv) <= TOL
     dD2 = torch.zeros_like(dD)
     sg.sgemm_pairwise_sqdist(*p.call_args(dX, dY, dD2, ws), stream=s)
     torch.cuda.synchronize()
