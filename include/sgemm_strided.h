@@ -42,6 +42,7 @@
  *   sgemm_strided_batched_ex[_path]    + beta*C + per-row and per-column terms
  *   sgemm_strided_batched2[_path]      two batch levels, grouped inputs (KV heads)
  *   sgemm_sqnorms, sgemm_pairwise_sqdist   squared norms, squared distances
+ *   sgemm_pairwise_sqdist_noalloc      the same distances without a workspace
  *   sgemm_attention[_path]             softmax(alpha Q K^T) V, fused, over two batch levels
  *   sgemm_plan_describe[2], sgemm_attention_describe   the launch a call would make
  *   sgemm_status_string, sgemm_last_error   status text
@@ -243,6 +244,30 @@ int sgemm_pairwise_sqdist(int64_t batch, int64_t m, int64_t n, int64_t k,
                           float *D, int64_t sD_batch, int64_t sD_row, int64_t sD_col,
                           float *workspace, int64_t workspace_floats,
                           void *stream);
+
+/*
+ * sgemm_pairwise_sqdist without a workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, result bits and status
+ * codes as sgemm_pairwise_sqdist, except that the two norm vectors go to a
+ * device array inside the library (one per GPU, SGEMM_SCRATCH_FLOATS floats,
+ * 4 MiB, held from the library's load until the process ends), so no memory
+ * is allocated or freed by the call.
+ *
+ * Limit: batch*m + nY*n <= SGEMM_SCRATCH_FLOATS (nY = 1 when sY_batch == 0,
+ * else batch); a larger call returns SGEMM_ERR_WORKSPACE before anything is
+ * enqueued, with the sizes in sgemm_last_error().  Every call on one GPU uses
+ * that GPU's array and leaves its norms there: calls that overlap in time on
+ * one GPU (different streams or host threads without ordering) race and
+ * must be serialised by the caller.  Nothing in the array needs clearing
+ * between calls (each call writes every norm it reads).
+ */
+#define SGEMM_SCRATCH_FLOATS (1 << 20)
+int sgemm_pairwise_sqdist_noalloc(int64_t batch, int64_t m, int64_t n, int64_t k,
+                                  const float *X, int64_t sX_batch, int64_t sX_row, int64_t sX_col,
+                                  const float *Y, int64_t sY_batch, int64_t sY_row, int64_t sY_col,
+                                  float *D, int64_t sD_batch, int64_t sD_row, int64_t sD_col,
+                                  void *stream);
 
 /* What the planner would launch (filled by sgemm_plan_describe). */
 typedef struct sgemm_plan_info {

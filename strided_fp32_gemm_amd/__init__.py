@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     PATH_MFMA,
     PATH_NAMES,
     PATH_WAVE,
+    SCRATCH_FLOATS,
     SgemmError,
     load,
     sgemm_attention,
@@ -27,6 +28,7 @@ from ._binding import (  # noqa: F401
     sgemm_attention_path,
     sgemm_last_error,
     sgemm_pairwise_sqdist,
+    sgemm_pairwise_sqdist_noalloc,
     sgemm_plan_describe,
     sgemm_plan_describe2,
     sgemm_sqnorms,

@@ -30,7 +30,8 @@ STATUS = {
 # Every symbol include/sgemm_strided.h declares.
 EXPORTS = ("sgemm_strided_batched", "sgemm_strided_batched_path", "sgemm_strided_batched_ex",
            "sgemm_strided_batched_ex_path", "sgemm_strided_batched2", "sgemm_strided_batched2_path",
-           "sgemm_sqnorms", "sgemm_pairwise_sqdist", "sgemm_attention", "sgemm_attention_path",
+           "sgemm_sqnorms", "sgemm_pairwise_sqdist", "sgemm_pairwise_sqdist_noalloc",
+           "sgemm_attention", "sgemm_attention_path",
            "sgemm_attention_describe",
            "sgemm_plan_describe", "sgemm_plan_describe2", "sgemm_status_string", "sgemm_last_error")
 
@@ -134,6 +135,12 @@ def load(path: str = LIB_PATH):
                                           _vp, _i64, _i64, _i64,
                                           _vp, _i64, _i64, _i64,
                                           _vp, _i64, _vp]
+    lib.sgemm_pairwise_sqdist_noalloc.restype = _int
+    lib.sgemm_pairwise_sqdist_noalloc.argtypes = [_i64, _i64, _i64, _i64,
+                                                  _vp, _i64, _i64, _i64,
+                                                  _vp, _i64, _i64, _i64,
+                                                  _vp, _i64, _i64, _i64,
+                                                  _vp]
     lib.sgemm_plan_describe.restype = _int
     lib.sgemm_plan_describe.argtypes = _GEMM_ARGS + [_int, _int, ctypes.POINTER(PlanInfo)]
     lib.sgemm_plan_describe2.restype = _int
@@ -357,6 +364,24 @@ def sgemm_pairwise_sqdist(batch, m, n, k,
                                         _ptr(Y), int(sY_batch), int(sY_row), int(sY_col),
                                         _ptr(D), int(sD_batch), int(sD_row), int(sD_col),
                                         _ptr(workspace), int(workspace_floats), _stream(stream)))
+
+
+# Norm floats the allocation-free distance entry point can hold
+# (SGEMM_SCRATCH_FLOATS of the public header).
+SCRATCH_FLOATS = 1 << 20
+
+
+def sgemm_pairwise_sqdist_noalloc(batch, m, n, k,
+                                  X, sX_batch, sX_row, sX_col,
+                                  Y, sY_batch, sY_row, sY_col,
+                                  D, sD_batch, sD_row, sD_col, stream=None) -> None:
+    """sgemm_pairwise_sqdist with the norms in the library's fixed device
+    scratch (no workspace; batch*m + nY*n <= SCRATCH_FLOATS)."""
+    _check(load().sgemm_pairwise_sqdist_noalloc(int(batch), int(m), int(n), int(k),
+                                                _ptr(X), int(sX_batch), int(sX_row), int(sX_col),
+                                                _ptr(Y), int(sY_batch), int(sY_row), int(sY_col),
+                                                _ptr(D), int(sD_batch), int(sD_row), int(sD_col),
+                                                _stream(stream)))
 
 
 def sgemm_plan_describe(batch, m, n, k, alpha,

@@ -17,6 +17,7 @@
 #include <string>
 
 #include "attention.hpp"
+#include "entry.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
 
@@ -334,6 +335,17 @@ int sgemm_pairwise_sqdist(int64_t batch, int64_t m, int64_t n, int64_t k, const 
                           int64_t sY_batch, int64_t sY_row, int64_t sY_col, float *D,
                           int64_t sD_batch, int64_t sD_row, int64_t sD_col, float *workspace,
                           int64_t workspace_floats, void *stream) {
+    return sgemm::pairwise_sqdist(batch, m, n, k, X, sX_batch, sX_row, sX_col, Y, sY_batch, sY_row, sY_col, D,
+                                  sD_batch, sD_row, sD_col, workspace, workspace_floats, 0, nullptr, stream);
+}
+
+}  // extern "C"
+
+int sgemm::pairwise_sqdist(int64_t batch, int64_t m, int64_t n, int64_t k, const float *X, int64_t sX_batch,
+                           int64_t sX_row, int64_t sX_col, const float *Y, int64_t sY_batch, int64_t sY_row,
+                           int64_t sY_col, float *D, int64_t sD_batch, int64_t sD_row, int64_t sD_col,
+                           float *workspace, int64_t workspace_floats, int64_t fixed_floats,
+                           ScratchAddressFn fixed_address, void *stream) {
     // Validate the whole call first (as the product D <- -2 X Y^T), so that
     // an error enqueues nothing.
     sgemm::GemmArgs a = pack(batch, m, n, k, -2.0f, X, sX_batch, sX_row, sX_col, Y, sY_batch,
@@ -347,6 +359,16 @@ int sgemm_pairwise_sqdist(int64_t batch, int64_t m, int64_t n, int64_t k, const 
     if (__builtin_mul_overflow(batch, m, &need) || __builtin_mul_overflow(ny, n, &ny_n) ||
         __builtin_add_overflow(need, ny_n, &need))
         return fail(SGEMM_ERR_UNSUPPORTED, "workspace size overflows int64");
+    if (fixed_floats > 0) {
+        if (need > fixed_floats)
+            return fail(SGEMM_ERR_WORKSPACE,
+                        "the call needs batch*m + nY*n = " + std::to_string(need) +
+                            " floats of norms; the allocation-free entry point's fixed device scratch holds " +
+                            std::to_string(fixed_floats) + " (use sgemm_pairwise_sqdist with a workspace)");
+        st = fixed_address(&workspace, why);
+        if (st != SGEMM_OK) return fail(st, why);
+        workspace_floats = fixed_floats;
+    }
     if (!workspace || workspace_floats < need)
         return fail(SGEMM_ERR_WORKSPACE, "workspace needs batch*m + nY*n floats");
     const uintptr_t ws = reinterpret_cast<uintptr_t>(workspace);
@@ -366,6 +388,8 @@ int sgemm_pairwise_sqdist(int64_t batch, int64_t m, int64_t n, int64_t k, const 
     a.col_add = reinterpret_cast<uintptr_t>(nyv); a.sL_batch = sY_batch == 0 ? 0 : n; a.sL_col = 1;
     return run_gemm(a, SGEMM_PATH_AUTO, stream);
 }
+
+extern "C" {
 
 int sgemm_strided_batched(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
                           const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,

@@ -349,3 +349,23 @@ def test_measured_tile_choices(name, tile):
     128x128 (no GPU: planning runs on the host)."""
     p = _cfg_plan(name)
     assert p["path_name"] == "mfma" and tile in p["kernel"], p
+
+
+def test_noalloc_distance_checks_before_the_device():
+    """The allocation-free distance entry point validates exactly like the
+    workspace one and refuses a call whose norms exceed its fixed scratch,
+    both before any HIP call (this host has no GPU); its capacity is the
+    header's SGEMM_SCRATCH_FLOATS."""
+    text = open(HEADER).read()
+    (cap,) = re.findall(r"#define\s+SGEMM_SCRATCH_FLOATS\s+\(1 << (\d+)\)", text)
+    assert sg.SCRATCH_FLOATS == 1 << int(cap)
+    f = sg.sgemm_pairwise_sqdist_noalloc
+    assert status_of(lambda: f(1, -1, 4, 4, PA, 16, 4, 1, PB, 16, 4, 1, PC, 16, 4, 1)) == -1
+    assert status_of(lambda: f(1, 4, 4, 4, PA, 16, -4, 1, PB, 16, 4, 1, PC, 16, 4, 1)) == -2
+    assert status_of(lambda: f(1, 4, 4, 4, 0, 16, 4, 1, PB, 16, 4, 1, PC, 16, 4, 1)) == -3
+    m = sg.SCRATCH_FLOATS      # batch*m + n exceeds the scratch by n
+    with pytest.raises(sg.SgemmError) as e:
+        f(1, m, 8, 4, PA, m * 4, 4, 1, PB, 0, 4, 1, PC, m * 8, 8, 1)
+    assert e.value.status == -8 and "fixed device scratch" in str(e.value)
+    # Empty calls return OK without touching anything.
+    f(0, 4, 4, 4, PA, 16, 4, 1, PB, 16, 4, 1, PC, 16, 4, 1)
