@@ -278,6 +278,7 @@ typedef struct sgemm_plan_info {
     int vec_a, vec_b;    /* global load width in floats for A and B */
     int a_kfast, b_kfast;/* 1 if the operand's contiguous axis is k */
     int launches;        /* kernels enqueued (0 for an empty product) */
+    int fixed_offsets;   /* LDS-tiled kernel: load offsets computed once, k bounded by the buffer size */
     int64_t workgroups;  /* workgroups of the main launch */
     char kernel[64];     /* kernel variant name */
 } sgemm_plan_info;

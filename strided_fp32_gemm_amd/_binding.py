@@ -58,6 +58,7 @@ class PlanInfo(ctypes.Structure):
         ("a_kfast", ctypes.c_int),
         ("b_kfast", ctypes.c_int),
         ("launches", ctypes.c_int),
+        ("fixed_offsets", ctypes.c_int),
         ("workgroups", ctypes.c_int64),
         ("kernel", ctypes.c_char * 64),
     ]

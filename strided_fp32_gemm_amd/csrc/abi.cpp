@@ -446,6 +446,7 @@ int describe(const sgemm::GemmArgs &a, int path, int num_cus, sgemm_plan_info *i
     info->a_kfast = plan.a_kfast ? 1 : 0;
     info->b_kfast = plan.b_kfast ? 1 : 0;
     info->launches = plan.empty ? 0 : 1;
+    info->fixed_offsets = plan.fixed_offsets ? 1 : 0;
     info->workgroups = plan.empty ? 0 : plan.workgroups;
     std::strncpy(info->kernel, plan.kernel_name.c_str(), sizeof info->kernel - 1);
     return SGEMM_OK;

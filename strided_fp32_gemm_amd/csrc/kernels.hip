@@ -263,7 +263,7 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
             wave_table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4](
                 a, unsigned(p.workgroups), stream);
         else
-            table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4](
+            table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4][p.fixed_offsets](
                 a, unsigned(p.workgroups), stream);
     }
     hipError_t e = hipGetLastError();

@@ -73,12 +73,12 @@ struct GenericArgs {
 };
 
 // Launchers indexed [tile][A k-fast][B k-fast][A 16-byte loads]
-// [B 16-byte loads].  Each tile's row is filled by its own translation unit
-// (mfma_t<tile>.hip, wave_w<tile>.hip) so the instantiations compile in
-// parallel.
+// [B 16-byte loads] (and, for the LDS-tiled kernel, [fixed slot offsets]).
+// Each tile's row is filled by its own translation unit (mfma_t<tile>.hip,
+// wave_w<tile>.hip) so the instantiations compile in parallel.
 using MfmaLaunch = void (*)(const MfmaArgs &, unsigned, hipStream_t);
 struct MfmaTable {
-    MfmaLaunch f[kNumTiles][2][2][2][2];
+    MfmaLaunch f[kNumTiles][2][2][2][2][2];
 };
 struct WaveTable {
     MfmaLaunch f[kNumWaveTiles][2][2][2][2];

@@ -403,6 +403,19 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         p.tiles_n = (p.n + bn - 1) / bn;
         p.workgroups = p.batch * p.tiles_m * p.tiles_n;
         if (best_persist) p.workgroups = persist_grid(p, kPersistTiles[best], num_cus, p.workgroups);
+        if (!best_wave && !best_persist) {
+            // The LDS-tiled kernel keeps each thread's load offsets for the
+            // whole k loop when the buffer resource alone can bound k: an
+            // operand read along k (tile columns along k) needs whole slices,
+            // one read across k (tile rows along k) needs rows that do not
+            // overlap, so that a row index past K means an offset past the
+            // resource's end.
+            const int64_t bk = kTiles[best].bk;
+            auto bounded = [&](bool kfast, int64_t extent, int64_t s_fast, int64_t s_k) {
+                return kfast ? p.k % bk == 0 : (extent - 1) * s_fast < s_k;
+            };
+            p.fixed_offsets = bounded(p.a_kfast, p.m, p.sA_m, p.sA_k) && bounded(p.b_kfast, p.n, p.sB_n, p.sB_k);
+        }
         p.kernel_name = std::string(best_wave ? "wave_" : best_persist ? "persist_" : "mfma_") + name +
                         (p.a_kfast ? "_ak" : "_am") + (p.b_kfast ? "_bk" : "_bn") +
                         (p.accumulate ? "_acc" : "") + (p.row_add || p.col_add ? "_vec" : "");

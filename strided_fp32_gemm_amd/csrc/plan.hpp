@@ -275,6 +275,7 @@ struct Plan {
     bool strip = false;        // MFMA family, short-k strip kernel (tile indexes kStripTiles)
     bool a_kfast = true, b_kfast = false;
     int vec_a = 1, vec_b = 1;
+    bool fixed_offsets = false;  // LDS-tiled kernel: load offsets fixed over the k loop (see make_plan)
     bool c_vec4 = false;       // C rows take 16-byte stores
     int64_t batch = 0, m = 0, n = 0, k = 0;
     float alpha = 1.0f;

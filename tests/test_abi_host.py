@@ -369,3 +369,25 @@ def test_noalloc_distance_checks_before_the_device():
     assert e.value.status == -8 and "fixed device scratch" in str(e.value)
     # Empty calls return OK without touching anything.
     f(0, 4, 4, 4, PA, 16, 4, 1, PB, 16, 4, 1, PC, 16, 4, 1)
+
+
+def test_fixed_offsets_where_the_buffer_size_bounds_k():
+    """The LDS-tiled kernel keeps its load offsets for the whole k loop when
+    the buffer resource alone can bound k: every benchmark product does; a
+    k-fast operand with a partial last slice, or a k-slow one whose rows
+    overlap, takes the per-slice loader."""
+    for name in ("linear_xWt", "attn_pv", "spectrogram", "square4096_acc", "linear_bwd_dx", "linear_bwd_dw",
+                 "linear_xT"):
+        p = _cfg_plan(name)
+        assert p["fixed_offsets"] == 1 and p["kernel"].startswith("mfma_"), (name, p)
+    mfma = sg.PATH_MFMA
+    # k-fast A and B, k = 100 (not a multiple of the 32-deep slice): per slice.
+    assert plan(2, 128, 128, 100, (128 * 100, 100, 1), (128 * 100, 1, 100), (128 * 128, 128, 1),
+                path=mfma)["fixed_offsets"] == 0
+    # k-slow A and B with the same ragged k: the buffer size bounds the rows.
+    assert plan(2, 128, 128, 100, (128 * 100, 1, 128), (128 * 100, 128, 1), (128 * 128, 128, 1),
+                path=mfma)["fixed_offsets"] == 1
+    # k-slow B whose rows overlap (row stride 64 < 128 columns): per slice.
+    assert plan(1, 128, 128, 96, (0, 96, 1), (0, 64, 1), (0, 128, 1), path=mfma)["fixed_offsets"] == 0
+    # Other kernel families never use it.
+    assert plan(1, 100, 90, 70, (0, 70, 1), (0, 90, 1), (0, 90, 1), path=sg.PATH_WAVE)["fixed_offsets"] == 0
