@@ -43,6 +43,10 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, unsigned off, f
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, int(off), 0, 0);
 }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedVmemWrite = 0x040, kSchedLdsRead = 0x100,
+              kSchedLdsWrite = 0x200;
+
 // Device-scope store (cache-policy operand 16 sets sc1): the line goes out to
 // the memory side of the fabric instead of collecting as a dirty line in the
 // XCD's L2.  The short-k kernels, whose time is set by streaming their

@@ -174,8 +174,6 @@ struct Mfma<16> {
     static __device__ __forceinline__ int row(int r, int lh) { return 4 * lh + r; }
 };
 
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedLdsRead = 0x100, kSchedLdsWrite = 0x200;
 
 // The 16-byte-load layouts of the 16-wide-block tiles whose LDS lets two
 // workgroups share a CU are held to two wavefronts per SIMD (at most 256
