@@ -262,9 +262,16 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         else if (p.family == Family::Wave)
             wave_table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4](
                 a, unsigned(p.workgroups), stream);
-        else
-            table().f[p.tile][p.a_kfast][p.b_kfast][p.vec_a == 4][p.vec_b == 4][p.fixed_offsets](
-                a, unsigned(p.workgroups), stream);
+        else {
+            const MfmaLaunch fn =
+                table().f[p.tile][p.a_kfast][p.b_kfast][width_index(p.vec_a)][width_index(p.vec_b)][p.fixed_offsets];
+            if (!fn) {
+                why = "no tiled kernel instance for load widths " + std::to_string(p.vec_a) + "/" +
+                      std::to_string(p.vec_b) + (p.fixed_offsets ? " with" : " without") + " fixed offsets";
+                return kErrUnsupported;
+            }
+            fn(a, unsigned(p.workgroups), stream);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) {

@@ -73,13 +73,16 @@ struct GenericArgs {
 };
 
 // Launchers indexed [tile][A k-fast][B k-fast][A 16-byte loads]
-// [B 16-byte loads] (and, for the LDS-tiled kernel, [fixed slot offsets]).
-// Each tile's row is filled by its own translation unit (mfma_t<tile>.hip,
-// wave_w<tile>.hip) so the instantiations compile in parallel.
+// [B 16-byte loads]; the LDS-tiled kernel's table is indexed by load width
+// (0: element, 1: 8-byte, 2: 16-byte; see width_index) and [fixed slot
+// offsets].  Each tile's row is filled by its own translation unit
+// (mfma_t<tile>.hip, wave_w<tile>.hip) so the instantiations compile in
+// parallel.
 using MfmaLaunch = void (*)(const MfmaArgs &, unsigned, hipStream_t);
 struct MfmaTable {
-    MfmaLaunch f[kNumTiles][2][2][2][2][2];
+    MfmaLaunch f[kNumTiles][2][2][3][3][2];
 };
+constexpr int width_index(int floats) { return floats == 4 ? 2 : floats == 2 ? 1 : 0; }
 struct WaveTable {
     MfmaLaunch f[kNumWaveTiles][2][2][2][2];
 };

@@ -54,9 +54,13 @@ namespace sgemm {
 
 // An R x F tile (F along the operand's contiguous axis) held as one f32x4
 // per slot; NT threads cover its R*F/4 slots in rounds, the last round
-// possibly partial.  In LDS the tile is stored [R][F + PAD].
-template <int R, int F, int PAD, int NT, bool V4>
+// possibly partial.  In LDS the tile is stored [R][F + PAD].  VW is the
+// global load width in floats: 4 (16-byte loads), 2 (8-byte loads, fixed
+// offsets only) or 1 (element loads, any stride).
+template <int R, int F, int PAD, int NT, int VW>
 struct TileLoader {
+    static constexpr bool V4 = VW == 4;
+    static constexpr int kPieces = 4 / VW;   // loads per slot
     static constexpr int kSlotsPerRow = F / 4;
     static constexpr int kTotal = R * F / 4;
     static constexpr int kSlots = (kTotal + NT - 1) / NT;
@@ -97,12 +101,15 @@ struct TileLoader {
     // Fixed slot offsets (bytes within one k slice, kOutOfRange for a lane
     // outside the bound that does not move with k), computed once per
     // workgroup; per slice only the buffer resource changes (SliceOffsets).
-    __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, const unsigned (&off)[kSlots][V4 ? 1 : 4]) {
+    __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, const unsigned (&off)[kSlots][kPieces]) {
 #pragma unroll
         for (int q = 0; q < kSlots; ++q) {
             if (!active(q, threadIdx.x)) continue;
-            if constexpr (V4) {
+            if constexpr (VW == 4) {
                 v[q] = load4(rs, off[q][0]);
+            } else if constexpr (VW == 2) {
+                const f32x2 lo = load2(rs, off[q][0]), hi = load2(rs, off[q][1]);
+                v[q] = f32x4{lo[0], lo[1], hi[0], hi[1]};
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[q][e] = load1(rs, off[q][e]);
@@ -114,15 +121,17 @@ struct TileLoader {
     // slice by the resource's size) and columns f along m or n, valid below
     // lim.  Otherwise tile rows run along m or n, valid below lim, and
     // columns along k (whole slices only).
-    static __device__ __forceinline__ void offsets(unsigned (&off)[kSlots][V4 ? 1 : 4], int tid, bool kslow,
+    // With VW = 2 a pair is in or out as a whole (lim is even: the planner
+    // checks the extent).
+    static __device__ __forceinline__ void offsets(unsigned (&off)[kSlots][kPieces], int tid, bool kslow,
                                                    unsigned lim, unsigned s_r, unsigned s_f) {
 #pragma unroll
         for (int q = 0; q < kSlots; ++q) {
             const int s = tid + q * NT;
             const unsigned r = unsigned(s / kSlotsPerRow), f = unsigned(s % kSlotsPerRow) * 4u;
 #pragma unroll
-            for (int e = 0; e < (V4 ? 1 : 4); ++e) {
-                const unsigned fe = f + unsigned(e);
+            for (int e = 0; e < kPieces; ++e) {
+                const unsigned fe = f + unsigned(e * VW);
                 const bool valid = kslow ? fe < lim : r < lim;
                 off[q][e] = valid ? (r * s_r + fe * s_f) * 4u : kOutOfRange;
             }
@@ -194,9 +203,9 @@ constexpr bool kTwoPerSimd = kTiles[T].mf == 16 && 2 * kTiles[T].lds_bytes(AK, B
 // copies: with loads from fixed addresses it ran at 97% of peak, with the
 // per-slice arithmetic kept and the loads pointed at a 16 KB window at 92%,
 // like the unchanged kernel).
-template <int T, bool AK, bool BKF, bool AV4, bool BV4, bool FX>
+template <int T, bool AK, bool BKF, int AW, int BW, bool FX>
 __global__ __launch_bounds__(kTiles[T].wgm * kTiles[T].wgn * 64)
-__attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTwoPerSimd<T, AK, BKF> ? 2 : 1))) void sgemm_mfma(MfmaArgs p) {
+__attribute__((amdgpu_waves_per_eu(AW == 4 && BW == 4 && kTwoPerSimd<T, AK, BKF> ? 2 : 1))) void sgemm_mfma(MfmaArgs p) {
     constexpr TileCfg cfg = kTiles[T];
     constexpr int BM = cfg.bm, BN = cfg.bn, BK = cfg.bk, MF = cfg.mf;
     constexpr int NT = cfg.wgm * cfg.wgn * 64;
@@ -238,9 +247,10 @@ __attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTwoPerSimd<T, AK, BKF> ? 2 : 1
     const unsigned sAm = unsigned(p.sA_m), sAk = unsigned(p.sA_k);
     const unsigned sBk = unsigned(p.sB_k), sBn = unsigned(p.sB_n);
 
-    using LoaderA = TileLoader<A_R, A_F, A_PAD, NT, AV4>;
-    using LoaderB = TileLoader<B_R, B_F, B_PAD, NT, BV4>;
-    unsigned offA[FX ? LoaderA::kSlots : 1][AV4 ? 1 : 4], offB[FX ? LoaderB::kSlots : 1][BV4 ? 1 : 4];
+    using LoaderA = TileLoader<A_R, A_F, A_PAD, NT, AW>;
+    using LoaderB = TileLoader<B_R, B_F, B_PAD, NT, BW>;
+    static_assert(FX || (AW != 2 && BW != 2), "8-byte loads need fixed offsets");
+    unsigned offA[FX ? LoaderA::kSlots : 1][LoaderA::kPieces], offB[FX ? LoaderB::kSlots : 1][LoaderB::kPieces];
     if constexpr (FX) {
         LoaderA::offsets(offA, tid, !AK, m_left, AK ? sAm : sAk, AK ? sAk : sAm);
         LoaderB::offsets(offB, tid, !BKF, n_left, BKF ? sBn : sBk, BKF ? sBk : sBn);
@@ -376,7 +386,7 @@ __attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTwoPerSimd<T, AK, BKF> ? 2 : 1
     // per slice) the slice's global loads and LDS writes.
     constexpr int kFragReads = (A_IL ? 4 : AK ? TM : 4 * TM) + (B_IL ? 4 : BKF ? TN : 4 * TN);
     constexpr int kProducts = 4 * TM * TN;
-    constexpr int kGlobalLoads = LoaderA::kSlots * (AV4 ? 1 : 4) + LoaderB::kSlots * (BV4 ? 1 : 4);
+    constexpr int kGlobalLoads = LoaderA::kSlots * LoaderA::kPieces + LoaderB::kSlots * LoaderB::kPieces;
     constexpr int kLdsWrites = LoaderA::kSlots + LoaderB::kSlots;
     // Spacing in products: the fragment reads spread over the first 3/8 of
     // the group's products, the LDS writes over half of them (measured
@@ -389,7 +399,7 @@ __attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTwoPerSimd<T, AK, BKF> ? 2 : 1
     // the barrier's wait for them overlaps the loads rather than following
     // the group's last product (linear layer dW 105.6 -> 100.6 us, dX 88.1 ->
     // 86.7; with single-float loads of B, as in the spectrogram, 2% slower).
-    constexpr bool kWritesFirst = G == 2 && kProducts <= 16 && AV4 && BV4;
+    constexpr bool kWritesFirst = G == 2 && kProducts <= 16 && AW == 4 && BW == 4;
 
     const int KT = (p.k + BK - 1) / BK;
     if (KT > 0) {
@@ -608,7 +618,7 @@ __attribute__((amdgpu_waves_per_eu(AV4 && BV4 && kTwoPerSimd<T, AK, BKF> ? 2 : 1
 
 // Launch-table rows for one tile: every (A fast axis, B fast axis, A load
 // width, B load width) combination.
-template <int T, bool AK, bool BKF, bool AV4, bool BV4, bool FX>
+template <int T, bool AK, bool BKF, int AW, int BW, bool FX>
 void launch_mfma(const MfmaArgs &a, unsigned grid, hipStream_t s) {
     constexpr TileCfg cfg = kTiles[T];
     constexpr int nt = cfg.wgm * cfg.wgn * 64;
@@ -616,29 +626,36 @@ void launch_mfma(const MfmaArgs &a, unsigned grid, hipStream_t s) {
     const int lds = cfg.lds_bytes(AK, BKF, slices);
     // Allow this kernel the largest dynamic LDS any of its launches asks for.
     static std::atomic<unsigned long long> lds_set{0};
-    allow_dynamic_lds(reinterpret_cast<const void *>(&sgemm_mfma<T, AK, BKF, AV4, BV4, FX>),
+    allow_dynamic_lds(reinterpret_cast<const void *>(&sgemm_mfma<T, AK, BKF, AW, BW, FX>),
                       cfg.lds_bytes(AK, BKF, 2), lds_set);
-    hipLaunchKernelGGL((sgemm_mfma<T, AK, BKF, AV4, BV4, FX>), dim3(grid), dim3(nt), lds, s, a);
+    hipLaunchKernelGGL((sgemm_mfma<T, AK, BKF, AW, BW, FX>), dim3(grid), dim3(nt), lds, s, a);
 }
 
-template <int T, bool AK, bool BKF, bool FX>
+// Launch-table row of one layout: load widths 1 and 4 with the per-slice
+// loader; 1, 2 and 4 with fixed offsets.
+template <int T, bool AK, bool BKF>
 void fill_layout(MfmaTable &tab) {
-    tab.f[T][AK][BKF][0][0][FX] = launch_mfma<T, AK, BKF, false, false, FX>;
-    tab.f[T][AK][BKF][0][1][FX] = launch_mfma<T, AK, BKF, false, true, FX>;
-    tab.f[T][AK][BKF][1][0][FX] = launch_mfma<T, AK, BKF, true, false, FX>;
-    tab.f[T][AK][BKF][1][1][FX] = launch_mfma<T, AK, BKF, true, true, FX>;
+    tab.f[T][AK][BKF][0][0][0] = launch_mfma<T, AK, BKF, 1, 1, false>;
+    tab.f[T][AK][BKF][0][2][0] = launch_mfma<T, AK, BKF, 1, 4, false>;
+    tab.f[T][AK][BKF][2][0][0] = launch_mfma<T, AK, BKF, 4, 1, false>;
+    tab.f[T][AK][BKF][2][2][0] = launch_mfma<T, AK, BKF, 4, 4, false>;
+    tab.f[T][AK][BKF][0][0][1] = launch_mfma<T, AK, BKF, 1, 1, true>;
+    tab.f[T][AK][BKF][0][1][1] = launch_mfma<T, AK, BKF, 1, 2, true>;
+    tab.f[T][AK][BKF][0][2][1] = launch_mfma<T, AK, BKF, 1, 4, true>;
+    tab.f[T][AK][BKF][1][0][1] = launch_mfma<T, AK, BKF, 2, 1, true>;
+    tab.f[T][AK][BKF][1][1][1] = launch_mfma<T, AK, BKF, 2, 2, true>;
+    tab.f[T][AK][BKF][1][2][1] = launch_mfma<T, AK, BKF, 2, 4, true>;
+    tab.f[T][AK][BKF][2][0][1] = launch_mfma<T, AK, BKF, 4, 1, true>;
+    tab.f[T][AK][BKF][2][1][1] = launch_mfma<T, AK, BKF, 4, 2, true>;
+    tab.f[T][AK][BKF][2][2][1] = launch_mfma<T, AK, BKF, 4, 4, true>;
 }
 
 template <int T>
 void fill_tile(MfmaTable &tab) {
-    fill_layout<T, false, false, false>(tab);
-    fill_layout<T, false, true, false>(tab);
-    fill_layout<T, true, false, false>(tab);
-    fill_layout<T, true, true, false>(tab);
-    fill_layout<T, false, false, true>(tab);
-    fill_layout<T, false, true, true>(tab);
-    fill_layout<T, true, false, true>(tab);
-    fill_layout<T, true, true, true>(tab);
+    fill_layout<T, false, false>(tab);
+    fill_layout<T, false, true>(tab);
+    fill_layout<T, true, false>(tab);
+    fill_layout<T, true, true>(tab);
 }
 
 }  // namespace sgemm

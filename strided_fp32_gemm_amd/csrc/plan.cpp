@@ -26,11 +26,11 @@ namespace {
 int vector_width(uintptr_t base, int64_t fast_stride, int64_t fast_extent,
                  int64_t slow_stride, int64_t batch_stride, int64_t batch) {
     if (fast_stride != 1) return 1;
-    if (fast_extent % 4) return 1;
-    if (base % 16) return 1;
-    if (slow_stride % 4) return 1;
-    if (batch > 1 && batch_stride % 4) return 1;
-    return 4;
+    for (int w : {4, 2}) {
+        if (fast_extent % w || base % (4 * w) || slow_stride % w || (batch > 1 && batch_stride % w)) continue;
+        return w;
+    }
+    return 1;
 }
 
 // Which axis of a rows x cols operand is contiguous: returns true if the
@@ -312,8 +312,8 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
     p.vec_b = p.b_kfast ? vector_width(p.B, p.sB_k, p.k, p.sB_n, p.sB_b, p.batch)
                         : vector_width(p.B, p.sB_n, p.n, p.sB_k, p.sB_b, p.batch);
     // The inner batch stride moves every tile base as well.
-    if (p.sA_i % 4) p.vec_a = 1;
-    if (p.sB_i % 4) p.vec_b = 1;
+    while (p.vec_a > 1 && p.sA_i % p.vec_a) p.vec_a /= 2;
+    while (p.vec_b > 1 && p.sB_i % p.vec_b) p.vec_b /= 2;
 
     p.c_vec4 = p.sC_n == 1 && p.n % 4 == 0 && p.C % 16 == 0 && p.sC_m % 4 == 0 &&
                (p.batch == 1 || p.sC_b % 4 == 0) && p.sC_i % 4 == 0;
@@ -429,6 +429,12 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         p.workgroups = std::min<int64_t>(tiles, 65536);
         p.kernel_name = std::string("generic_t64x64") + (p.accumulate ? "_acc" : "") +
                         (p.row_add || p.col_add ? "_vec" : "");
+    }
+    // 8-byte loads exist only in the LDS-tiled kernel with fixed offsets;
+    // every other kernel reads such an operand element by element.
+    if (p.family != Family::Mfma || p.persist || p.strip || !p.fixed_offsets) {
+        if (p.vec_a == 2) p.vec_a = 1;
+        if (p.vec_b == 2) p.vec_b = 1;
     }
     return kOk;
 }

@@ -116,13 +116,14 @@ def _cfg_plan(name):
     ("linear_xWt", "mfma", 1, 1, 4),
     ("attn_qk", "mfma", 1, 1, 4),
     ("attn_pv", "mfma", 1, 0, 4),
-    ("spectrogram", "mfma", 1, 0, 1),
+    ("spectrogram", "mfma", 1, 0, 2),
     ("square4096_acc", "mfma", 0, 0, 4),
 ])
 def test_workload_plans(name, path, a_kfast, b_kfast, vec_b):
     """Each workload reaches the matrix-core family with the loader its
     layout calls for (the four transpose cases map to k-fast or m/n-fast
-    loaders; the spectrogram basis rows of 514 floats are read element-wise)."""
+    loaders; the spectrogram basis rows of 514 floats are 8-byte aligned and
+    read 8 bytes at a time)."""
     p = _cfg_plan(name)
     assert p["path_name"] == path, p
     assert (p["a_kfast"], p["b_kfast"], p["vec_b"]) == (a_kfast, b_kfast, vec_b), p
@@ -155,9 +156,17 @@ def test_vector_width_follows_alignment():
     # Misaligned base pointer (4 bytes past 16-byte alignment) forces scalar loads.
     p = plan(1, 128, 128, 128, (0, 128, 1), (0, 128, 1), (0, 128, 1), ptrs=(PA + 4, PB, PC))
     assert p["vec_a"] == 1 and p["vec_b"] == 4
-    # Fast extent not a multiple of 4: element loads.
+    # Fast extent and row stride even but not multiples of 4: 8-byte loads
+    # (LDS-tiled kernel with fixed offsets only), odd: element loads.
     p = plan(1, 128, 130, 128, (0, 128, 1), (0, 130, 1), (0, 130, 1))
+    assert p["vec_b"] == 2 and p["fixed_offsets"] == 1
+    p = plan(1, 128, 130, 128, (0, 128, 1), (0, 130, 1), (0, 130, 1), path=sg.PATH_WAVE)
     assert p["vec_b"] == 1
+    p = plan(1, 128, 131, 128, (0, 128, 1), (0, 131, 1), (0, 131, 1))
+    assert p["vec_b"] == 1
+    # A misaligned by 8 bytes: 8-byte loads of A.
+    p = plan(1, 128, 128, 128, (0, 128, 1), (0, 128, 1), (0, 128, 1), ptrs=(PA + 8, PB, PC))
+    assert p["vec_a"] == 2
     # Neither stride 1: element loads along the smaller stride.
     p = plan(1, 64, 64, 64, (0, 128, 2), (0, 64, 1), (0, 64, 1))
     assert p["vec_a"] == 1

@@ -206,6 +206,31 @@ def test_every_tile(tile, monkeypatch):
                 assert e <= TOL, (tile, m, n, k, pad, a_major, b_major, acc, e)
 
 
+@pytest.mark.parametrize("tile", [t for t in TILE_NAMES if t.startswith("t")])
+def test_every_tile_8byte_loads(tile, monkeypatch):
+    """Each LDS-tiled configuration, forced, with operands whose rows are
+    8- but not 16-byte aligned (row strides 2 more than a multiple of 4, even
+    extents): the fixed-offset loader reads them 8 bytes at a time, in all
+    four transpose cases, with whole k slices and (when both operands run
+    across k) a ragged last slice bounded by the buffer size."""
+    monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+    shapes = [(2, 130, 146, 96), (1, 66, 210, 64), (3, 98, 70, 130), (2, 34, 514, 32)]
+    widths = set()
+    for batch, m, n, k in shapes:
+        for a_major, b_major in LAYOUTS:
+            for acc in (False, True):
+                p = wl.random_problem(3 * m + n + k, batch, m, n, k, a_major=a_major, b_major=b_major,
+                                      dist="normal", alpha=0.75, accumulate=acc, pad=2)
+                info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
+                assert tile in info["kernel"], info
+                if info["fixed_offsets"]:
+                    widths.update((info["vec_a"], info["vec_b"]))
+                got, ref = out(p, gpu_call(p)), out(p, oracle_call(p))
+                e = err_ratio(p, got, ref)
+                assert e <= TOL, (tile, m, n, k, a_major, b_major, acc, info["vec_a"], info["vec_b"], e)
+    assert 2 in widths, widths
+
+
 @pytest.mark.parametrize("tile", ["p64x64k64", "p128x64k64", "p64x128k64"])
 @pytest.mark.parametrize("wgs", [None, "8", "7", "1"])
 def test_persistent_tile(tile, wgs, monkeypatch):
