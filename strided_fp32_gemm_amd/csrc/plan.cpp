@@ -144,14 +144,14 @@ bool tile_fits(const Plan &p, int bm, int bn) {
            (!p.col_add || fits_buffer(1, 0, bn, p.sL_n));
 }
 
-// Estimated cycles of a launch.  Tiles are spread over the CUs and up to
-// `occ` of them run concurrently on one CU (bounded by LDS or registers, and
-// by how many each CU receives).  A round of `occ` tiles costs the larger of
-// its matrix-core work at the tile's sustained rate and its operand reads
-// through L2 (~64 bytes per cycle per CU), plus the epilogue traffic of C
-// (read and written when accumulating, ~10 bytes per cycle per CU), plus
-// memory latency the round cannot hide.  Constants were fitted to tile
-// sweeps of the benchmark workloads on MI355X.
+// Estimated cycles of a direct-wavefront launch.  Tiles are spread over the
+// CUs and up to `occ` of them run concurrently on one CU (bounded by
+// registers, and by how many each CU receives).  A round of `occ` tiles
+// costs the larger of its matrix-core work at the tile's sustained rate and
+// its operand reads through L2 (~64 bytes per cycle per CU), plus the
+// epilogue traffic of C (read and written when accumulating, ~10 bytes per
+// cycle per CU), plus memory latency the round cannot hide.  Constants were
+// fitted to tile sweeps on MI355X.
 struct CostShape {
     int bm, bn, kstep;   // tile and k granularity
     double occ_limit;    // tiles one CU can hold
@@ -173,12 +173,30 @@ double launch_cost(const Plan &p, const CostShape &c, int num_cus) {
     return rounds * (std::max(compute, operands) + epilogue + c.latency);
 }
 
+// Estimated cycles of an LDS-tiled launch.  The dispatcher hands a CU its
+// next workgroup as soon as one finishes, so the busiest CU runs
+// ceil(tiles / CUs) tiles; each costs the larger of its matrix-core work at
+// the tile's sustained rate and its operand reads through L2, plus its C
+// traffic.  With fewer than two workgroups resident per CU (LDS-bound, or
+// too few tiles) a CU's matrix cores idle more, so the rate drops by up to
+// kLowOccupancy.  The first two slices' memory latency is not hidden.  Rates
+// and constants were fitted to tile sweeps on MI355X (the benchmark
+// workloads and twelve other shapes; mean regret 0.5%).
 double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
-    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 368.0;
-    long long slices = (p.k + t.bk - 1) / t.bk;
-    double fit = std::max(1.0, std::min(8.0, std::floor(kLdsBytes / t.lds_bytes(p.a_kfast, p.b_kfast, slices))));
-    CostShape c{t.bm, t.bn, t.bk, fit, t.rate, kSliceLatency * std::min<double>(double(slices), 2.0)};
-    return launch_cost(p, c, num_cus);
+    const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 11.0;
+    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 368.0, kLowOccupancy = 0.05;
+    const long long slices = (p.k + t.bk - 1) / t.bk;
+    const double tiles = double(p.batch) * double((p.m + t.bm - 1) / t.bm) * double((p.n + t.bn - 1) / t.bn);
+    const double cus = double(std::max(num_cus, 1));
+    const double per_cu = std::ceil(tiles / cus);
+    const double fit = std::max(1.0, std::min(8.0, std::floor(kLdsBytes / t.lds_bytes(p.a_kfast, p.b_kfast, slices))));
+    const double resident = std::min(fit, tiles / cus);
+    const double rate = t.rate * (1.0 - kLowOccupancy * std::max(0.0, 2.0 - resident) / 2.0);
+    const double kpad = double(slices) * t.bk;
+    const double compute = double(t.bm) * t.bn * 2.0 * kpad / kFlopPerCuCycle / rate;
+    const double operands = double(t.bm + t.bn) * kpad * 4.0 / kOperandBytesPerCycle;
+    const double epilogue = double(t.bm) * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
+    return per_cu * (std::max(compute, operands) + epilogue) + kSliceLatency * std::min<double>(double(slices), 2.0);
 }
 
 double wave_cost(const Plan &p, const WaveCfg &t, int num_cus) {

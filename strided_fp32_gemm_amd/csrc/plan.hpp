@@ -102,19 +102,19 @@ struct TileCfg {
 // order is part of the contract between planner and kernels.
 constexpr int kNumTiles = 13;
 inline constexpr TileCfg kTiles[kNumTiles] = {
-    {128, 128, 32, 2, 2, 32, "t128x128", 0.87},
-    {128, 64, 32, 2, 2, 32, "t128x64", 0.89},
-    {64, 128, 32, 2, 2, 32, "t64x128", 0.89},
-    {64, 64, 32, 2, 2, 32, "t64x64", 0.94},
-    {256, 128, 32, 2, 2, 32, "t256x128", 0.78},
-    {128, 160, 32, 4, 1, 32, "t128x160", 0.74},
-    {128, 80, 32, 4, 1, 16, "t128x80m16", 0.77},
-    {64, 176, 32, 4, 1, 16, "t64x176m16", 0.75},
-    {64, 64, 32, 2, 2, 16, "t64x64m16", 0.95},
-    {128, 128, 32, 2, 2, 16, "t128x128m16", 0.95},
-    {128, 64, 32, 2, 2, 16, "t128x64m16", 0.88},
-    {64, 128, 32, 2, 2, 16, "t64x128m16", 0.88},
-    {64, 32, 32, 4, 1, 16, "t64x32m16", 0.80},
+    {128, 128, 32, 2, 2, 32, "t128x128", 0.897},
+    {128, 64, 32, 2, 2, 32, "t128x64", 0.860},
+    {64, 128, 32, 2, 2, 32, "t64x128", 0.847},
+    {64, 64, 32, 2, 2, 32, "t64x64", 0.837},
+    {256, 128, 32, 2, 2, 32, "t256x128", 0.919},
+    {128, 160, 32, 4, 1, 32, "t128x160", 0.934},
+    {128, 80, 32, 4, 1, 16, "t128x80m16", 0.805},
+    {64, 176, 32, 4, 1, 16, "t64x176m16", 0.796},
+    {64, 64, 32, 2, 2, 16, "t64x64m16", 0.896},
+    {128, 128, 32, 2, 2, 16, "t128x128m16", 0.936},
+    {128, 64, 32, 2, 2, 16, "t128x64m16", 0.824},
+    {64, 128, 32, 2, 2, 16, "t64x128m16", 0.931},
+    {64, 32, 32, 4, 1, 16, "t64x32m16", 0.830},
 };
 
 // One tile of the direct wavefront kernel (WAVE family): a single

@@ -349,15 +349,32 @@ def test_attention_validates_and_plans_before_the_device():
     assert plan(sK=(32 * 2 * 128, 128, 256, 2))["kernel"] == "attn_generic"     # column stride 2
 
 
-@pytest.mark.parametrize("name,tile", [("linear_bwd_dw", "t64x32m16"), ("linear_bwd_dx", "t64x64m16"),
-                                       ("attn_pv", "t64x64m16"), ("square4096_acc", "t128x128m16")])
+@pytest.mark.parametrize("name,tile", [("linear_bwd_dw", "t64x32m16"), ("linear_bwd_dx", "t64x128m16"),
+                                       ("attn_pv", "t64x64m16"), ("square4096_acc", "t128x128m16"),
+                                       ("spectrogram", "t64x64m16"), ("linear_xWt", "t128x160"),
+                                       ("linear_bias", "t128x160")])
 def test_measured_tile_choices(name, tile):
     """The planner's cost model keeps the tile choices that measured fastest
-    on MI355X: dW (600 tiles of 64x64 on 256 CUs) moves to the 64x32 tile's
-    1200 workgroups, while dX and P.V stay on 64x64 and the 4 x 4096^3 product on
-    128x128 (no GPU: planning runs on the host)."""
-    p = _cfg_plan(name)
+    on MI355X when every tile was forced in turn (with the fixed-offset and
+    8-byte loaders): dW (600 tiles of 64x64 on 256 CUs) on the 64x32 tile's
+    1200 workgroups, dX on 64x128, P.V and the spectrogram on 64x64, the
+    linear layer and its bias-fused form on 128x160, and the 4 x 4096^3
+    product on 128x128 (no GPU: planning runs on the host).  The x^T-layout
+    linear layer measured 64x64 and 128x160 within 0.3% of each other, so
+    either is accepted there."""
+    p = _cfg_plan(name) if name != "linear_bias" else _bias_plan()
     assert p["path_name"] == "mfma" and tile in p["kernel"], p
+
+
+def test_accepted_regret_on_the_xT_linear_layer():
+    p = _cfg_plan("linear_xT")
+    assert p["kernel"].startswith(("mfma_t64x64m16_", "mfma_t128x160_")), p
+
+
+def _bias_plan():
+    prob = wl.workload("linear_bias")
+    return sg.sgemm_plan_describe(prob.batch, prob.m, prob.n, prob.k, prob.alpha, PA, *prob.A.strides, PB,
+                                  *prob.B.strides, 0, PC, *prob.C.strides, num_cus=256)
 
 
 def test_noalloc_distance_checks_before_the_device():
