@@ -19,9 +19,10 @@ The JSON line carries:
   roofline   the dominant (only) kernel: algorithmic FLOPs per launch divided
              by its mean launch duration from HIP events recorded on the
              launch stream, against the MI355X dense fp32 matrix peak
-             (157.3 TFLOP/s); `traffic` is the HBM bytes per launch measured
-             by rocprofv3 counters, when a committed record for the current
-             kernel sources exists, else null; `achieved_tb_per_s` is the
+             (157.3 TFLOP/s); `traffic` (HBM bytes per launch) and
+             `mfma_busy` (matrix-core busy fraction) come from the committed
+             rocprofv3 counter record when it was taken on the current
+             library sources, else null; `achieved_tb_per_s` is the
              algorithmic bytes per launch over the same mean duration
   cpu_baseline  the CPU oracle timed on a bounded slice of the same workload
              (a block of rows of batch 0), as TFLOP/s, with its thread count,
@@ -79,12 +80,13 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def traffic_record(workload: str, kernel: str):
-    """HBM bytes per launch from the committed counter summary of this
-    kernel and workload, if it was taken on the current kernel sources."""
+def counter_record(workload: str, kernel: str) -> dict:
+    """HBM bytes per launch and the matrix-core busy fraction from the
+    committed counter summary of this kernel and workload, if it was taken
+    on the current library sources (else an empty dict)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
     if not os.path.exists(path):
-        return None
+        return {}
     rec = {}
     with open(path) as f:
         for line in f:
@@ -92,11 +94,14 @@ def traffic_record(workload: str, kernel: str):
                 key, _, val = line.partition(":")
                 rec[key.strip("-* `").strip()] = val.strip().strip("`")
     if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
-        return None
-    try:
-        return float(rec["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return {}
+    out = {}
+    for key, name in (("hbm_bytes_per_launch", "traffic"), ("mfma_busy", "mfma_busy")):
+        try:
+            out[name] = float(rec[key])
+        except (KeyError, ValueError):
+            pass
+    return out
 
 
 def cpu_model() -> str:
@@ -351,7 +356,7 @@ def bench_one(name: str, steps: int, warmup, cpu_seconds: float) -> dict:
     flops = float(p.flops)
     value = flops * steps / wall / 1e12
     achieved = flops / (mean_ms * 1e-3) / 1e12
-    traffic = traffic_record(name, info["kernel"])
+    counters = counter_record(name, info["kernel"])
     alg_bytes = wl.algorithmic_bytes(p)
     line = {
         "metric": METRIC,
@@ -374,7 +379,8 @@ def bench_one(name: str, steps: int, warmup, cpu_seconds: float) -> dict:
             "peak": PEAK_FP32_MATRIX_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
-            "traffic": traffic,
+            "traffic": counters.get("traffic"),
+            "mfma_busy": counters.get("mfma_busy"),
             "algorithmic_bytes": alg_bytes,
             "achieved_tb_per_s": round(alg_bytes / (mean_ms * 1e-3) / 1e12, 3),
             "kernel": info["kernel"],
