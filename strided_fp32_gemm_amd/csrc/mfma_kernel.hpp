@@ -534,6 +534,14 @@ __attribute__((amdgpu_waves_per_eu(AW == 4 && BW == 4 && kTwoPerSimd<T, AK, BKF>
                 for (int r = 0; r < R; ++r)
                     *reinterpret_cast<f32x4 *>(stage + arow_w(a, M::row(r, lh)) * E_LD + bcol_w(0, lr)) =
                         f32x4{acc[a][0][r], acc[a][1][r], acc[a][2][r], acc[a][3][r]};
+        } else if constexpr (B_IL && TN == 2) {
+            // The 2 blocks of a row hold 2 adjacent columns: one 8-byte write.
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    *reinterpret_cast<f32x2 *>(stage + arow_w(a, M::row(r, lh)) * E_LD + bcol_w(0, lr)) =
+                        f32x2{acc[a][0][r], acc[a][1][r]};
         } else {
 #pragma unroll
             for (int a = 0; a < TM; ++a)

@@ -78,15 +78,17 @@ struct TileCfg {
     // its (bm/wgm) x (bn/wgn) sub-tile of C before storing whole rows.  The
     // row stores read it back with 16-byte LDS reads, 16 lanes per cycle in
     // the groups above; with rows of 32 or 64 floats and no padding those
-    // groups cover 64 distinct banks.  The accumulators go in with 16-byte
-    // writes (four 16-wide blocks side by side: n-fast B tile with 4 blocks)
-    // or, on 32-wide blocks, with single-float writes of 32 consecutive
-    // columns: both free of conflicts at that pitch.  The single-float writes
-    // of the other 16-wide-block tiles put lane quarters 4 rows apart in one
-    // 32-lane cycle, so their rows keep 4 floats of padding.
+    // groups cover 64 distinct banks.  The accumulators go in with 16- or
+    // 8-byte writes (four or two 16-wide blocks side by side: an n-fast B
+    // tile with 4 or 2 blocks per wavefront; 8 and 16 consecutive lanes per
+    // cycle, all on one row) or, on 32-wide blocks, with single-float writes
+    // of 32 consecutive columns: all free of conflicts at that pitch.  The
+    // single-float writes of the other 16-wide-block tiles put lane quarters
+    // 4 rows apart in one 32-lane cycle, so their rows keep 4 floats of
+    // padding.
     constexpr int epi_pitch(bool b_kfast) const {
         const int wn = bn / wgn;
-        return (mf == 32 || (!b_kfast && b_blocks() == 4)) ? wn : wn + 4;
+        return (mf == 32 || (!b_kfast && (b_blocks() == 4 || b_blocks() == 2))) ? wn : wn + 4;
     }
     // LDS bytes of the staged epilogue: every wavefront's sub-tile of C.
     constexpr int epilogue_lds_bytes(bool b_kfast) const { return 4 * waves() * (bm / wgm) * epi_pitch(b_kfast); }

@@ -76,7 +76,7 @@ static void check_split(int64_t inner, int64_t gA, int64_t gB, uint32_t b) {
 // (measured per lane pair with the bank-conflict counter): 16-byte reads in four groups of 16,
 // 8- and 4-byte reads in halves of 32, 16-byte writes in runs of 8.  Two lanes of one group
 // conflict when they touch the same bank at different addresses.
-enum class Op { Read16, Read8, Read4, Write16, Write4 };
+enum class Op { Read16, Read8, Read4, Write16, Write8, Write4 };
 
 static int lane_group(Op op, int lane) {
     switch (op) {
@@ -89,13 +89,14 @@ static int lane_group(Op op, int lane) {
         case Op::Read4:
         case Op::Write4: return lane >> 5;
         case Op::Write16: return lane >> 3;
+        case Op::Write8: return lane >> 4;
     }
     return 0;
 }
 
 // Extra cycles one instruction spends on conflicts; addr[l] < 0 marks an idle lane.
 static int conflict_cycles(Op op, const long long addr[64]) {
-    const int width = (op == Op::Read4 || op == Op::Write4) ? 1 : op == Op::Read8 ? 2 : 4;
+    const int width = (op == Op::Read4 || op == Op::Write4) ? 1 : (op == Op::Read8 || op == Op::Write8) ? 2 : 4;
     int extra = 0;
     for (int g = 0; g < 8; ++g) {
         std::vector<long long> bank[64];
@@ -166,7 +167,7 @@ static void check_tiled_reads(const TileCfg &t, int layout, bool kfast, int bloc
 // Staged epilogue of the LDS-tiled kernel for one wavefront: the accumulators written at
 // (row of register r of block a, column of block c), then read back 16 bytes per lane along
 // whole rows.  Checked where the pitch has no padding (epi_pitch): 32-wide blocks, and 16-wide
-// blocks written 16 bytes at a time (an n-fast B tile with 4 blocks per wavefront).
+// blocks written 16 or 8 bytes at a time (an n-fast B tile with 4 or 2 blocks per wavefront).
 static void check_epilogue(const TileCfg &t, int layout, bool a_kfast, bool b_kfast) {
     const int wm = t.bm / t.wgm, wn = t.bn / t.wgn, mf = t.mf, tm = wm / mf, tn = wn / mf;
     const int ld = t.epi_pitch(b_kfast);
@@ -178,11 +179,12 @@ static void check_epilogue(const TileCfg &t, int layout, bool a_kfast, bool b_kf
     auto mrow = [&](int r, int lh) { return mf == 32 ? 8 * (r >> 2) + 4 * lh + (r & 3) : 4 * lh + r; };
     const int regs = mf == 32 ? 16 : 4;
     long long addr[64];
+    const Op wop = b_il && tn == 4 ? Op::Write16 : b_il && tn == 2 ? Op::Write8 : Op::Write4;
     for (int a = 0; a < tm; ++a)
-        for (int c = 0; c < (b_il && tn == 4 ? 1 : tn); ++c)
+        for (int c = 0; c < (b_il ? 1 : tn); ++c)
             for (int r = 0; r < regs; ++r) {
                 for (int l = 0; l < 64; ++l) addr[l] = (long long)arow(a, mrow(r, l / mf)) * ld + bcol(c, l % mf);
-                expect_free("epilogue write", t.name, layout, b_il && tn == 4 ? Op::Write16 : Op::Write4, addr);
+                expect_free("epilogue write", t.name, layout, wop, addr);
             }
     const int per_row = wn / 4;
     for (int i = 0; i < wm * wn / 4 / 64; ++i) {
