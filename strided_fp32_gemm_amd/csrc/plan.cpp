@@ -428,9 +428,13 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
             // one read across k (tile rows along k) needs rows that do not
             // overlap, so that a row index past K means an offset past the
             // resource's end.
+            // The size is formed in 32 bits from at most one slice of rows, so
+            // that slice must stay below 2 GiB (it can exceed it only through
+            // the stride of a k extent of 1, which otherwise never matters).
             const int64_t bk = kTiles[best].bk;
             auto bounded = [&](bool kfast, int64_t extent, int64_t s_fast, int64_t s_k) {
-                return kfast ? p.k % bk == 0 : (extent - 1) * s_fast < s_k;
+                return kfast ? p.k % bk == 0
+                             : (extent - 1) * s_fast < s_k && std::min(p.k, bk) * s_k * 4 < kBufferLimit;
             };
             p.fixed_offsets = bounded(p.a_kfast, p.m, p.sA_m, p.sA_k) && bounded(p.b_kfast, p.n, p.sB_n, p.sB_k);
         }

@@ -415,5 +415,8 @@ def test_fixed_offsets_where_the_buffer_size_bounds_k():
                 path=mfma)["fixed_offsets"] == 1
     # k-slow B whose rows overlap (row stride 64 < 128 columns): per slice.
     assert plan(1, 128, 128, 96, (0, 96, 1), (0, 64, 1), (0, 128, 1), path=mfma)["fixed_offsets"] == 0
+    # k = 1 with a k stride whose one-slice size would pass 2 GiB (the stride of
+    # an extent-1 axis is otherwise irrelevant): per slice.
+    assert plan(1, 128, 128, 1, (0, 1, 1 << 30), (0, 128, 1), (0, 128, 1), path=mfma)["fixed_offsets"] == 0
     # Other kernel families never use it.
     assert plan(1, 100, 90, 70, (0, 70, 1), (0, 90, 1), (0, 90, 1), path=sg.PATH_WAVE)["fixed_offsets"] == 0

@@ -388,6 +388,29 @@ def test_offsets_beyond_32_bits():
         torch.cuda.empty_cache()
 
 
+def test_k1_with_huge_k_stride():
+    """k = 1 with a k stride of 2^30 floats on A, B or both (irrelevant for a
+    single k row, and past what the fixed-offset loader's 32-bit buffer size
+    can hold): every family gives the oracle's result, bit for bit (alpha 1:
+    each output is one product, rounded once on both sides)."""
+    rng = np.random.default_rng(1301)
+    m, n = 130, 70
+    A = rng.standard_normal(m).astype(np.float32)
+    B = rng.standard_normal(n).astype(np.float32)
+    huge = 1 << 30
+    for sA, sB in (((0, 1, huge), (0, huge, 1)), ((0, 1, huge), (0, n, 1)), ((0, 1, m), (0, huge, 1))):
+        for path in FAMILIES:
+            dA, dB = dev(A), dev(B)
+            dC = torch.zeros(m * n, device="cuda")
+            sg.sgemm_strided_batched_path(1, m, n, 1, 1.0, dA, *sA, dB, *sB, 0, dC, 0, n, 1,
+                                          path=path, stream=torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            got = dC.cpu().numpy()
+            ref = np.zeros(m * n, np.float32)
+            oracle.ref_sgemm(1, m, n, 1, 1.0, A, *sA, B, *sB, 0, ref, 0, n, 1)
+            assert np.array_equal(got, ref), (sA, sB, path, float(np.abs(got - ref).max()))
+
+
 def test_determinism_repeated_calls():
     p = wl.random_problem(47, 4, 300, 260, 500, a_major="col", b_major="col", dist="normal")
     first = gpu_call(p)
