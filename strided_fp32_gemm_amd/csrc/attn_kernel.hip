@@ -3,46 +3,67 @@
 // Scores, softmax and the product with V in one pass per query block (the
 // rvllm post, "What's basic about it": a fused kernel keeps the scores out of
 // global memory).  The softmax is the online form of the post's three steps
-// (max, sum of exponentials, divide; "The kernels"): the running maximum and
-// sum are rescaled as each block of keys arrives, and the division happens
-// once at the end.
+// (max, sum of exponentials, divide; "The kernels"): the weights of each
+// block of keys are taken relative to a reference maximum that moves as
+// larger scores arrive, the sums already formed are rescaled when it moves,
+// and the division happens once at the end.
+//
+// On gfx950 the fp32 matrix instructions and ordinary vector instructions
+// share one issue path per SIMD and never run at the same time, so every
+// vector instruction in the key loop adds to the time of the products.  The
+// matrix-core kernel is built around keeping that count small.
 //
 // attn_mfma_d64 (head dimension 64, unit column strides):
 //  - A wavefront owns 16 query rows.  It forms the scores transposed,
 //    S^T = K Q^T, with v_mfma_f32_16x16x4_f32, so lane l holds query l%16 and
 //    16 of its scores in accumulator registers (keys 4*(l/16) + r of each
 //    16-key block).  Those registers are already the B operand of
-//    O^T = V^T P^T, so the probabilities never leave registers, and each lane
-//    ends with 4 consecutive head-dimension outputs of its query per block
-//    (one 16-byte store).
+//    O^T = V^T P^T, so the probabilities never leave registers.
+//  - Q is loaded once, scaled by alpha*log2(e), and the score products start
+//    from minus the row's reference maximum m instead of zero, so they end
+//    as the exponent of each weight, exp2(alpha*log2(e)*s - m), with no
+//    vector work in between.
+//  - The reference maximum moves only when a score exceeds it by more than
+//    kSlack (weights stay below 2^kSlack); the test is one compare and a
+//    wavefront vote, and the rescaling (a lane swap reduction, one exp2,
+//    multiplies of the output and the sum) runs only when the vote says so.
+//    Softmax is invariant to the reference, so this changes no result
+//    beyond rounding.  The first key block sets the reference from its own
+//    row maxima.
+//  - Keys past a query's last visible key (causal, or past the end) are
+//    masked with one compare and select per score, only in the blocks that
+//    hold such keys; every other block skips the test.
+//  - Keys arrive in blocks of 64, K and V staged through double-buffered LDS;
+//    the next block's global loads are in flight while the current one is
+//    multiplied; one barrier per block.  K rows have a pitch of 68 floats
+//    with the 16-byte chunks of rows whose bits 2 and 3 differ swapped in
+//    pairs (chunk c stored at c ^ 4), and V rows a pitch of 64: under
+//    gfx950's LDS lane groups every 16-byte read and write is free of bank
+//    conflicts.  Each lane's LDS addresses are fixed for the whole loop
+//    (immediate offsets), and the global load offsets too (the buffer
+//    resource moves with the block), so the loop spends no vector
+//    instructions on addresses.
+//  - In O^T = V^T P^T, matrix instruction nb takes head dimensions 4i + nb
+//    for its rows i, so a lane's V operands for the four instructions of a
+//    step are four consecutive floats of one V row (one 16-byte LDS read),
+//    and the four accumulators hold, per element e, four consecutive outputs
+//    (16*(l/16) + 4e .. +3) of the lane's query: one 16-byte store each.
 //  - The head-dimension sum of the scores runs in the order d = 16*(l/16) + s
-//    for step s, so each lane reads its 16 K values of a key with four 16-byte
-//    LDS reads.  The key sum of P V follows the score layout.  Both orders are
-//    fixed, so results are reproducible bit for bit.
-//  - Keys arrive in blocks of 64, K and V staged through double-buffered LDS
-//    (row pitch 68 floats: the 4-byte V reads are free of bank conflicts; the
-//    16-byte K reads take two cycles per 16-lane group instead of one, which
-//    no row pitch avoids with this head-dimension order, but LDS time stays a
-//    small fraction of the matrix-core time); the next block's global loads
-//    are in flight while the current one is multiplied; one barrier per block.
-//  - Weights are exp2(s * alpha*log2(e) - running max), with v_exp_f32.  The
-//    row maximum needs two lane swaps per key block (v_permlane16_swap,
-//    v_permlane32_swap: vector instructions, no LDS round trip); the row sum
-//    stays per lane until the end.
+//    for step s, and the key sum of P V follows the score layout.  Both
+//    orders are fixed, so results are reproducible bit for bit.
 //  - Causal: a workgroup pairs an early and a late block of query rows (one
 //    per half of its wavefronts) so that workgroups carry equal work; it
 //    stops at the last key its queries see, and a wavefront skips the blocks
-//    entirely past its own diagonal.  Keys past a
-//    query's last visible key (or past the end) get weight exp2(-inf) = 0
-//    through one compare and select per score.
+//    entirely past its own diagonal.
 //
 // attn_generic: any head dimension up to 256 and any strides, 64-bit
 // addressing; one wavefront per query row, the score of each key summed
-// across the wavefront, the same online softmax.
+// across the wavefront, the online softmax with the exact running maximum.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <string>
+#include <type_traits>
 
 #include "attention.hpp"
 #include "buffer.hpp"
@@ -52,12 +73,15 @@ namespace sgemm {
 
 namespace {
 
-constexpr int kD = 64;                      // head dimension of the matrix-core kernel
-constexpr int kBKV = 64;                    // keys per LDS block
-constexpr int kPitch = kD + 4;              // LDS row pitch (floats)
-constexpr int kTileFloats = kBKV * kPitch;  // one K or V block in LDS
-constexpr int kQW = 16;                     // query rows per wavefront
-constexpr int kLdsBytes = 2 * 2 * kTileFloats * 4;
+constexpr int kD = 64;                            // head dimension of the matrix-core kernel
+constexpr int kBKV = 64;                          // keys per LDS block
+constexpr int kKPitch = kD + 4;                   // K rows in LDS (floats)
+constexpr int kVPitch = kD;                       // V rows in LDS (floats)
+constexpr int kKFloats = kBKV * kKPitch;          // one K block
+constexpr int kBufFloats = kKFloats + kBKV * kVPitch;   // one K block and one V block
+constexpr int kQW = 16;                           // query rows per wavefront
+constexpr int kLdsBytes = 2 * kBufFloats * 4;
+constexpr float kSlack = 8.0f;                    // log2 of the largest weight before the reference moves
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -85,15 +109,21 @@ __device__ __forceinline__ float across_rows(float v, Op op) {
     return op(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
 }
 
+// 16-byte chunk c of K row `key` sits at chunk c ^ k_chunk_flip(key) of its
+// LDS row.
+__device__ __forceinline__ int k_chunk_flip(int key) { return (((key >> 2) ^ (key >> 3)) & 1) << 2; }
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
     constexpr int NT = NW * 64;
     constexpr int BQ = NW * kQW;
     constexpr int SL = kBKV * kD / 4 / NT;   // 16-byte slots per thread per K (or V) block
+    constexpr int SR = NT / 16;              // key rows between a thread's slots
     static_assert(kBKV * kD / 4 % NT == 0, "every thread stages the same number of slots");
     extern __shared__ float lds[];           // [2 buffers][K block, V block]
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lq = lane & 15, lh = lane >> 4;
 
     // Workgroup -> (outer o, inner i, query block qb); KV head kv = i / g.
@@ -127,41 +157,62 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
     const int qrow = qwave + lq;
     const bool qok = wave_on && qrow < tq;
 
+    const float *Kb = p.K + o * p.sK_o + kv * p.sK_i;
+    const float *Vb = p.V + o * p.sV_o + kv * p.sV_i;
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(p.Q + o * p.sQ_o + i * p.sQ_i);
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.K + o * p.sK_o + kv * p.sK_i);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.V + o * p.sV_o + kv * p.sV_i);
     const __amdgpu_buffer_rsrc_t rO = make_rsrc(p.O + o * p.sO_o + i * p.sO_i);
     const unsigned sQr = unsigned(p.sQ_r), sKr = unsigned(p.sK_r), sVr = unsigned(p.sV_r),
                    sOr = unsigned(p.sO_r);
+    const float c2 = p.scale_log2;
 
-    // This lane's Q values: query qrow, head dimensions 16*lh .. 16*lh + 15.
+    // This lane's Q values, scaled by alpha*log2(e): query qrow, head
+    // dimensions 16*lh .. 16*lh + 15.
     f32x4 qf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        qf[j] = load4(rQ, qok ? (unsigned(qrow) * sQr + unsigned(16 * lh + 4 * j)) * 4u : kOutOfRange);
+        qf[j] = c2 * load4(rQ, qok ? (unsigned(qrow) * sQr + unsigned(16 * lh + 4 * j)) * 4u : kOutOfRange);
 
-    // K and V blocks: slot s of a block is key s/16, head dimensions 4*(s%16) .. +3.
+    // Staging: slot u of a block is key row kr + SR*u, head dimensions
+    // 4*c .. 4*c + 3.  Global offsets are relative to the block's first row
+    // (the second slot's distance is a scalar offset), LDS addresses are
+    // fixed per thread.
+    const int kr = tid >> 4, c = tid & 15;
+    const unsigned kgo = (unsigned(kr) * sKr + 4u * unsigned(c)) * 4u;
+    const unsigned vgo = (unsigned(kr) * sVr + 4u * unsigned(c)) * 4u;
+    float *const kwr = lds + kr * kKPitch + 4 * (c ^ k_chunk_flip(kr));
+    float *const vwr = lds + kKFloats + kr * kVPitch + 4 * c;
+    static_assert(SR % 16 == 0, "a thread's slots share the K chunk order");
     f32x4 kst[SL], vst[SL];
     auto issue = [&](int kv0) {
+        const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kb + size_t(kv0) * p.sK_r);
+        const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vb + size_t(kv0) * p.sV_r);
+        const int left = tk - kv0;   // keys of this block that exist
+        if (left >= kBKV) {
 #pragma unroll
-        for (int u = 0; u < SL; ++u) {
-            const int s = tid + u * NT;
-            const int key = kv0 + (s >> 4);
-            const unsigned c = unsigned(s & 15) * 4u;
-            const bool ok = key < tk;
-            kst[u] = load4(rK, ok ? (unsigned(key) * sKr + c) * 4u : kOutOfRange);
-            vst[u] = load4(rV, ok ? (unsigned(key) * sVr + c) * 4u : kOutOfRange);
+            for (int u = 0; u < SL; ++u) {
+                kst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rK, int(kgo), int(unsigned(SR * u) * sKr * 4u), 0));
+                vst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rV, int(vgo), int(unsigned(SR * u) * sVr * 4u), 0));
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < SL; ++u) {
+                // Rows past the end get an offset beyond the resource's range.
+                const unsigned past = unsigned(kr + SR * u >= left) << 31;
+                kst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rK, int(kgo + past), int(unsigned(SR * u) * sKr * 4u), 0));
+                vst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rV, int(vgo + past), int(unsigned(SR * u) * sVr * 4u), 0));
+            }
         }
     };
-    auto put = [&](int buf) {
-        float *Kl = lds + buf * 2 * kTileFloats;
-        float *Vl = Kl + kTileFloats;
+    auto put = [&](auto bufc) {
+        constexpr int off = decltype(bufc)::value * kBufFloats;
 #pragma unroll
         for (int u = 0; u < SL; ++u) {
-            const int s = tid + u * NT;
-            const int at = (s >> 4) * kPitch + (s & 15) * 4;
-            *reinterpret_cast<f32x4 *>(Kl + at) = kst[u];
-            *reinterpret_cast<f32x4 *>(Vl + at) = vst[u];
+            *reinterpret_cast<f32x4 *>(kwr + off + SR * u * kKPitch) = kst[u];
+            *reinterpret_cast<f32x4 *>(vwr + off + SR * u * kVPitch) = vst[u];
         }
     };
 
@@ -169,113 +220,148 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
     if (p.causal) last_key = min(last_key, wg_last_row + shift);
     const int nblocks = last_key / kBKV + 1;
     const int wave_last = qwave + kQW - 1 + shift;   // last key this wavefront sees (causal)
+    // Keys before wave_full are visible to every query row of the wavefront.
+    const int wave_full = p.causal ? min(tk, qwave + shift + 1) : tk;
 
-    const float c2 = p.scale_log2;
-    float m = -INFINITY;   // running maximum of c2 * score over the keys seen
-    float l = 0.0f;        // this lane's share of the running sum of weights
-    f32x4 oacc[4];
+    // This lane's LDS read addresses (floats): K row lq with its chunk order,
+    // and V row 4*lh at column 4*lq.
+    const float *const krd = lds + lq * kKPitch + 16 * (lh ^ (k_chunk_flip(lq) >> 2));
+    const float *const vrd = lds + kKFloats + 4 * lh * kVPitch + 4 * lq;
+
+    float m = 0.0f;        // reference maximum of this lane's query (log2 units)
+    f32x4 negm = f32x4{0.0f, 0.0f, 0.0f, 0.0f};   // -m in every element
+    float l = 0.0f;        // this lane's share of the sum of weights
+    f32x4 oacc[4];         // oacc[nb][e]: output 16*lh + 4*e + nb of query qrow
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) oacc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    issue(0);
-    put(0);
-    if (nblocks > 1) issue(kBKV);
-    __syncthreads();
-
-    for (int t = 0; t < nblocks; ++t) {
+    auto compute = [&](int t, auto bufc, bool active, auto &&stage_put, auto &&stage_issue) {
+        constexpr int off = decltype(bufc)::value * kBufFloats;
         const int kv0 = t * kBKV;
-        const float *Kl = lds + (t & 1) * 2 * kTileFloats;
-        const float *Vl = Kl + kTileFloats;
-        if (wave_on && (!p.causal || kv0 <= wave_last)) {
-            // Scores^T for keys kv0 + 16*kb + (0..15): sacc[kb][r] is key
-            // kv0 + 16*kb + 4*lh + r of query qrow.
-            f32x4 sacc[4];
+        // Exponents for keys kv0 + 16*kb + (0..15): sacc[kb][r] is
+        // alpha*log2(e)*score - m for key kv0 + 16*kb + 4*lh + r of query qrow.
+        f32x4 sacc[4];
+        f32x4 kf[2][4];   // K fragments of step group j: head dimensions 16*lh + 4*j + e
+        auto read_k = [&](int j, f32x4 (&dst)[4]) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) sacc[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            // K fragments of step group j (head dimensions 16*lh + 4*j + e),
-            // read one group ahead; the four accumulators take turns.
-            f32x4 kf[2][4];
-            auto read_k = [&](int j, f32x4 (&dst)[4]) {
+            for (int kb = 0; kb < 4; ++kb)
+                dst[kb] = *reinterpret_cast<const f32x4 *>(krd + off + 16 * kb * kKPitch + 4 * j);
+        };
+        if (active) read_k(0, kf[0]);
+        stage_put();
+        if (!active) {
+            stage_issue();
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j + 1 < 4) read_k(j + 1, kf[(j + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
-                    dst[kb] = *reinterpret_cast<const f32x4 *>(Kl + (16 * kb + lq) * kPitch + 16 * lh + 4 * j);
-            };
-            read_k(0, kf[0]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j + 1 < 4) read_k(j + 1, kf[(j + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) sacc[kb] = mfma16(kf[j & 1][kb][e], qf[j][e], sacc[kb]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // Last key of this block the lane's query sees, relative to the
-            // lane's first key (kv0 + 4*lh); >= 63 when the block is all visible.
+                    sacc[kb] = mfma16(kf[j & 1][kb][e], qf[j][e], j == 0 && e == 0 ? negm : sacc[kb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        stage_issue();
+        if (kv0 + kBKV > wave_full) {
+            // Some key of this block is hidden from some row: the last key of
+            // the block the lane's query sees, relative to its first key.
             int lim = tk - 1;
             if (p.causal) lim = min(lim, qrow + shift);
             lim -= kv0 + 4 * lh;
-            float x[4][4];
-            float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = sacc[kb][r] * c2;
-                    x[kb][r] = 16 * kb + r <= lim ? v : -INFINITY;
-                    mt = fmaxf(mt, x[kb][r]);
-                }
-            mt = across_rows(mt, [](float x, float y) { return fmaxf(x, y); });
-            const float mnew = fmaxf(m, mt);
-            const float corr = exp2_fast(m - mnew);
-            m = mnew;
-            float ls = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    x[kb][r] = exp2_fast(x[kb][r] - mnew);
-                    ls += x[kb][r];
-                }
-            l = l * corr + ls;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) oacc[nb] *= corr;
-            // O^T += V^T P^T over the 64 keys of this block; the V values of
-            // 16-key group kb are read one group ahead.
-            float vf[2][4][4];   // [buffer][r][nb]: V[kv0 + 16*kb + 4*lh + r][16*nb + lq]
-            auto read_v = [&](int kb, float (&dst)[4][4]) {
-#pragma unroll
                 for (int r = 0; r < 4; ++r)
+                    if (16 * kb + r > lim) sacc[kb][r] = -INFINITY;
+        }
+        float lm = sacc[0][0];
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-                        dst[r][nb] = Vl[(16 * kb + 4 * lh + r) * kPitch + 16 * nb + lq];
-            };
-            read_v(0, vf[0]);
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (kb + 1 < 4) read_v(kb + 1, vf[(kb + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int r = 0; r < 4; ++r)
+                if (kb + r > 0) lm = fmaxf(lm, sacc[kb][r]);
+        if (t == 0 || __builtin_amdgcn_ballot_w64(lm > kSlack)) {
+            // Move the reference: to the row maxima on the first block (every
+            // row sees key 0), else up to them where they exceed it.
+            float dm = across_rows(lm, [](float x, float y) { return fmaxf(x, y); });
+            if (t != 0) {
+                dm = fmaxf(dm, 0.0f);
+                const float corr = exp2_fast(-dm);
+                l *= corr;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) oacc[nb] = mfma16(vf[kb & 1][r][nb], x[kb][r], oacc[nb]);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int nb = 0; nb < 4; ++nb) oacc[nb] *= corr;
             }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) sacc[kb] -= dm;
+            m += dm;
+            negm = f32x4{-m, -m, -m, -m};
         }
-        if (t + 1 < nblocks) {
-            put((t + 1) & 1);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sacc[kb][r] = exp2_fast(sacc[kb][r]);
+                l += sacc[kb][r];
+            }
+        // O^T += V^T P^T over the 64 keys of this block; vf[r] is V row
+        // kv0 + 16*kb + 4*lh + r, columns 4*lq .. 4*lq + 3, read one key
+        // group ahead.
+        f32x4 vf[2][4];
+        auto read_v = [&](int kb, f32x4 (&dst)[4]) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[r] = *reinterpret_cast<const f32x4 *>(vrd + off + (16 * kb + r) * kVPitch);
+        };
+        read_v(0, vf[0]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb + 1 < 4) read_v(kb + 1, vf[(kb + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) oacc[nb] = mfma16(vf[kb & 1][r][nb], sacc[kb][r], oacc[nb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Block t: its K and V are in buffer t % 2.  The next block's data,
+    // loaded one block ago, goes to the other buffer as soon as the block
+    // starts (every wavefront finished reading that buffer before the last
+    // barrier), right after this wavefront's first K reads, so the LDS writes
+    // complete during the products and the barrier waits only for them; the
+    // loads of the block after it are issued once the score products are done.
+    auto block = [&](int t, auto bufc) {
+        constexpr int next = 1 - decltype(bufc)::value;
+        auto stage_put = [&]() {
+            if (t + 1 < nblocks) put(std::integral_constant<int, next>{});
+        };
+        auto stage_issue = [&]() {
             if (t + 2 < nblocks) issue((t + 2) * kBKV);
-        }
+        };
+        compute(t, bufc, wave_on && (!p.causal || t * kBKV <= wave_last), stage_put, stage_issue);
         __syncthreads();
+    };
+
+    issue(0);
+    put(std::integral_constant<int, 0>{});
+    if (nblocks > 1) issue(kBKV);
+    __syncthreads();
+    for (int t = 0; t < nblocks; t += 2) {
+        block(t, std::integral_constant<int, 0>{});
+        if (t + 1 < nblocks) block(t + 1, std::integral_constant<int, 1>{});
     }
 
     // The four lanes of a query hold disjoint key subsets of its sum.
     l = across_rows(l, [](float x, float y) { return x + y; });
+    const float rl = 1.0f / l;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const f32x4 v = oacc[nb] / l;
-        store4_device(rO, qok ? (unsigned(qrow) * sOr + unsigned(16 * nb + 4 * lh)) * 4u : kOutOfRange, v);
+    for (int e = 0; e < 4; ++e) {
+        const f32x4 v = f32x4{oacc[0][e], oacc[1][e], oacc[2][e], oacc[3][e]} * rl;
+        store4_device(rO, qok ? (unsigned(qrow) * sOr + unsigned(16 * lh + 4 * e)) * 4u : kOutOfRange, v);
     }
 }
 
