@@ -3,13 +3,17 @@ the CPU oracle's attention on the same host bytes.
 
 Tolerance, derived from the fp32 arithmetic (u = 2^-24):
   * each score alpha*<q, k> carries an error of at most
-    Delta = (d + 3) * u * |alpha| * |q|_2 * |k|_2 (the d-term sum plus the
-    scale, the subtraction of the running maximum and exp2's argument);
+    Delta = (d + 3) * u * |alpha| * |q|_2 * |k|_2 (the d-term sum, the scale,
+    the subtraction of the reference maximum and exp2's argument; the
+    matrix-core kernel scales Q once and starts the d-term sum from minus the
+    reference, which is itself one of the row's scaled scores, so its terms
+    are the same ones);
   * logits perturbed by at most Delta move the softmax weights by at most
     2*Delta in the 1-norm, so the output moves by at most 2*Delta*max|V|;
   * the weights' own rounding, the rescaling of the running sums (at most
-    once per key) and the tk-term sums of the weights and of P V add at most
-    (5*tk + 16)*u relative to max|V|.
+    once per key; weights may reach 2^8 between rescalings, which changes no
+    relative error) and the tk-term sums of the weights and of P V add at
+    most (5*tk + 16)*u relative to max|V|.
   max |O_gpu - O_ref| <= 2 * max|V| * (2*Delta + (5*tk + 16)*u), with the
   largest row norms of Q and K; the outer factor 2 covers second-order terms.
 Bitwise checks cover what must not depend on the launch: two calls, grouped
