@@ -355,13 +355,16 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
         if (t + 1 < nblocks) block(t + 1, std::integral_constant<int, 1>{});
     }
 
-    // The four lanes of a query hold disjoint key subsets of its sum.
+    // The four lanes of a query hold disjoint key subsets of its sum.  Each
+    // store writes 16 of the 64 bytes of four row segments; the default
+    // (write-back) policy lets L2 merge the four stores of a segment before
+    // it goes to memory, where device-scope stores would write each piece.
     l = across_rows(l, [](float x, float y) { return x + y; });
     const float rl = 1.0f / l;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const f32x4 v = f32x4{oacc[0][e], oacc[1][e], oacc[2][e], oacc[3][e]} * rl;
-        store4_device(rO, qok ? (unsigned(qrow) * sOr + unsigned(16 * lh + 4 * e)) * 4u : kOutOfRange, v);
+        store4(rO, qok ? (unsigned(qrow) * sOr + unsigned(16 * lh + 4 * e)) * 4u : kOutOfRange, v);
     }
 }
 
