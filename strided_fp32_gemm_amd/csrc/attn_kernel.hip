@@ -66,6 +66,7 @@
 #include <type_traits>
 
 #include "attention.hpp"
+#include "attn_layout.hpp"
 #include "buffer.hpp"
 #include "kernels.hpp"
 
@@ -73,12 +74,11 @@ namespace sgemm {
 
 namespace {
 
-constexpr int kD = 64;                            // head dimension of the matrix-core kernel
-constexpr int kBKV = 64;                          // keys per LDS block
-constexpr int kKPitch = kD + 4;                   // K rows in LDS (floats)
-constexpr int kVPitch = kD;                       // V rows in LDS (floats)
-constexpr int kKFloats = kBKV * kKPitch;          // one K block
-constexpr int kBufFloats = kKFloats + kBKV * kVPitch;   // one K block and one V block
+constexpr int kD = kAttnD;                        // head dimension of the matrix-core kernel
+constexpr int kBKV = kAttnBlockKeys;              // keys per LDS block
+constexpr int kKPitch = kAttnKPitch;              // K rows in LDS (floats)
+constexpr int kVPitch = kAttnVPitch;              // V rows in LDS (floats)
+constexpr int kBufFloats = kAttnBufFloats;        // one K block and one V block
 constexpr int kQW = 16;                           // query rows per wavefront
 constexpr int kLdsBytes = 2 * kBufFloats * 4;
 constexpr float kSlack = 8.0f;                    // log2 of the largest weight before the reference moves
@@ -109,9 +109,6 @@ __device__ __forceinline__ float across_rows(float v, Op op) {
     return op(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
 }
 
-// 16-byte chunk c of K row `key` sits at chunk c ^ k_chunk_flip(key) of its
-// LDS row.
-__device__ __forceinline__ int k_chunk_flip(int key) { return (((key >> 2) ^ (key >> 3)) & 1) << 2; }
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
@@ -176,11 +173,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
     // 4*c .. 4*c + 3.  Global offsets are relative to the block's first row
     // (the second slot's distance is a scalar offset), LDS addresses are
     // fixed per thread.
-    const int kr = tid >> 4, c = tid & 15;
+    const int kr = tid >> 4, c = tid & 15;   // slot 0: key row, head dimensions 4*c .. +3
     const unsigned kgo = (unsigned(kr) * sKr + 4u * unsigned(c)) * 4u;
     const unsigned vgo = (unsigned(kr) * sVr + 4u * unsigned(c)) * 4u;
-    float *const kwr = lds + kr * kKPitch + 4 * (c ^ k_chunk_flip(kr));
-    float *const vwr = lds + kKFloats + kr * kVPitch + 4 * c;
+    // LDS layout (attn_layout.hpp): slot tid + SR*16*u sits SR*u rows below
+    // slot tid, with the same K chunk order.
+    float *const kwr = lds + attn_k_slot(tid);
+    float *const vwr = lds + attn_v_slot(tid);
     static_assert(SR % 16 == 0, "a thread's slots share the K chunk order");
     f32x4 kst[SL], vst[SL];
     auto issue = [&](int kv0) {
@@ -223,10 +222,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_d64(AttnArgs p) {
     // Keys before wave_full are visible to every query row of the wavefront.
     const int wave_full = p.causal ? min(tk, qwave + shift + 1) : tk;
 
-    // This lane's LDS read addresses (floats): K row lq with its chunk order,
-    // and V row 4*lh at column 4*lq.
-    const float *const krd = lds + lq * kKPitch + 16 * (lh ^ (k_chunk_flip(lq) >> 2));
-    const float *const vrd = lds + kKFloats + 4 * lh * kVPitch + 4 * lq;
+    // This lane's LDS read addresses (attn_layout.hpp): fragment (kb, j) of
+    // K and (kb, r) of V sit 16*kb*kKPitch + 4*j and (16*kb + r)*kVPitch
+    // floats past fragment (0, 0).
+    const float *const krd = lds + attn_k_frag(lane, 0, 0);
+    const float *const vrd = lds + attn_v_frag(lane, 0, 0);
 
     float m = 0.0f;        // reference maximum of this lane's query (log2 units)
     f32x4 negm = f32x4{0.0f, 0.0f, 0.0f, 0.0f};   // -m in every element

@@ -8,6 +8,7 @@
 #include <random>
 #include <vector>
 
+#include "attn_layout.hpp"
 #include "plan.hpp"
 
 using namespace sgemm;
@@ -258,10 +259,77 @@ static int print_tiles(int batch, int rows, int cols, int edge) {
     return 0;
 }
 
+// The fused attention kernel's key blocks (attn_layout.hpp): every
+// fragment read finds the element a staging write put there, the kernel's
+// incremental addressing (a base per lane or thread plus constants) matches
+// the layout functions, and every 16-byte access is free of bank conflicts.
+static void check_attention_lds() {
+    using namespace sgemm;
+    auto bad = [](const char *what, int a, int b, int c) {
+        if (fails++ < 10) std::printf("attention LDS: %s (%d, %d, %d)\n", what, a, b, c);
+    };
+    // Writes land inside their part of the buffer, each element once.
+    std::vector<int> hits(kAttnBufFloats, 0);
+    for (int s = 0; s < kAttnSlots; ++s)
+        for (int e = 0; e < 4; ++e) {
+            const int k = attn_k_slot(s) + e, v = attn_v_slot(s) + e;
+            if (k < 0 || k >= kAttnKFloats || v < kAttnKFloats || v >= kAttnBufFloats) bad("slot out of its part", s, e, 0);
+            else { ++hits[k]; ++hits[v]; }
+        }
+    for (int row = 0; row < kAttnBlockKeys; ++row)
+        for (int col = 0; col < kAttnD; ++col) {
+            if (hits[row * kAttnKPitch + col] != 1) bad("K element not written once", row, col, 0);
+            if (hits[kAttnKFloats + row * kAttnVPitch + col] != 1) bad("V element not written once", row, col, 0);
+        }
+    for (int lane = 0; lane < 64; ++lane) {
+        const int lq = lane & 15, lh = lane >> 4;
+        for (int kb = 0; kb < 4; ++kb)
+            for (int j = 0; j < 4; ++j) {
+                // K key 16kb + lq, head dimensions 16lh + 4j .. +3 = slot chunk 4lh + j.
+                if (attn_k_frag(lane, kb, j) != attn_k_slot(16 * (16 * kb + lq) + 4 * lh + j)) bad("K read", lane, kb, j);
+                if (attn_k_frag(lane, kb, j) != attn_k_frag(lane, 0, 0) + 16 * kb * kAttnKPitch + 4 * j)
+                    bad("K read offset", lane, kb, j);
+                // V key 16kb + 4lh + j, head dimensions 4lq .. +3 = slot chunk lq.
+                if (attn_v_frag(lane, kb, j) != attn_v_slot(16 * (16 * kb + 4 * lh + j) + lq)) bad("V read", lane, kb, j);
+                if (attn_v_frag(lane, kb, j) != attn_v_frag(lane, 0, 0) + (16 * kb + j) * kAttnVPitch)
+                    bad("V read offset", lane, kb, j);
+            }
+    }
+    for (int nt : {256, 512}) {
+        const int sr = nt / 16;   // key rows between a thread's slots
+        for (int t = 0; t < nt; ++t)
+            for (int u = 1; u * nt < kAttnSlots; ++u) {
+                if (attn_k_slot(t + u * nt) != attn_k_slot(t) + sr * u * kAttnKPitch) bad("K slot offset", nt, t, u);
+                if (attn_v_slot(t + u * nt) != attn_v_slot(t) + sr * u * kAttnVPitch) bad("V slot offset", nt, t, u);
+            }
+        for (int w = 0; w < nt / 64; ++w)
+            for (int u = 0; u * nt < kAttnSlots; ++u) {
+                long long ka[64], va[64];
+                for (int l = 0; l < 64; ++l) {
+                    ka[l] = attn_k_slot(64 * w + l + u * nt);
+                    va[l] = attn_v_slot(64 * w + l + u * nt);
+                }
+                expect_free("K staging write", "attention", nt, Op::Write16, ka);
+                expect_free("V staging write", "attention", nt, Op::Write16, va);
+            }
+    }
+    for (int kb = 0; kb < 4; ++kb)
+        for (int j = 0; j < 4; ++j) {
+            long long ka[64], va[64];
+            for (int l = 0; l < 64; ++l) {
+                ka[l] = attn_k_frag(l, kb, j);
+                va[l] = attn_v_frag(l, kb, j);
+            }
+            expect_free("K fragment read", "attention", kb, Op::Read16, ka);
+            expect_free("V fragment read", "attention", kb, Op::Read16, va);
+        }
+}
+
 int main(int argc, char **argv) {
     if (argc == 6 && std::string(argv[1]) == "tiles")
         return print_tiles(std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]));
     check_lds_banks();
+    check_attention_lds();
     std::mt19937_64 rng(12345);
     const uint32_t top = 0x7fffffffu;
     std::vector<uint32_t> ds;

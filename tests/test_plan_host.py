@@ -1,9 +1,11 @@
 """Host-side arithmetic of the planner, compiled with g++ (no GPU): the
 multiply-shift division by launch constants and the tile order built on it
 (every tile id maps to one in-range tile, exactly once, in the documented
-order), the two-level batch split, and the LDS row pads (every kernel's
+order), the two-level batch split, the LDS row pads (every kernel's
 fragment reads and staging writes free of bank conflicts under gfx950's
-lane groups)."""
+lane groups), and the fused attention kernel's key-block layout (each
+fragment read finds what the staging wrote, the kernel's base-plus-constant
+addressing matches the layout, and every access is conflict-free)."""
 import os
 import shutil
 import subprocess
