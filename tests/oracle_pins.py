@@ -214,6 +214,36 @@ def _exact_case(lib, rng, batch, m, n, k, a_major, b_major, alpha, acc):
     assert np.array_equal(got, exact.astype(np.float32)), (batch, m, n, k, a_major, b_major, alpha, acc)
 
 
+def pin_denormals(lib):
+    """Denormal operands and results are exact powers of two times the
+    integer case: A scaled by 2^-130 (denormal inputs), A and B each by
+    2^-70 (normal inputs, denormal products), and a denormal C_old added to
+    a zero product; int64 matmul times the scale gives each result, which
+    fp32 represents exactly (nothing is flushed to zero)."""
+    rng = np.random.default_rng(77)
+    m, n, k, batch = 6, 5, 7, 2
+    per_a, sa = layout_strides(m, k, "row")
+    per_b, sb = layout_strides(k, n, "col")
+    per_c, sc = layout_strides(m, n, "row")
+    Ai = rng.integers(-3, 4, per_a * batch).astype(np.float32)
+    Bi = rng.integers(-3, 4, per_b * batch).astype(np.float32)
+    exact_i = np.matmul(view(Ai, batch, m, k, sa).astype(np.int64),
+                        view(Bi, batch, k, n, sb).astype(np.int64)).astype(np.float64)
+    for sa_scale, sb_scale in ((2.0 ** -130, 1.0), (2.0 ** -70, 2.0 ** -70)):
+        A = (Ai.astype(np.float64) * sa_scale).astype(np.float32)
+        B = (Bi.astype(np.float64) * sb_scale).astype(np.float32)
+        out = np.zeros(per_c * batch, np.float32)
+        oracle.ref_sgemm(batch, m, n, k, 1.0, A, *sa, B, *sb, 0, out, *sc, lib=lib)
+        want = (exact_i * sa_scale * sb_scale).astype(np.float32)
+        assert np.count_nonzero(want) > 0 and np.abs(want[want != 0]).min() < 2.0 ** -126   # some denormal
+        assert np.array_equal(view(out, batch, m, n, sc), want), (sa_scale, sb_scale)
+    C0 = ((np.arange(per_c * batch) % 7 + 1) * 2.0 ** -135).astype(np.float32)
+    out = C0.copy()
+    oracle.ref_sgemm(batch, m, n, k, 1.0, np.zeros(per_a * batch, np.float32), *sa,
+                     Bi, *sb, 1, out, *sc, lib=lib)
+    assert np.array_equal(out, C0)
+
+
 # ------------------------------------------------ library cross-check (fp64)
 
 AWKWARD = [(17, 33, 9), (5, 129, 31), (1, 1, 1), (4, 4, 4), (5, 3, 9), (8, 16, 7),
@@ -675,7 +705,7 @@ def pin_attention_numpy_float64(lib):
 
 PINS = [pin_all_ones, pin_identity, pin_k_zero, pin_golden_transpose_trace,
         pin_golden_column_major, pin_blas_linear_mapping, pin_blas_rowmajor_trick,
-        pin_exact_bruteforce, pin_numpy_float64, pin_stride_swap, pin_transpose_identity,
+        pin_exact_bruteforce, pin_denormals, pin_numpy_float64, pin_stride_swap, pin_transpose_identity,
         pin_batch_slices, pin_accumulate, pin_order_and_entries, pin_nan_and_canaries,
         pin_epilogue_bruteforce, pin_epilogue_closed_forms, pin_sqnorms, pin_sqdist,
         pin_batched2_bthd_gqa, pin_batched2_gqa_row_folding, pin_attention_closed_forms,

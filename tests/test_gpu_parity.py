@@ -277,6 +277,42 @@ def test_strip_tile(tile, monkeypatch):
             assert e <= TOL, (tile, m, n, k, acc, e)
 
 
+def _denormal_problem(kind, seed, batch, m, n, k, a_major="row", b_major="row"):
+    """Small integers scaled by powers of two, so every partial sum is exact
+    and the result is unique: kind "in" makes A's entries denormal (2^-130
+    scale), "out" keeps A and B normal but every product denormal (2^-70
+    each), "c" multiplies zeros and adds a denormal C_old (accumulating)."""
+    p = wl.random_problem(seed, batch, m, n, k, a_major=a_major, b_major=b_major, dist="int",
+                          accumulate=kind == "c")
+    if kind == "in":
+        p.A.storage[:] = p.A.storage * np.float32(2.0 ** -130)
+    elif kind == "out":
+        p.A.storage[:] = p.A.storage * np.float32(2.0 ** -70)
+        p.B.storage[:] = p.B.storage * np.float32(2.0 ** -70)
+    else:
+        p.A.storage[:] = 0.0
+        p.C.storage[:] = (np.arange(p.C.storage.size) % 7 + 1).astype(np.float32) * np.float32(2.0 ** -135)
+    return p
+
+
+@pytest.mark.parametrize("kind", ["in", "out", "c"])
+def test_denormals_are_kept(kind, monkeypatch):
+    """Denormal inputs, denormal products and a denormal C_old come out of
+    every kernel family (the matrix-core tiles, the short-k strip and
+    persistent kernels, the direct wavefront and generic kernels) exactly
+    as the oracle computes them: nothing is flushed to zero."""
+    for fam in FAMILIES:
+        p = _denormal_problem(kind, 91, 2, 96, 80, 40)
+        got, ref = out(p, gpu_call(p, fam)), out(p, oracle_call(p))
+        assert np.count_nonzero(ref) > 0
+        assert np.array_equal(got, ref), (kind, fam)
+    for tile in ("s64k64", "p64x64k64"):
+        monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+        p = _denormal_problem(kind, 92, 2, 96, 80, 40, a_major="row", b_major="col")
+        assert tile in sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))["kernel"]
+        assert np.array_equal(out(p, gpu_call(p)), out(p, oracle_call(p))), (kind, tile)
+
+
 def test_column_major_output():
     """C stored column-major is served as C^T = B^T A^T."""
     for a_major, b_major in LAYOUTS:
