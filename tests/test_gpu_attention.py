@@ -191,6 +191,40 @@ def test_attention_large_scores():
         assert np.all(np.isfinite(got))
 
 
+def _block_trend_problem(seed, step, causal):
+    """Scores that move by `step` (log2 units, alpha*log2(e)*score) from one
+    64-key block to the next: Q rows are a shared unit vector u plus a little
+    noise, K row j is u scaled to put its score near step * (j // 64), plus
+    the same noise.  Rising scores move the matrix-core kernel's reference
+    maximum on every block (each move well past its 2^8 slack); falling ones
+    leave it at the first block and drive the later weights to zero."""
+    p = wl.random_attention(seed, 1, 4, 200, 320, 64, g=2, causal=causal, alpha=0.125, scale=0.05)
+    c2 = p.alpha * 1.4426950408889634
+    u = np.ones(p.d) / np.sqrt(p.d)
+    hk = -(-p.nb_inner // p.g)
+    def flat(shape, strides):   # storage index of every element
+        grids = np.meshgrid(*[np.arange(n) for n in shape], indexing="ij")
+        return sum(gr * st for gr, st in zip(grids, strides))
+    iq = flat((p.nb_outer, p.nb_inner, p.tq, p.d), p.Q.strides)
+    ik = flat((p.nb_outer, hk, p.tk, p.d), p.K.strides)
+    target = step * (np.arange(p.tk) // 64) / c2            # score wanted for key j
+    p.Q.storage[iq] = (p.Q.storage[iq] + u).astype(np.float32)
+    p.K.storage[ik] = (p.K.storage[ik] + target[None, None, :, None] * u).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("step", [10.0, -10.0, 3.0], ids=["rising", "falling", "within_slack"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_attention_reference_moves(step, causal):
+    """The online softmax against the oracle when the row maxima rise past
+    the matrix-core kernel's slack on every key block, fall after the first,
+    or rise within the slack (the reference stays put and weights exceed 1)."""
+    p = _block_trend_problem(61, step, causal)
+    assert describe(p)["kernel"].startswith("attn_mfma_d64")
+    got = check(p)
+    assert np.all(np.isfinite(got))
+
+
 def test_attention_never_reads_O_and_leaves_gaps():
     """O starts as NaN inside and as a sentinel in the gaps between rows,
     heads and sequences: outputs come out finite and the gaps untouched."""
