@@ -49,6 +49,7 @@ if ROOT not in sys.path:
 
 PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 WARMUP_SECONDS = 0.3              # default warm-up: the clock ramps up within it
+CONFIG_WARMUP_SECONDS = 1.0       # the configurations' short kernels: a longer ramp, measured steadier
 METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
 DEFAULT_WORKLOAD = "square4096_acc"
 # The other configurations of the method's workload set, timed beside the
@@ -269,7 +270,7 @@ def _step_fn(p, dev, stream):
     return (lambda: sg.sgemm_strided_batched(*args, stream=stream)), info, (dA, dB, dC)
 
 
-def measure(name: str, steps: int, warmup):
+def measure(name: str, steps: int, warmup, warmup_seconds: float = WARMUP_SECONDS):
     """Time `steps` launches of one workload (inputs resident in device
     memory); returns the problem, its plan, the wall time of the timed region,
     the mean launch time from one HIP event pair on the launch stream around
@@ -284,10 +285,10 @@ def measure(name: str, steps: int, warmup):
     stream = torch.cuda.current_stream(dev)
     step, info, keep = _step_fn(p, dev, stream)
     if warmup is None:
-        # Warm up for WARMUP_SECONDS of device time (at least 5 steps).
+        # Warm up for warmup_seconds of device time (at least 5 steps).
         warmup = 0
         t_warm = time.perf_counter()
-        while warmup < 5 or time.perf_counter() - t_warm < WARMUP_SECONDS:
+        while warmup < 5 or time.perf_counter() - t_warm < warmup_seconds:
             for _ in range(5):
                 step()
             warmup += 5
@@ -327,12 +328,13 @@ def measure(name: str, steps: int, warmup):
     return p, info, wall, mean_ms, launch_ms, warmup
 
 
-def config_entry(label: str, name: str, cpu_seconds: float) -> dict:
+def config_entry(label: str, name: str) -> dict:
     """One configuration of the workload set: its kernel's mean launch time
-    and rate against the fp32 matrix peak, and the oracle beside it."""
+    and rate against the fp32 matrix peak (the oracle is timed afterwards,
+    once every configuration's kernel has been timed)."""
     from strided_fp32_gemm_amd import workloads as wl
 
-    p, info, _, mean_ms, launch_ms, warmup = measure(name, CONFIG_STEPS, None)
+    p, info, _, mean_ms, launch_ms, warmup = measure(name, CONFIG_STEPS, None, CONFIG_WARMUP_SECONDS)
     flops = float(p.flops)
     achieved = flops / (mean_ms * 1e-3) / 1e12
     alg_bytes = wl.algorithmic_bytes(p)
@@ -344,8 +346,6 @@ def config_entry(label: str, name: str, cpu_seconds: float) -> dict:
          "tflops": round(achieved, 3), "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
          "algorithmic_bytes": alg_bytes,
          "achieved_tb_per_s": round(alg_bytes / (mean_ms * 1e-3) / 1e12, 3)}
-    if cpu_seconds > 0:
-        e["cpu_baseline"] = cpu_baseline(p, cpu_seconds)
     return e
 
 
@@ -474,10 +474,19 @@ def main() -> int:
 def configs_object(headline: dict, cpu_seconds: float) -> dict:
     """Every configuration of the workload set beside the headline (config
     5), each timed in this same process, plus the attention pair together."""
+    from strided_fp32_gemm_amd import workloads as wl
+
+    # Every kernel first, back to back, so the device's clock stays where its
+    # warm-up put it (an oracle slice in between leaves the GPU idle for
+    # seconds); then the oracle slices.
     out = {}
     for label, name in CONFIG_WORKLOADS:
         print(f"[bench] config {label}: {name}", file=sys.stderr, flush=True)
-        out[name] = config_entry(label, name, cpu_seconds)
+        out[name] = config_entry(label, name)
+    if cpu_seconds > 0:
+        for label, name in CONFIG_WORKLOADS:
+            print(f"[bench] config {label}: oracle slice", file=sys.stderr, flush=True)
+            out[name]["cpu_baseline"] = cpu_baseline(wl.workload(name), cpu_seconds)
     qk, pv = out["attn_qk"], out["attn_pv"]
     ms = qk["launch_ms_mean"] + pv["launch_ms_mean"]
     fl = qk["flops_per_launch"] + pv["flops_per_launch"]
