@@ -32,6 +32,8 @@ The JSON line carries:
              64^3 product, the linear layer, attention's Q K^T and P V, and
              the spectrogram -- mean launch time, TFLOP/s, fraction of the
              fp32 matrix peak, kernel, and the oracle on a slice of each.
+             Their kernels are timed back to back (1 s warm-up each), and
+             the oracle slices run after the last of them.
 """
 from __future__ import annotations
 
