@@ -19,7 +19,10 @@ The JSON line carries:
   roofline   the dominant (only) kernel: algorithmic FLOPs per launch divided
              by its mean launch duration from HIP events recorded on the
              launch stream, against the MI355X dense fp32 matrix peak
-             (157.3 TFLOP/s); `traffic` (HBM bytes per launch) and
+             (157.3 TFLOP/s) -- or, for a workload below the machine balance
+             (fewer than ~19.7 flops per algorithmic byte, e.g. skinny_xWt),
+             its algorithmic bytes per launch against the HBM peak
+             (8000 GB/s); `traffic` (HBM bytes per launch) and
              `mfma_busy` (matrix-core busy fraction) come from the committed
              rocprofv3 counter record when it was taken on the current
              library sources, else null; `achieved_tb_per_s` is the
@@ -50,6 +53,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E peak bandwidth
 WARMUP_SECONDS = 0.3              # default warm-up: the clock ramps up within it
 CONFIG_WARMUP_SECONDS = 1.0       # the configurations' short kernels: a longer ramp, measured steadier
 METRIC = "fp32 batched strided GEMM TFLOP/s and % of MI355X fp32 matrix peak"
@@ -357,7 +361,6 @@ def bench_one(name: str, steps: int, warmup, cpu_seconds: float) -> dict:
     p, info, wall, mean_ms, launch_ms, warmup = measure(name, steps, warmup)
     flops = float(p.flops)
     value = flops * steps / wall / 1e12
-    achieved = flops / (mean_ms * 1e-3) / 1e12
     counters = counter_record(name, info["kernel"])
     alg_bytes = wl.algorithmic_bytes(p)
     line = {
@@ -376,11 +379,7 @@ def bench_one(name: str, steps: int, warmup, cpu_seconds: float) -> dict:
         "config": _config(p, info),
         "frac_of_peak": round(value / PEAK_FP32_MATRIX_TFLOPS, 4),
         "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 3),
-            "peak": PEAK_FP32_MATRIX_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
+            **_roofline_bound(flops, alg_bytes, mean_ms),
             "traffic": counters.get("traffic"),
             "mfma_busy": counters.get("mfma_busy"),
             "algorithmic_bytes": alg_bytes,
@@ -394,6 +393,20 @@ def bench_one(name: str, steps: int, warmup, cpu_seconds: float) -> dict:
     if cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(p, cpu_seconds)
     return line
+
+
+def _roofline_bound(flops: float, alg_bytes: int, mean_ms: float) -> dict:
+    """The roof one launch is held to: matrix-core throughput when the
+    workload's arithmetic intensity (flops per algorithmic byte) reaches the
+    machine balance (peak flops / peak HBM bandwidth, ~19.7 flop per byte),
+    HBM bandwidth below it."""
+    if flops / alg_bytes >= PEAK_FP32_MATRIX_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        achieved = flops / (mean_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MATRIX_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4)}
+    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4)}
 
 
 def _config(p, info) -> dict:

@@ -433,7 +433,7 @@ int describe(const sgemm::GemmArgs &a, int path, int num_cus, sgemm_plan_info *i
     } else if (plan.tile >= 0 && plan.family == sgemm::Family::Wave) {
         const sgemm::WaveCfg &t = sgemm::kWaveTiles[plan.tile];
         info->tile_m = t.bm; info->tile_n = t.bn; info->tile_k = 16;
-        info->waves = 1;
+        info->waves = plan.ksplit;
     } else if (plan.tile >= 0) {
         const sgemm::TileCfg &t = sgemm::kTiles[plan.tile];
         info->tile_m = t.bm; info->tile_n = t.bn; info->tile_k = t.bk;

@@ -186,7 +186,11 @@ const WaveTable &wave_table() {
         fill_wave_1(tab);
         fill_wave_2(tab);
         fill_wave_3(tab);
-        static_assert(kNumWaveTiles == 4, "launch table covers every wave tile");
+        fill_wave_4(tab);
+        fill_wave_5(tab);
+        fill_wave_6(tab);
+        fill_wave_7(tab);
+        static_assert(kNumWaveTiles == 8, "launch table covers every wave tile");
         return tab;
     }();
     return t;
@@ -254,6 +258,7 @@ int launch_plan(const Plan &p, hipStream_t stream, std::string &why) {
         a.c_vec4 = p.c_vec4 ? 1 : 0;
         a.alpha = p.alpha;
         a.epi = make_epilogue(p);
+        a.ksplit = p.ksplit;
         if (p.persist)
             persist_table().f[p.tile][p.a_kfast][p.b_kfast][p.accumulate != 0](
                 a, unsigned(p.workgroups), stream);

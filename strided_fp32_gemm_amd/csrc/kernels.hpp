@@ -54,6 +54,7 @@ struct MfmaArgs {
     int c_vec4;   // C rows take 16-byte stores (n-contiguous, aligned, n % 4 == 0)
     float alpha;
     Epilogue epi;
+    int ksplit;   // wavefront kernel: wavefronts per workgroup sharing one tile's k (1: no split)
 };
 
 // Arguments of the generic kernel: everything 64-bit.
@@ -107,6 +108,10 @@ void fill_wave_0(WaveTable &);
 void fill_wave_1(WaveTable &);
 void fill_wave_2(WaveTable &);
 void fill_wave_3(WaveTable &);
+void fill_wave_4(WaveTable &);
+void fill_wave_5(WaveTable &);
+void fill_wave_6(WaveTable &);
+void fill_wave_7(WaveTable &);
 void fill_persist_0(PersistTable &);
 void fill_persist_1(PersistTable &);
 void fill_persist_2(PersistTable &);

@@ -144,33 +144,21 @@ bool tile_fits(const Plan &p, int bm, int bn) {
            (!p.col_add || fits_buffer(1, 0, bn, p.sL_n));
 }
 
-// Estimated cycles of a direct-wavefront launch.  Tiles are spread over the
-// CUs and up to `occ` of them run concurrently on one CU (bounded by
-// registers, and by how many each CU receives).  A round of `occ` tiles
-// costs the larger of its matrix-core work at the tile's sustained rate and
-// its operand reads through L2 (~64 bytes per cycle per CU), plus the
-// epilogue traffic of C (read and written when accumulating, ~10 bytes per
-// cycle per CU), plus memory latency the round cannot hide.  Constants were
-// fitted to tile sweeps on MI355X.
-struct CostShape {
-    int bm, bn, kstep;   // tile and k granularity
-    double occ_limit;    // tiles one CU can hold
-    double rate;
-    double latency;      // cycles per round
-};
-
-double launch_cost(const Plan &p, const CostShape &c, int num_cus) {
-    const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 11.0;
-    int64_t tm = (p.m + c.bm - 1) / c.bm, tn = (p.n + c.bn - 1) / c.bn;
-    double tiles = double(p.batch) * double(tm) * double(tn);
-    double cus = double(std::max(num_cus, 1));
-    double occ = std::max(1.0, std::min(c.occ_limit, std::ceil(tiles / cus)));
-    double rounds = std::ceil(tiles / (cus * occ));
-    double kpad = double((p.k + c.kstep - 1) / c.kstep) * c.kstep;
-    double compute = occ * c.bm * c.bn * 2.0 * kpad / kFlopPerCuCycle / c.rate;
-    double operands = occ * double(c.bm + c.bn) * kpad * 4.0 / kOperandBytesPerCycle;
-    double epilogue = occ * c.bm * c.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
-    return rounds * (std::max(compute, operands) + epilogue + c.latency);
+// No launch streams faster than HBM: ~2700 bytes per cycle across the chip,
+// and ~15 per cycle into one CU (measured: with few workgroups only their
+// CUs fetch).  Each distinct operand is read once (a zero batch stride
+// shares it) and C written once (read too when accumulating).  Streaming
+// and compute overlap imperfectly: a quarter of the smaller of the two
+// shows, which also ranks launches that all sit at the HBM floor.
+double stream_floor(const Plan &p, double cost, double workgroups, int num_cus) {
+    const double kHbmBytesPerCycle = 2700.0, kCuStreamBytesPerCycle = 15.0, kOverlapLoss = 0.25;
+    const double a_elems = double(p.sA_b == 0 && p.sA_i == 0 ? 1 : p.batch) * double(p.m) * double(p.k);
+    const double b_elems = double(p.sB_b == 0 && p.sB_i == 0 ? 1 : p.batch) * double(p.k) * double(p.n);
+    const double c_elems = double(p.batch) * double(p.m) * double(p.n) * (p.accumulate ? 2.0 : 1.0);
+    const double bytes = 4.0 * (a_elems + b_elems + c_elems);
+    const double cus = std::min(std::max(workgroups, 1.0), double(std::max(num_cus, 1)));
+    const double fetch = std::max(bytes / kHbmBytesPerCycle, bytes / (cus * kCuStreamBytesPerCycle));
+    return std::max(cost, fetch) + kOverlapLoss * std::min(cost, fetch);
 }
 
 // Estimated cycles of an LDS-tiled launch.  The dispatcher hands a CU its
@@ -196,14 +184,42 @@ double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
     const double compute = double(t.bm) * t.bn * 2.0 * kpad / kFlopPerCuCycle / rate;
     const double operands = double(t.bm + t.bn) * kpad * 4.0 / kOperandBytesPerCycle;
     const double epilogue = double(t.bm) * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
-    return per_cu * (std::max(compute, operands) + epilogue) + kSliceLatency * std::min<double>(double(slices), 2.0);
+    return stream_floor(p, per_cu * (std::max(compute, operands) + epilogue) +
+                               kSliceLatency * std::min<double>(double(slices), 2.0), tiles, num_cus);
 }
 
-double wave_cost(const Plan &p, const WaveCfg &t, int num_cus) {
-    const double kLatency = 2720.0;
-    CostShape c{t.bm, t.bn, 16, 4.0 * t.waves_per_simd, t.rate, kLatency};
-    return launch_cost(p, c, num_cus);
+// Estimated cycles of a direct-wavefront launch whose workgroups hold
+// `splits` wavefronts sharing one tile's k.  Workgroups are spread over the
+// CUs and up to `occ` of them run concurrently on one CU (bounded by
+// registers, and by how many each CU receives).  A CU's four SIMDs share its
+// wavefronts; with fewer than four, SIMDs idle and each wavefront runs at
+// one SIMD's pace.  A round costs the larger of the busiest SIMD's
+// matrix-core work at the tile's sustained rate and the CU's operand reads
+// through L2 (~64 bytes per cycle), plus the epilogue traffic of C (read and
+// written when accumulating, ~11 bytes per cycle per CU), the fixed-order sum
+// of the split partials through LDS, and memory latency the round cannot
+// hide (a SIMD with a single wavefront hides less of it: kLoneWave); then
+// the HBM floor.  Rates and constants were fitted to tile and split sweeps
+// on MI355X.
+double wave_cost(const Plan &p, const WaveCfg &t, int splits, int num_cus) {
+    const double kFlopPerSimdCycle = 64.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 11.0;
+    const double kLdsBytesPerCycle = 128.0, kLatency = 2720.0, kLoneWave = 0.8;
+    const double tiles = double(p.batch) * double((p.m + t.bm - 1) / t.bm) * double((p.n + t.bn - 1) / t.bn);
+    const double cus = double(std::max(num_cus, 1));
+    const double fit = std::max(1.0, std::floor(4.0 * t.waves_per_simd / splits));
+    const double occ = std::max(1.0, std::min(fit, std::ceil(tiles / cus)));
+    const double rounds = std::ceil(tiles / (cus * occ));
+    const double groups = double((p.k + 15) / 16);
+    const double kwave = std::ceil(groups / splits) * 16.0;   // k of one wavefront
+    const double per_simd = std::max(1.0, occ * splits / 4.0);
+    const double rate = t.rate * (occ * splits <= 4.0 ? kLoneWave : 1.0);
+    const double compute = per_simd * t.bm * t.bn * 2.0 * kwave / kFlopPerSimdCycle / rate;
+    const double operands = occ * double(t.bm + t.bn) * groups * 16.0 * 4.0 / kOperandBytesPerCycle;
+    const double epilogue = occ * t.bm * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
+    const double reduce = splits > 1 ? occ * (splits - 1) * t.bm * t.bn * 4.0 / kLdsBytesPerCycle : 0.0;
+    return stream_floor(p, rounds * (std::max(compute, operands) + epilogue + reduce + kLatency), tiles, num_cus);
 }
+
 
 // Workgroups of a persistent launch: as many as the CUs hold at once (LDS
 // bound, two slabs each), at most one per tile.  When the tile count is a
@@ -238,7 +254,7 @@ double persist_cost(const Plan &p, const PersistCfg &t, int num_cus, int64_t gri
     double compute = occ * t.bm * t.bn * 2.0 * kpad / kFlopPerCuCycle / t.rate;
     double operands = occ * double(t.bm + t.bn) * kpad * 4.0 / kOperandBytesPerCycle;
     double epilogue = occ * t.bm * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
-    return iters * std::max({compute, operands, epilogue}) + kFill;
+    return stream_floor(p, iters * std::max({compute, operands, epilogue}) + kFill, double(grid), num_cus);
 }
 
 bool persist_serves(const Plan &p, const PersistCfg &t) {
@@ -268,7 +284,7 @@ double strip_cost(const Plan &p, const StripCfg &t, int num_cus) {
     double npad = double((p.n + StripCfg::kBlockCols - 1) / StripCfg::kBlockCols) * StripCfg::kBlockCols;
     double compute = occ * t.rows * npad * 2.0 * t.kmax / kFlopPerCuCycle / t.rate;
     double epilogue = occ * t.rows * double(p.n) * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
-    return rounds * std::max(compute, epilogue) + kFill;
+    return stream_floor(p, rounds * std::max(compute, epilogue) + kFill, wgs, num_cus);
 }
 
 }  // namespace
@@ -364,14 +380,15 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         if (!force_known || family != Family::Auto) force = nullptr;
     }
 
-    int best = -1;
+    int best = -1, best_split = 1;
     bool best_wave = false, best_persist = false, best_strip = false;
     double best_cost = 0;
-    auto consider = [&](int t, bool wave, bool persist, int bm, int bn, double cost) {
+    auto consider = [&](int t, bool wave, bool persist, int bm, int bn, double cost, int split = 1) {
         int64_t wgs = p.batch * ((p.m + bm - 1) / bm) * ((p.n + bn - 1) / bn);
         if (wgs > i32max || !tile_fits(p, bm, bn)) return;
         if (best < 0 || cost < best_cost) {
             best = t; best_wave = wave; best_persist = persist; best_strip = false; best_cost = cost;
+            best_split = split;
         }
     };
     if (small_enough && family != Family::Generic) {
@@ -395,10 +412,35 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
                 }
             }
         }
-        if (family != Family::Mfma)
-            for (int t = 0; t < kNumWaveTiles; ++t)
-                if (allowed(kWaveTiles[t].name))
-                    consider(t, true, false, kWaveTiles[t].bm, kWaveTiles[t].bn, wave_cost(p, kWaveTiles[t], num_cus));
+        if (family != Family::Mfma) {
+            // Splits of k over 1, 2, 4, ... wavefronts.  SGEMM_WAVE_SPLIT=<s>
+            // fixes the split at the largest power of two <= s the tile
+            // allows (tuning sweeps, and tests that force a split on small
+            // shapes).
+            int fixed_split = 0;
+            if (const char *ks = std::getenv("SGEMM_WAVE_SPLIT")) fixed_split = std::max(1, std::atoi(ks));
+            const int64_t groups = (p.k + 15) / 16;
+            for (int t = 0; t < kNumWaveTiles; ++t) {
+                if (!allowed(kWaveTiles[t].name)) continue;
+                // 16-wide tiles serve a dimension of at most 16 (unforced).
+                if (!force && ((kWaveTiles[t].bm == 16 && p.m > 16) || (kWaveTiles[t].bn == 16 && p.n > 16)))
+                    continue;
+                const int most = std::min(kWaveTiles[t].max_split, fixed_split ? fixed_split : kWaveMaxSplit);
+                const int64_t tiles = p.batch * ((p.m + kWaveTiles[t].bm - 1) / kWaveTiles[t].bm) *
+                                      ((p.n + kWaveTiles[t].bn - 1) / kWaveTiles[t].bn);
+                for (int s = 1; s <= most; s *= 2) {
+                    // Unforced, a split is for launches that leave SIMDs idle
+                    // unsplit (fewer tiles than SIMDs); it must leave every
+                    // wavefront at least four groups and the chip at most two
+                    // wavefronts per SIMD.
+                    const int64_t simds = 4 * int64_t(num_cus);
+                    if (fixed_split ? 2 * s <= most
+                                    : s > 1 && (tiles >= simds || groups < 4 * s || tiles * s > 2 * simds))
+                        continue;
+                    consider(t, true, false, kWaveTiles[t].bm, kWaveTiles[t].bn, wave_cost(p, kWaveTiles[t], s, num_cus), s);
+                }
+            }
+        }
     }
     if (best >= 0 && best_strip) {
         const StripCfg &c = kStripTiles[best];
@@ -420,6 +462,7 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         p.tiles_m = (p.m + bm - 1) / bm;
         p.tiles_n = (p.n + bn - 1) / bn;
         p.workgroups = p.batch * p.tiles_m * p.tiles_n;
+        p.ksplit = best_wave ? best_split : 1;
         if (best_persist) p.workgroups = persist_grid(p, kPersistTiles[best], num_cus, p.workgroups);
         if (!best_wave && !best_persist) {
             // The LDS-tiled kernel keeps each thread's load offsets for the
@@ -440,7 +483,8 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         }
         p.kernel_name = std::string(best_wave ? "wave_" : best_persist ? "persist_" : "mfma_") + name +
                         (p.a_kfast ? "_ak" : "_am") + (p.b_kfast ? "_bk" : "_bn") +
-                        (p.accumulate ? "_acc" : "") + (p.row_add || p.col_add ? "_vec" : "");
+                        (p.accumulate ? "_acc" : "") + (p.row_add || p.col_add ? "_vec" : "") +
+                        (p.ksplit > 1 ? "_s" + std::to_string(p.ksplit) : "");
     } else {
         p.family = Family::Generic;
         p.tile = -1;

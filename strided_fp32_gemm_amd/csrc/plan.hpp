@@ -119,22 +119,30 @@ inline constexpr TileCfg kTiles[kNumTiles] = {
     {64, 32, 32, 4, 1, 16, "t64x32m16", 0.830},
 };
 
-// One tile of the direct wavefront kernel (WAVE family): a single
-// wavefront owns bm x bn outputs in 16 x 16 matrix-core blocks and reads its
-// operands straight from global memory.
+// One tile of the direct wavefront kernel (WAVE family): a wavefront owns
+// bm x bn outputs in 16 x 16 matrix-core blocks and reads its operands
+// straight from global memory.  Up to max_split wavefronts of one workgroup
+// may share a tile, each taking a share of k.
 struct WaveCfg {
     int bm, bn;
     int waves_per_simd;  // resident wavefronts per SIMD (register-limited, from the compiled code)
     const char *name;
     double rate;         // sustained fraction of peak on a full CU (fitted)
+    int max_split;       // most wavefronts per workgroup in the split variant
 };
 
-constexpr int kNumWaveTiles = 4;
+constexpr int kNumWaveTiles = 8;
+// Largest split of a wave tile's k over the wavefronts of a workgroup.
+constexpr int kWaveMaxSplit = 16;
 inline constexpr WaveCfg kWaveTiles[kNumWaveTiles] = {
-    {32, 32, 5, "w32x32", 0.58},
-    {32, 64, 3, "w32x64", 0.75},
-    {64, 32, 3, "w64x32", 0.76},
-    {64, 64, 2, "w64x64", 0.77},
+    {32, 32, 5, "w32x32", 0.58, 16},
+    {32, 64, 3, "w32x64", 0.75, 8},
+    {64, 32, 3, "w64x32", 0.76, 8},
+    {64, 64, 2, "w64x64", 0.77, 8},
+    {16, 32, 7, "w16x32", 0.41, 16},
+    {16, 64, 4, "w16x64", 0.48, 16},
+    {32, 16, 7, "w32x16", 0.36, 16},
+    {64, 16, 4, "w64x16", 0.41, 16},
 };
 
 // One tile of the persistent short-k kernel (MFMA family): a fixed grid of
@@ -293,6 +301,7 @@ struct Plan {
     int64_t sB_b = 0, sB_k = 0, sB_n = 0;
     int64_t sC_b = 0, sC_m = 0, sC_n = 0;
     int64_t tiles_m = 0, tiles_n = 0, workgroups = 0;  // workgroups < tiles for the persistent kernel
+    int ksplit = 1;            // WAVE family: wavefronts per workgroup sharing one tile's k
     std::string kernel_name;
 };
 

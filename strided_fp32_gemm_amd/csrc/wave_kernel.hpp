@@ -24,23 +24,38 @@
 //    multiplied.  Loads past the end of k fail the buffer range check and
 //    read zeros, so the load sequence is the same in every iteration.
 //
-// Summation order per output is fixed (k groups in order), so results are
-// reproducible bit for bit.  No atomics.
+// Split variant (SPLIT, p.ksplit = S wavefronts per workgroup, 2 <= S <=
+// the tile's max_split): the S wavefronts share one output tile; wavefront w takes
+// the k groups w, w + S, w + 2S, ... and keeps its own partial tile.  After
+// the loop wavefronts 1 .. S-1 leave their partials in LDS and wavefront 0
+// adds them to its own in the order w = 1, 2, ..., S-1 and runs the
+// epilogue.  This is for products with few tiles and a long k (skinny
+// shapes: a few rows or columns), where one wavefront per tile leaves most
+// of the chip idle and too few loads in flight to stream the long operand
+// at HBM speed.
+//
+// Summation order per output is fixed (k groups in order, then the split
+// partials in wavefront order), so results are reproducible bit for bit.
+// No atomics.
 #pragma once
 
 #include "mfma_kernel.hpp"
 
 namespace sgemm {
 
-template <int W, bool AK, bool BKF, bool AV4, bool BV4>
-__global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
+template <int W, bool AK, bool BKF, bool AV4, bool BV4, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 64 * kWaveTiles[W].max_split : 64) void sgemm_wave(MfmaArgs p) {
     constexpr WaveCfg cfg = kWaveTiles[W];
     constexpr int WM = cfg.bm, WN = cfg.bn;
     constexpr int TM = WM / 16, TN = WN / 16;
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile shape");
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int lr = lane & 15, lh = lane >> 4;
+    // This wavefront's share of k: groups wid, wid + S, ... (wid = 0, S = 1
+    // unless SPLIT).
+    const int S = SPLIT ? p.ksplit : 1;
+    const int wid = SPLIT ? __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6) : 0;
     int b, tm, tn;
     tile_coords(p.map, blockIdx.x, b, tm, tn);
     const int i0 = tm * WM, j0 = tn * WN;
@@ -120,19 +135,44 @@ __global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
     // multiply conditional on the group count would give the accumulators
     // two incoming paths and cost register copies every iteration); an odd
     // last group is multiplied after the loop.
-    const int NG = (p.k + 15) / 16;
+    const int NG_all = (p.k + 15) / 16;
+    const int NG = NG_all > wid ? (NG_all - wid + S - 1) / S : 0;   // this wavefront's groups
     if (NG > 0) {
+        const unsigned g0 = unsigned(wid), gs = unsigned(S);
         f32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-        fetch(0u, fa0, fb0);
-        fetch(1u, fa1, fb1);
+        fetch(g0, fa0, fb0);
+        fetch(g0 + gs, fa1, fb1);
         int g = 0;
         for (; g + 1 < NG; g += 2) {
             multiply(fa0, fb0);
-            fetch(unsigned(g + 2), fa0, fb0);
+            fetch(g0 + unsigned(g + 2) * gs, fa0, fb0);
             multiply(fa1, fb1);
-            fetch(unsigned(g + 3), fa1, fb1);
+            fetch(g0 + unsigned(g + 3) * gs, fa1, fb1);
         }
         if (g < NG) multiply(fa0, fb0);
+    }
+
+    if constexpr (SPLIT) {
+        // Partials of wavefronts 1 .. S-1: part[(w - 1) * TM * TN + block][lane].
+        extern __shared__ f32x4 part[];
+        if (wid > 0) {
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int c = 0; c < TN; ++c) part[((wid - 1) * TM * TN + a * TN + c) * 64 + lane] = acc[a][c];
+        }
+        __syncthreads();
+        if (wid > 0) return;
+        for (int w = 1; w < S; ++w) {
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int c = 0; c < TN; ++c) {
+                    const f32x4 q = part[((w - 1) * TM * TN + a * TN + c) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[a][c][e] += q[e];
+                }
+        }
     }
 
     // Epilogue: lane (lr, lh) of block (a, c) holds C[a*16 + lr][c*16 + 4*lh + r]
@@ -191,9 +231,20 @@ __global__ __launch_bounds__(64) void sgemm_wave(MfmaArgs p) {
     }
 }
 
+// LDS of the split variant: the partial tiles of wavefronts 1 .. S-1.
+constexpr int wave_split_lds(int w, int splits) { return (splits - 1) * kWaveTiles[w].bm * kWaveTiles[w].bn * 4; }
+
 template <int W, bool AK, bool BKF, bool AV4, bool BV4>
 void launch_wave(const MfmaArgs &a, unsigned grid, hipStream_t s) {
-    hipLaunchKernelGGL((sgemm_wave<W, AK, BKF, AV4, BV4>), dim3(grid), dim3(64), 0, s, a);
+    if (a.ksplit > 1) {
+        const int lds = wave_split_lds(W, a.ksplit);
+        static std::atomic<unsigned long long> lds_set{0};
+        const void *fn = reinterpret_cast<const void *>(&sgemm_wave<W, AK, BKF, AV4, BV4, true>);
+        if (lds > 64 * 1024) allow_dynamic_lds(fn, lds, lds_set);
+        hipLaunchKernelGGL((sgemm_wave<W, AK, BKF, AV4, BV4, true>), dim3(grid), dim3(64 * a.ksplit), lds, s, a);
+    } else {
+        hipLaunchKernelGGL((sgemm_wave<W, AK, BKF, AV4, BV4, false>), dim3(grid), dim3(64), 0, s, a);
+    }
 }
 
 template <int W, bool AK, bool BKF>

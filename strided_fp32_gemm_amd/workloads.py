@@ -35,7 +35,7 @@ ROOT_SEED = 2024
 # Benchmark workloads.
 WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
              "linear_bwd_dx", "linear_bwd_dw", "linear_xT", "linear_bias", "sqdist",
-             "attn_qk_gqa", "attn_pv_gqa", "attn_fused", "attn_fused_causal")
+             "attn_qk_gqa", "attn_pv_gqa", "attn_fused", "attn_fused_causal", "skinny_xWt")
 # Entry point each workload goes through: "plain" (sgemm_strided_batched),
 # "ex" (sgemm_strided_batched_ex), "dist" (sgemm_pairwise_sqdist) or
 # "batched2" (sgemm_strided_batched2) or "attention" (sgemm_attention).
@@ -51,7 +51,7 @@ def kind(name: str) -> str:
 # layer's backward pass share one draw of dy, W and x).
 SEED_NAMES = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
               "linear_bwd", "linear_xT", "linear_bias", "sqdist", "attn_qk_gqa", "attn_pv_gqa",
-              "attn_fused")
+              "attn_fused", "skinny_xWt")
 
 
 @dataclasses.dataclass
@@ -296,6 +296,20 @@ def linear_bias() -> Problem:
                    beta=0.0, col=Vector(bias, (0, 1)))
 
 
+def skinny_xWt() -> Problem:
+    """A skinny product: y = x W^T for 4 rows, x [4][4096] N(0,1), W stored
+    [16384][4096] N(0,0.02) and read transposed (B k-fast), y [4][16384].
+    Not a size the pages print: it is the skinny case of the wavefront
+    fallback (a few rows, a long k, one large operand streamed once) at a
+    size where HBM rather than launch overhead bounds it."""
+    gx, gw = _gens("skinny_xWt", 2)
+    x = _f32(gx.normal(0.0, 1.0, (4, 4096)))
+    W = _f32(gw.normal(0.0, 0.02, (16384, 4096)))
+    y = np.zeros(4 * 16384, np.float32)
+    return Problem("skinny_xWt", 1, 4, 16384, 4096, 1.0, False,
+                   Operand(x, (0, 4096, 1)), Operand(W, (0, 1, 4096)), Operand(y, (0, 16384, 1)))
+
+
 @dataclasses.dataclass
 class DistProblem:
     """Squared distances D[b,i,j] = |X[b,i,:] - Y[b,j,:]|^2 between the rows
@@ -531,6 +545,7 @@ BUILDERS = {
     "attn_pv_gqa": attn_pv_gqa,
     "attn_fused": attn_fused,
     "attn_fused_causal": attn_fused_causal,
+    "skinny_xWt": skinny_xWt,
 }
 
 

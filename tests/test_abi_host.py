@@ -366,6 +366,45 @@ def test_measured_tile_choices(name, tile):
     assert p["path_name"] == "mfma" and tile in p["kernel"], p
 
 
+def test_skinny_products_split_k_over_wavefronts(monkeypatch):
+    """Products with too few tiles to occupy the SIMDs unsplit and a long k
+    plan the wavefront kernel with k split over several wavefronts of a
+    workgroup (measured on MI355X: 1 x 4096 x 4096 from 100 us unsplit on
+    32 x 32 tiles to 18 us on 16 x 32 tiles split 8 ways); the 16-wide
+    tiles serve dimensions of at most 16; products with enough tiles, or
+    too short a k, stay unsplit.  SGEMM_WAVE_SPLIT forces a split (rounded
+    down to a power of two, capped by the tile), and the describe call
+    reports the wavefronts per workgroup."""
+    gemv = plan(1, 1, 4096, 4096, (0, 4096, 1), (0, 4096, 1), (0, 4096, 1))
+    assert gemv["kernel"] == "wave_w16x32_ak_bn_s8" and gemv["waves"] == 8, gemv
+    assert gemv["tile_m"] == 16 and gemv["tile_n"] == 32 and gemv["workgroups"] == 128
+    tall = plan(1, 4096, 1, 4096, (0, 4096, 1), (0, 1, 1), (0, 1, 1))
+    assert tall["kernel"].startswith("wave_w32x16_") and tall["waves"] == 8, tall
+    few = plan(1, 1, 1000, 16384, (0, 16384, 1), (0, 1, 16384), (0, 1000, 1))
+    assert few["waves"] == 8 and few["workgroups"] == 32, few
+    # Enough tiles to give every SIMD a wavefront: no split.
+    wide = plan(64, 1, 4096, 512, (512, 512, 1), (512 * 4096, 4096, 1), (4096, 4096, 1))
+    assert not re.search(r"_s\d+$", wide["kernel"]), wide
+    # k of 64 is four 16-deep groups: too short to split.
+    short = plan(1, 1, 4096, 64, (0, 64, 1), (0, 4096, 1), (0, 4096, 1))
+    assert not re.search(r"_s\d+$", short["kernel"]), short
+    # 16-wide tiles only for a dimension of at most 16.
+    for m in (24, 64):
+        p = plan(1, m, 4096, 4096, (0, 4096, 1), (0, 4096, 1), (0, 4096, 1))
+        assert p["tile_m"] != 16, p
+    # Forced splits.
+    monkeypatch.setenv("SGEMM_FORCE_TILE", "w32x64")
+    monkeypatch.setenv("SGEMM_WAVE_SPLIT", "16")
+    p = plan(2, 70, 96, 300, (70 * 300, 300, 1), (300 * 96, 96, 1), (70 * 96, 96, 1))
+    assert p["kernel"] == "wave_w32x64_ak_bn_s8" and p["waves"] == 8, p          # capped at 8
+    monkeypatch.setenv("SGEMM_FORCE_TILE", "w16x32")
+    monkeypatch.setenv("SGEMM_WAVE_SPLIT", "5")
+    p = plan(2, 70, 96, 3, (70 * 3, 3, 1), (3 * 96, 96, 1), (70 * 96, 96, 1))
+    assert p["kernel"] == "wave_w16x32_ak_bn_s4" and p["waves"] == 4, p          # rounded down; k of 3
+    monkeypatch.setenv("SGEMM_WAVE_SPLIT", "1")
+    assert plan(1, 1, 4096, 4096, (0, 4096, 1), (0, 4096, 1), (0, 4096, 1))["waves"] == 1
+
+
 def test_accepted_regret_on_the_xT_linear_layer():
     p = _cfg_plan("linear_xT")
     assert p["kernel"].startswith(("mfma_t64x64m16_", "mfma_t128x160_")), p

@@ -63,3 +63,24 @@ def test_traffic_record_hash_covers_every_built_source():
     assert os.path.join("include", "sgemm_strided.h") in seen
     before = bench.kernel_sources_sha256()
     assert before == bench.kernel_sources_sha256() and len(before) == 64
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    """A workload at or above the machine balance (157.3 TFLOP/s over
+    8 TB/s, ~19.7 flops per byte) is held to the matrix-core peak in
+    TFLOP/s; one below it (the skinny product: 2 flops per byte) to the HBM
+    peak in GB/s, with achieved = algorithmic bytes over the launch time."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from strided_fp32_gemm_amd import workloads as wl
+
+    sq = wl.workload("square64")
+    big = bench._roofline_bound(2.0 * 4 * 4096 ** 3, 4 * 4 * 4 * 4096 ** 2, 3.6)
+    assert big["bound"] == "mfma" and big["unit"] == "TFLOP/s" and big["peak"] == 157.3
+    assert abs(big["achieved"] - 2.0 * 4 * 4096 ** 3 / 3.6e-3 / 1e12) < 1e-3
+    flops, nbytes = 2.0 * 4 * 16384 * 4096, 4 * (4 * 4096 + 16384 * 4096 + 4 * 16384)
+    thin = bench._roofline_bound(flops, nbytes, 0.05)
+    assert thin["bound"] == "hbm" and thin["unit"] == "GB/s" and thin["peak"] == 8000.0
+    assert abs(thin["achieved"] - nbytes / 0.05e-3 / 1e9) < 0.1
+    assert abs(thin["frac"] - thin["achieved"] / 8000.0) < 1e-4
+    assert bench._roofline_bound(float(sq.flops), wl.algorithmic_bytes(sq), 0.006)["bound"] == "hbm"

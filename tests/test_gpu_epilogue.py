@@ -119,6 +119,26 @@ def test_general_epilogue_every_family(path):
                 assert e <= TOL, (path, a_major, b_major, beta, row, col, e)
 
 
+@pytest.mark.parametrize("tile", ["w32x32", "w16x64", "w64x16"])
+def test_general_epilogue_wave_split(tile, monkeypatch):
+    """The general epilogue after the split partials are summed: a wave tile
+    forced with k split over 4 wavefronts, beta in {0, -0.75} with and
+    without row and column terms, 16-byte and element C stores."""
+    monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+    monkeypatch.setenv("SGEMM_WAVE_SPLIT", "4")
+    case = 0
+    for (m, n, k), (a_major, b_major) in (((70, 96, 300), ("row", "col")), ((33, 50, 129), ("col", "row"))):
+        for beta in (0.0, -0.75):
+            for row, col in ((False, False), (True, True), (False, True)):
+                case += 1
+                p = _ex_problem(600 + case, 2, m, n, k, a_major, b_major, beta=beta, row=row, col=col)
+                info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
+                assert info["kernel"].startswith("wave_" + tile) and info["waves"] == 4, info
+                got, ref = out(p, gpu_ex(p)), out(p, oracle_ex(p))
+                e = ex_err(p, got, ref)
+                assert e <= TOL, (tile, m, n, k, beta, row, col, e)
+
+
 @pytest.mark.parametrize("path", FAMILIES, ids=FAM_IDS)
 def test_epilogue_layouts_and_vector_strides(path):
     """Column-major C (solved as C^T = B^T A^T, where the row and column

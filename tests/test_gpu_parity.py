@@ -181,15 +181,21 @@ def test_tile_boundaries(mnk, path):
 
 TILE_NAMES = ["t128x128", "t128x64", "t64x128", "t64x64", "t256x128", "t128x160", "t128x80m16",
               "t64x176m16", "t64x64m16", "t128x128m16", "t128x64m16", "t64x128m16", "t64x32m16",
-              "w32x32", "w32x64", "w64x32", "w64x64"]
+              "w32x32", "w32x64", "w64x32", "w64x64", "w16x32", "w16x64", "w32x16", "w64x16"]
+# Most wavefronts per workgroup each wave tile's split variant allows.
+WAVE_MAX_SPLIT = {"w32x32": 16, "w32x64": 8, "w64x32": 8, "w64x64": 8,
+                  "w16x32": 16, "w16x64": 16, "w32x16": 16, "w64x16": 16}
 
 
 @pytest.mark.parametrize("tile", TILE_NAMES)
 def test_every_tile(tile, monkeypatch):
     """Each matrix-core tile configuration, forced, on ragged multi-tile
     shapes in all four transpose cases, with 16-byte loads (aligned shape)
-    and element loads (padded lines), accumulating and not."""
+    and element loads (padded lines), accumulating and not.  Wave tiles run
+    unsplit here (one wavefront per tile); test_wave_split covers the split."""
     monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+    if tile.startswith("w"):
+        monkeypatch.setenv("SGEMM_WAVE_SPLIT", "1")
     # k slices of 32: 3, 3, 2, 7, 2, 1 (the main loop never runs), 4 and 5.
     shapes = [(2, 300, 260, 96, 0), (2, 150, 190, 70, 3), (1, 33, 520, 40, 1), (3, 70, 100, 200, 0),
               (2, 64, 96, 64, 0), (2, 100, 90, 20, 0), (1, 70, 80, 128, 0), (1, 130, 140, 160, 2)]
@@ -204,6 +210,52 @@ def test_every_tile(tile, monkeypatch):
                 got, ref = out(p, gpu_call(p)), out(p, oracle_call(p))
                 e = err_ratio(p, got, ref)
                 assert e <= TOL, (tile, m, n, k, pad, a_major, b_major, acc, e)
+
+
+@pytest.mark.parametrize("split", [2, 5, 16])
+@pytest.mark.parametrize("tile", [t for t in TILE_NAMES if t.startswith("w")])
+def test_wave_split(tile, split, monkeypatch):
+    """Each wave tile with k split over several wavefronts of a workgroup
+    (5 asks for 4; 16 is capped at the tile's limit), forced, on ragged
+    shapes in all four transpose cases, 16-byte and element loads,
+    accumulating and not.  k = 3 and 40 leave some wavefronts no k group at
+    all; k = 1000 gives each several, with a ragged last group.  The same
+    call twice gives the same bits (the partials are summed in a fixed
+    order)."""
+    monkeypatch.setenv("SGEMM_FORCE_TILE", tile)
+    monkeypatch.setenv("SGEMM_WAVE_SPLIT", str(split))
+    want = min(1 << (split.bit_length() - 1), WAVE_MAX_SPLIT[tile])
+    shapes = [(2, 70, 90, 3, 0), (1, 33, 50, 40, 1), (3, 50, 40, 1000, 0), (1, 1, 300, 777, 3),
+              (2, 130, 2, 520, 0)]
+    for batch, m, n, k, pad in shapes:
+        for a_major, b_major in LAYOUTS:
+            for acc in (False, True):
+                p = wl.random_problem(m + 3 * n + k + pad + split, batch, m, n, k, a_major=a_major,
+                                      b_major=b_major, dist="normal", alpha=-0.875, accumulate=acc,
+                                      pad=pad)
+                info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
+                assert tile in info["kernel"] and info["waves"] == want, info
+                assert info["kernel"].endswith(f"_s{want}"), info
+                got = gpu_call(p)
+                assert np.array_equal(got, gpu_call(p)), (tile, split, m, n, k)
+                e = err_ratio(p, out(p, got), out(p, oracle_call(p)))
+                assert e <= TOL, (tile, split, m, n, k, pad, a_major, b_major, acc, e)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 4096, 4096, "row", "row"), (1, 4, 8192, 8192, "row", "col"),
+                                   (1, 4096, 1, 4096, "row", "row"), (2, 3000, 8, 2000, "col", "row"),
+                                   (1, 1, 1000, 16384, "col", "col")])
+def test_skinny_products_split_k(shape):
+    """Skinny products (one or a few rows or columns, long k) plan the
+    wavefront kernel with k split over several wavefronts (planner's own
+    choice) and match the oracle on every output."""
+    batch, m, n, k, a_major, b_major = shape
+    p = wl.random_problem(sum(shape[:4]), batch, m, n, k, a_major=a_major, b_major=b_major, dist="normal",
+                          alpha=0.5, accumulate=True)
+    info = sg.sgemm_plan_describe(*p.call_args(1 << 40, 1 << 41, 1 << 42))
+    assert info["kernel"].startswith("wave_") and info["waves"] > 1, info
+    e = err_ratio(p, out(p, gpu_call(p)), out(p, oracle_call(p)))
+    assert e <= TOL, (shape, info["kernel"], e)
 
 
 @pytest.mark.parametrize("tile", [t for t in TILE_NAMES if t.startswith("t")])

@@ -74,3 +74,31 @@ def test_square_tile_keeps_two_wavefronts_per_simd(stats):
     vec4 = [(n, occ) for n, _, occ in stats["mfma_t9.hip"] if re.search(r"ELi4ELi4ELb[01]EEEvNS_8MfmaArgsE$", n)]
     assert len(vec4) == 8, vec4
     assert all(occ >= 2 for _, occ in vec4), vec4
+
+
+def _wave_table():
+    """kWaveTiles of the planner header: {bm, bn, waves_per_simd, name, rate, max_split}."""
+    text = open(os.path.join(b.CSRC, "plan.hpp")).read()
+    body = text[text.index("kWaveTiles[kNumWaveTiles] = {"):]
+    body = body[:body.index("};")]
+    rows = re.findall(r'\{(\d+), (\d+), (\d+), "(\w+)", ([\d.]+), (\d+)\}', body)
+    return [(int(bm), int(bn), int(w), name, int(s)) for bm, bn, w, name, _, s in rows]
+
+
+def test_wave_tile_table_matches_the_compiled_code(stats):
+    """The planner's wavefront tiles state the occupancy their compiled
+    code has: the unsplit kernel's resident wavefronts per SIMD (the least
+    over its 16 layout instances) is the table's waves_per_simd, and the
+    split kernel fits a workgroup of max_split wavefronts on one CU
+    (max_split / 4 per SIMD)."""
+    table = _wave_table()
+    assert len(table) == 8, table
+    for w, (bm, bn, wps, name, max_split) in enumerate(table):
+        plain, split = [], []
+        for n, _, occ in stats[f"wave_w{w}.hip"]:
+            m = re.search(r"sgemm_waveILi(\d+)E(?:Lb[01]E){4}Lb([01])EEEv", n)
+            if m and int(m.group(1)) == w:
+                (split if m.group(2) == "1" else plain).append(occ)
+        assert len(plain) == 16 and len(split) == 16, (name, len(plain), len(split))
+        assert min(plain) == wps, (name, min(plain), wps)
+        assert 4 * min(split) >= max_split, (name, min(split), max_split)
