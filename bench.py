@@ -265,6 +265,16 @@ def _step_fn(p, dev, stream):
         info = sg.sgemm_plan_describe2(*p.call_args(dA.data_ptr(), dB.data_ptr(), dC.data_ptr()),
                                        num_cus=0)
         return (lambda: sg.sgemm_strided_batched2(*args, stream=stream)), info, (dA, dB, dC)
+    if kind == "splitk":
+        plan = sg.sgemm_splitk_describe(*p.call_args(dA.data_ptr(), dB.data_ptr(), dC.data_ptr()), num_cus=0)
+        W = torch.empty(max(plan["workspace_floats"], 1), device=dev)
+        args = p.call_args(dA, dB, dC)
+        floats = plan["workspace_floats"]
+        info = plan["parts"]
+        if plan["splits"] > 1:
+            info["kernel"] += (f" (k in {plan['splits']} partitions of {plan['kc']}, then the reduction:"
+                               f" {plan['launches']} launches per step)")
+        return (lambda: sg.sgemm_strided_batched_splitk(*args, W, floats, stream=stream)), info, (dA, dB, dC, W)
     info = sg.sgemm_plan_describe(*p.call_args(dA.data_ptr(), dB.data_ptr(), dC.data_ptr()), num_cus=0)
     if kind == "ex":
         dr = torch.from_numpy(p.row.storage).to(dev) if p.row is not None else None

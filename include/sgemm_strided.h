@@ -41,10 +41,12 @@
  *   sgemm_strided_batched[_path]       the product (optionally + C)
  *   sgemm_strided_batched_ex[_path]    + beta*C + per-row and per-column terms
  *   sgemm_strided_batched2[_path]      two batch levels, grouped inputs (KV heads)
+ *   sgemm_strided_batched_splitk       the product with k split across workgroups (caller's workspace)
  *   sgemm_sqnorms, sgemm_pairwise_sqdist   squared norms, squared distances
  *   sgemm_pairwise_sqdist_noalloc      the same distances without a workspace
  *   sgemm_attention[_path]             softmax(alpha Q K^T) V, fused, over two batch levels
- *   sgemm_plan_describe[2], sgemm_attention_describe   the launch a call would make
+ *   sgemm_plan_describe[2], sgemm_splitk_describe, sgemm_attention_describe
+ *                                      the launch a call would make
  *   sgemm_status_string, sgemm_last_error   status text
  * The _path variants force a kernel family (tests, sweeps).
  */
@@ -207,6 +209,45 @@ int sgemm_strided_batched2_path(int64_t nb_outer, int64_t nb_inner, int64_t m, i
                                 int64_t sC_col, int path, void *stream);
 
 /*
+ * The product of sgemm_strided_batched (same arguments, same operation,
+ * C <- alpha * A * B (+ C)) with k split across workgroups, for products
+ * whose output has too few tiles to occupy the GPU and whose k is long (a
+ * weight gradient over many tokens, a small output over a deep
+ * contraction): StaleyNET "GPU Implementation", section "The matrix
+ * product", defines the operation; splitting the sum over k is a
+ * regrouping of it.
+ *
+ * The call enqueues, on `stream`, the partial products of P consecutive k
+ * partitions into `workspace` (partition q of batch entry b at
+ * workspace + (b*P + q)*m*n, rows of n floats), then one kernel that adds
+ * each output's partials in partition order and writes alpha * S (+ C_old).
+ * The planner picks P (1 when splitting does not pay for the extra traffic
+ * and launches; then this is exactly sgemm_strided_batched, same bits) among
+ * the splits whose P*batch*m*n floats fit in workspace_floats; a smaller
+ * workspace gives a smaller split or none, never an error.
+ * sgemm_splitk_describe tells what a call would do and how much workspace
+ * the best split needs.
+ *
+ * Numerics: fp32 throughout, partition order fixed, so repeated calls give
+ * the same bits; they differ from the unsplit product's bits (the k sum is
+ * grouped differently) within the same error bound.
+ * workspace: caller-owned device memory, NULL only with workspace_floats ==
+ * 0 (no split); it must not overlap A, B or C (SGEMM_ERR_C_ALIAS).  Its
+ * contents on entry do not matter and are left overwritten.
+ * Returns an sgemm_status: SGEMM_ERR_INVALID_SIZE if workspace_floats < 0,
+ * SGEMM_ERR_NULL_POINTER if workspace is NULL with workspace_floats > 0,
+ * otherwise as sgemm_strided_batched.
+ */
+int sgemm_strided_batched_splitk(int64_t batch, int64_t m, int64_t n, int64_t k,
+                                 float alpha,
+                                 const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                                 const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                                 int accumulate,
+                                 float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                                 float *workspace, int64_t workspace_floats,
+                                 void *stream);
+
+/*
  * Squared Euclidean norms of a batch of vectors, the terms a distance table
  * adds to its product:
  *
@@ -282,6 +323,33 @@ typedef struct sgemm_plan_info {
     int64_t workgroups;  /* workgroups of the main launch */
     char kernel[64];     /* kernel variant name */
 } sgemm_plan_info;
+
+/* What sgemm_strided_batched_splitk would launch (sgemm_splitk_describe). */
+typedef struct sgemm_splitk_info {
+    int splits;               /* k partitions (1: the unsplit product, no workspace used) */
+    int launches;             /* kernels enqueued: 1 unsplit; 2 or 3 split (a shorter last partition adds one) */
+    int64_t kc;               /* k of each partition but the last */
+    int64_t k_last;           /* k of the last partition */
+    int64_t workspace_floats; /* floats of workspace the plan writes (0 unsplit) */
+    sgemm_plan_info parts;    /* the launch of the partial products (of the product when unsplit) */
+} sgemm_splitk_info;
+
+/*
+ * Validates the arguments as sgemm_strided_batched_splitk does and fills
+ * *info with its plan, without touching the device or dereferencing any
+ * pointer.  workspace_floats < 0 asks what the best split needs (no cap;
+ * workspace is then ignored): info->workspace_floats is the size to pass.
+ * num_cus as for sgemm_plan_describe.  Returns an sgemm_status; *info is
+ * filled only on SGEMM_OK.
+ */
+int sgemm_splitk_describe(int64_t batch, int64_t m, int64_t n, int64_t k,
+                          float alpha,
+                          const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                          const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                          int accumulate,
+                          float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                          const float *workspace, int64_t workspace_floats, int num_cus,
+                          sgemm_splitk_info *info);
 
 /*
  * Validates the arguments exactly as sgemm_strided_batched does and fills

@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     sgemm_pairwise_sqdist_noalloc,
     sgemm_plan_describe,
     sgemm_plan_describe2,
+    sgemm_splitk_describe,
     sgemm_sqnorms,
     sgemm_status_string,
     sgemm_strided_batched,
@@ -38,6 +39,7 @@ from ._binding import (  # noqa: F401
     sgemm_strided_batched2_path,
     sgemm_strided_batched_ex,
     sgemm_strided_batched_ex_path,
+    sgemm_strided_batched_splitk,
     sgemm_strided_batched_path,
 )
 

@@ -30,6 +30,7 @@ STATUS = {
 # Every symbol include/sgemm_strided.h declares.
 EXPORTS = ("sgemm_strided_batched", "sgemm_strided_batched_path", "sgemm_strided_batched_ex",
            "sgemm_strided_batched_ex_path", "sgemm_strided_batched2", "sgemm_strided_batched2_path",
+           "sgemm_strided_batched_splitk", "sgemm_splitk_describe",
            "sgemm_sqnorms", "sgemm_pairwise_sqdist", "sgemm_pairwise_sqdist_noalloc",
            "sgemm_attention", "sgemm_attention_path",
            "sgemm_attention_describe",
@@ -67,6 +68,22 @@ class PlanInfo(ctypes.Structure):
         d = {name: getattr(self, name) for name, _ in self._fields_}
         d["kernel"] = self.kernel.decode()
         d["path_name"] = PATH_NAMES.get(self.path, str(self.path))
+        return d
+
+
+class SplitkInfo(ctypes.Structure):
+    _fields_ = [
+        ("splits", ctypes.c_int),
+        ("launches", ctypes.c_int),
+        ("kc", ctypes.c_int64),
+        ("k_last", ctypes.c_int64),
+        ("workspace_floats", ctypes.c_int64),
+        ("parts", PlanInfo),
+    ]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_ if name != "parts"}
+        d["parts"] = self.parts.as_dict()
         return d
 
 
@@ -144,6 +161,10 @@ def load(path: str = LIB_PATH):
                                                   _vp]
     lib.sgemm_plan_describe.restype = _int
     lib.sgemm_plan_describe.argtypes = _GEMM_ARGS + [_int, _int, ctypes.POINTER(PlanInfo)]
+    lib.sgemm_strided_batched_splitk.restype = _int
+    lib.sgemm_strided_batched_splitk.argtypes = _GEMM_ARGS + [_vp, _i64, _vp]
+    lib.sgemm_splitk_describe.restype = _int
+    lib.sgemm_splitk_describe.argtypes = _GEMM_ARGS + [_vp, _i64, _int, ctypes.POINTER(SplitkInfo)]
     lib.sgemm_plan_describe2.restype = _int
     lib.sgemm_plan_describe2.argtypes = _B2_ARGS + [_int, _int, ctypes.POINTER(PlanInfo)]
     lib.sgemm_status_string.restype = ctypes.c_char_p
@@ -396,6 +417,38 @@ def sgemm_plan_describe(batch, m, n, k, alpha,
     args = _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
                       sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col)
     _check(load().sgemm_plan_describe(*args, int(path), int(num_cus), ctypes.byref(info)))
+    return info.as_dict()
+
+
+def sgemm_strided_batched_splitk(batch, m, n, k, alpha,
+                                 A, sA_batch, sA_row, sA_col,
+                                 B, sB_batch, sB_row, sB_col,
+                                 accumulate,
+                                 C, sC_batch, sC_row, sC_col,
+                                 workspace, workspace_floats,
+                                 stream=None) -> None:
+    """C <- alpha*A*B (+C) with k split across workgroups, partials in
+    `workspace` (device memory of workspace_floats floats) through the C ABI."""
+    args = _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
+                      sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col)
+    _check(load().sgemm_strided_batched_splitk(*args, _ptr(workspace), int(workspace_floats),
+                                               _stream(stream)))
+
+
+def sgemm_splitk_describe(batch, m, n, k, alpha,
+                          A, sA_batch, sA_row, sA_col,
+                          B, sB_batch, sB_row, sB_col,
+                          accumulate,
+                          C, sC_batch, sC_row, sC_col,
+                          workspace=None, workspace_floats=-1, num_cus=256) -> dict:
+    """What sgemm_strided_batched_splitk would launch; workspace_floats < 0
+    asks for the workspace the best split needs (no device access when
+    num_cus > 0)."""
+    info = SplitkInfo()
+    args = _gemm_list(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
+                      sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col)
+    _check(load().sgemm_splitk_describe(*args, _ptr(workspace), int(workspace_floats), int(num_cus),
+                                        ctypes.byref(info)))
     return info.as_dict()
 
 

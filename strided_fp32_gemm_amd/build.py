@@ -24,8 +24,8 @@ OUT = os.path.join(PKG, "libsgemm_strided.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
-SOURCES = ["plan.cpp", "attention.cpp", "abi.cpp", "kernels.hip", "attn_kernel.hip", "strip_kernel.hip",
-           "scratch.hip"] + [f"mfma_t{t}.hip" for t in range(13)] + \
+SOURCES = ["plan.cpp", "attention.cpp", "splitk.cpp", "abi.cpp", "kernels.hip", "attn_kernel.hip",
+           "strip_kernel.hip", "splitk_kernel.hip", "scratch.hip"] + [f"mfma_t{t}.hip" for t in range(13)] + \
     [f"wave_w{t}.hip" for t in range(8)] + [f"persist_p{t}.hip" for t in range(3)]
 
 

@@ -20,6 +20,7 @@
 #include "entry.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "splitk.hpp"
 
 namespace {
 
@@ -405,6 +406,8 @@ int sgemm_strided_batched(int64_t batch, int64_t m, int64_t n, int64_t k, float 
 
 namespace {
 
+void fill_info(const sgemm::Plan &plan, sgemm_plan_info *info);
+
 // Validate and plan `a` without touching the device; fill *info.
 int describe(const sgemm::GemmArgs &a, int path, int num_cus, sgemm_plan_info *info) {
     if (!path_ok(path)) return fail(SGEMM_ERR_INVALID_PATH, "unknown path code");
@@ -419,6 +422,16 @@ int describe(const sgemm::GemmArgs &a, int path, int num_cus, sgemm_plan_info *i
     sgemm::Plan plan;
     st = sgemm::make_plan(a, static_cast<sgemm::Family>(path), num_cus, plan, why);
     if (st != sgemm::kOk) return fail(st, why);
+    fill_info(plan, info);
+    return SGEMM_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// The launch `plan` makes, as the public plan record.
+void fill_info(const sgemm::Plan &plan, sgemm_plan_info *info) {
     std::memset(info, 0, sizeof *info);
     info->path = plan.empty ? SGEMM_PATH_AUTO : static_cast<int>(plan.family);
     info->transposed = plan.transposed ? 1 : 0;
@@ -449,12 +462,90 @@ int describe(const sgemm::GemmArgs &a, int path, int num_cus, sgemm_plan_info *i
     info->fixed_offsets = plan.fixed_offsets ? 1 : 0;
     info->workgroups = plan.empty ? 0 : plan.workgroups;
     std::strncpy(info->kernel, plan.kernel_name.c_str(), sizeof info->kernel - 1);
+}
+
+// Checks of the split-k entry points beyond the product's own: the
+// workspace size, its pointer, and its overlap with A, B and C.
+int check_workspace(const sgemm::GemmArgs &a, const float *workspace, int64_t workspace_floats) {
+    if (workspace_floats < 0) return fail(SGEMM_ERR_INVALID_SIZE, "workspace_floats must be >= 0");
+    if (workspace_floats > 0 && !workspace)
+        return fail(SGEMM_ERR_NULL_POINTER, "workspace is NULL but workspace_floats > 0");
+    if (!workspace || workspace_floats == 0 || a.batch == 0 || a.m == 0 || a.n == 0) return SGEMM_OK;
+    const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
+    const int64_t cs = span3(a.batch, a.sC_batch, a.m, a.sC_row, a.n, a.sC_col);
+    if (ranges_meet(w, workspace_floats, a.C, cs)) return fail(SGEMM_ERR_C_ALIAS, "workspace overlaps C");
+    if (a.k > 0) {
+        const int64_t as = span3(a.batch, a.sA_batch, a.m, a.sA_row, a.k, a.sA_col);
+        const int64_t bs = span3(a.batch, a.sB_batch, a.k, a.sB_row, a.n, a.sB_col);
+        if (ranges_meet(w, workspace_floats, a.A, as)) return fail(SGEMM_ERR_C_ALIAS, "workspace overlaps A");
+        if (ranges_meet(w, workspace_floats, a.B, bs)) return fail(SGEMM_ERR_C_ALIAS, "workspace overlaps B");
+    }
     return SGEMM_OK;
 }
 
 }  // namespace
 
 extern "C" {
+
+int sgemm_strided_batched_splitk(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                                 const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                                 const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                                 int accumulate, float *C, int64_t sC_batch, int64_t sC_row,
+                                 int64_t sC_col, float *workspace, int64_t workspace_floats,
+                                 void *stream) {
+    const sgemm::GemmArgs a = pack(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
+                                   sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col);
+    std::string why;
+    int st = sgemm::validate(a, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    st = check_workspace(a, workspace, workspace_floats);
+    if (st != SGEMM_OK) return st;
+    if (a.batch == 0 || a.m == 0 || a.n == 0) return SGEMM_OK;
+    int cus = 0;
+    st = current_cus(cus, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    sgemm::SplitPlan sp;
+    const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
+    st = sgemm::make_split_plan(a, cus, w, workspace ? workspace_floats : 0, sp, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    st = sgemm::launch_split_plan(a, sp, w, static_cast<hipStream_t>(stream), why);
+    return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
+}
+
+int sgemm_splitk_describe(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
+                          const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,
+                          const float *B, int64_t sB_batch, int64_t sB_row, int64_t sB_col,
+                          int accumulate, float *C, int64_t sC_batch, int64_t sC_row, int64_t sC_col,
+                          const float *workspace, int64_t workspace_floats, int num_cus,
+                          sgemm_splitk_info *info) {
+    if (!info) return fail(SGEMM_ERR_NULL_POINTER, "info is NULL");
+    const sgemm::GemmArgs a = pack(batch, m, n, k, alpha, A, sA_batch, sA_row, sA_col, B, sB_batch,
+                                   sB_row, sB_col, accumulate, C, sC_batch, sC_row, sC_col);
+    std::string why;
+    int st = sgemm::validate(a, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    const bool query = workspace_floats < 0;   // no cap: the size the best split needs
+    if (!query) {
+        st = check_workspace(a, workspace, workspace_floats);
+        if (st != SGEMM_OK) return st;
+    }
+    if (num_cus <= 0) {
+        st = current_cus(num_cus, why);
+        if (st != sgemm::kOk) return fail(st, why);
+    }
+    sgemm::SplitPlan sp;
+    st = sgemm::make_split_plan(a, num_cus, query ? 0 : reinterpret_cast<uintptr_t>(workspace),
+                                query ? -1 : (workspace ? workspace_floats : 0), sp, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    std::memset(info, 0, sizeof *info);
+    info->splits = sp.splits;
+    info->kc = sp.splits > 1 ? sp.kc : k;
+    info->k_last = sp.splits > 1 ? sp.k_last : k;
+    info->workspace_floats = sp.splits > 1 ? sp.workspace_floats : 0;
+    info->launches = sp.whole.empty ? 0 : sp.splits == 1 ? 1 : (sp.full < sp.splits ? 3 : 2);
+    fill_info(sp.splits > 1 ? sp.parts : sp.whole, &info->parts);
+    return SGEMM_OK;
+}
 
 int sgemm_plan_describe(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha,
                         const float *A, int64_t sA_batch, int64_t sA_row, int64_t sA_col,

@@ -442,6 +442,7 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
             }
         }
     }
+    if (best >= 0) p.cost = best_cost;
     if (best >= 0 && best_strip) {
         const StripCfg &c = kStripTiles[best];
         p.family = Family::Mfma;
@@ -493,6 +494,9 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
         p.tiles_n = (p.n + 63) / 64;
         int64_t tiles = p.batch * p.tiles_m * p.tiles_n;
         p.workgroups = std::min<int64_t>(tiles, 65536);
+        // Plain fp32 FMA at a fifth of the vector peak (256 FLOP per CU cycle).
+        p.cost = 2.0 * double(p.batch) * double(p.m) * double(p.n) * double(std::max<int64_t>(p.k, 1)) /
+                 (256.0 * 0.2 * double(std::max(num_cus, 1)));
         p.kernel_name = std::string("generic_t64x64") + (p.accumulate ? "_acc" : "") +
                         (p.row_add || p.col_add ? "_vec" : "");
     }

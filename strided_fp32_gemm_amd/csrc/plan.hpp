@@ -302,6 +302,7 @@ struct Plan {
     int64_t sC_b = 0, sC_m = 0, sC_n = 0;
     int64_t tiles_m = 0, tiles_n = 0, workgroups = 0;  // workgroups < tiles for the persistent kernel
     int ksplit = 1;            // WAVE family: wavefronts per workgroup sharing one tile's k
+    double cost = 0.0;         // the cost model's estimate for the chosen kernel (cycles)
     std::string kernel_name;
 };
 

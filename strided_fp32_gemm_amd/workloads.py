@@ -35,12 +35,15 @@ ROOT_SEED = 2024
 # Benchmark workloads.
 WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
              "linear_bwd_dx", "linear_bwd_dw", "linear_xT", "linear_bias", "sqdist",
-             "attn_qk_gqa", "attn_pv_gqa", "attn_fused", "attn_fused_causal", "skinny_xWt")
+             "attn_qk_gqa", "attn_pv_gqa", "attn_fused", "attn_fused_causal", "skinny_xWt",
+             "linear_dw_deep")
 # Entry point each workload goes through: "plain" (sgemm_strided_batched),
 # "ex" (sgemm_strided_batched_ex), "dist" (sgemm_pairwise_sqdist) or
-# "batched2" (sgemm_strided_batched2) or "attention" (sgemm_attention).
+# "batched2" (sgemm_strided_batched2), "attention" (sgemm_attention) or
+# "splitk" (sgemm_strided_batched_splitk, with the workspace its plan asks for).
 KINDS = {"linear_bias": "ex", "sqdist": "dist", "attn_qk_gqa": "batched2",
-         "attn_pv_gqa": "batched2", "attn_fused": "attention", "attn_fused_causal": "attention"}
+         "attn_pv_gqa": "batched2", "attn_fused": "attention", "attn_fused_causal": "attention",
+         "linear_dw_deep": "splitk"}
 
 
 def kind(name: str) -> str:
@@ -51,7 +54,7 @@ def kind(name: str) -> str:
 # layer's backward pass share one draw of dy, W and x).
 SEED_NAMES = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
               "linear_bwd", "linear_xT", "linear_bias", "sqdist", "attn_qk_gqa", "attn_pv_gqa",
-              "attn_fused", "skinny_xWt")
+              "attn_fused", "skinny_xWt", "linear_dw_deep")
 
 
 @dataclasses.dataclass
@@ -310,6 +313,21 @@ def skinny_xWt() -> Problem:
                    Operand(x, (0, 4096, 1)), Operand(W, (0, 1, 4096)), Operand(y, (0, 16384, 1)))
 
 
+def linear_dw_deep() -> Problem:
+    """The weight gradient of a narrow layer over many tokens: dW = dy^T x
+    (the right gradient A^T dC of "PyTorch demystified 3", Opt. 4), dy
+    [16384][256] N(0,1) read transposed (A[i][p] = dy[p][i], m-fast), x
+    [16384][256] N(0,1) row-major (n-fast), dW [256][256].  Not a size the
+    pages print: a small output (16 tiles of 64 x 64) over a deep
+    contraction, the case the split-k entry point serves."""
+    gy, gx = _gens("linear_dw_deep", 2)
+    dy = _f32(gy.normal(0.0, 1.0, (16384, 256)))
+    x = _f32(gx.normal(0.0, 1.0, (16384, 256)))
+    dW = np.zeros(256 * 256, np.float32)
+    return Problem("linear_dw_deep", 1, 256, 256, 16384, 1.0, False,
+                   Operand(dy, (0, 1, 256)), Operand(x, (0, 256, 1)), Operand(dW, (0, 256, 1)))
+
+
 @dataclasses.dataclass
 class DistProblem:
     """Squared distances D[b,i,j] = |X[b,i,:] - Y[b,j,:]|^2 between the rows
@@ -546,6 +564,7 @@ BUILDERS = {
     "attn_fused": attn_fused,
     "attn_fused_causal": attn_fused_causal,
     "skinny_xWt": skinny_xWt,
+    "linear_dw_deep": linear_dw_deep,
 }
 
 

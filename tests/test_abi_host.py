@@ -283,6 +283,49 @@ def test_extended_entry_points_validate_before_the_device():
 
 
 
+def test_splitk_validates_and_plans_before_the_device(monkeypatch):
+    """The split-k entry point checks the product's arguments and its
+    workspace (size >= 0, NULL only when empty, no overlap with A, B or C)
+    before any device call, and its describe call plans without a device:
+    deep contractions into small outputs are split (1 x 128 x 128 x 65536
+    into 64 partitions of 1024, 64x64 tiles, the reduction as the second
+    launch), large outputs and short k are not, a shorter last partition
+    adds a launch, and a workspace cap gives the largest split that fits
+    (the partials take splits * batch * m * n floats)."""
+    run = lambda ws, floats, **kw: sg.sgemm_strided_batched_splitk(
+        1, 64, 64, kw.get("k", 4096), 1.0, PA, 0, 4096, 1, PB, 0, 64, 1, 0, PC, 0, 64, 1, ws, floats)
+    assert status_of(lambda: run(None, -1)) == -1
+    assert status_of(lambda: run(None, 100)) == -3
+    assert status_of(lambda: run(PA + 64, 1 << 16)) == -4      # workspace inside A
+    assert status_of(lambda: run(PB - 64, 1 << 16)) == -4      # reaching into B
+    assert status_of(lambda: run(PC, 4096)) == -4              # on C
+    assert status_of(lambda: run(PA + (1 << 30), 100, k=-1)) == -1
+    sg.sgemm_strided_batched_splitk(0, 64, 64, 64, 1.0, None, 0, 64, 1, None, 0, 64, 1, 0, None, 0, 64, 1,
+                                    None, 0)                      # empty: nothing to do
+
+    def d(batch, m, n, k, ws=-1, acc=0):
+        return sg.sgemm_splitk_describe(batch, m, n, k, 1.0, PA, m * k, k, 1, PB, k * n, 1, k, acc,
+                                        PC, m * n, n, 1, workspace=(1 << 44) if ws >= 0 else None,
+                                        workspace_floats=ws)
+    deep = d(1, 128, 128, 65536)
+    assert (deep["splits"], deep["kc"], deep["k_last"], deep["launches"]) == (64, 1024, 1024, 2), deep
+    assert deep["workspace_floats"] == 64 * 128 * 128
+    assert deep["parts"]["kernel"].startswith("mfma_t64x64m16_"), deep
+    assert deep["parts"]["workgroups"] == 64 * 4
+    for big in (d(4, 4096, 4096, 4096), d(1, 256, 256, 200)):
+        assert big["splits"] == 1 and big["launches"] == 1 and big["workspace_floats"] == 0, big
+    ragged = d(1, 128, 128, 65536 - 100)
+    assert ragged["splits"] > 1 and ragged["k_last"] < ragged["kc"] and ragged["launches"] == 3, ragged
+    capped = d(1, 128, 128, 65536, ws=5 * 128 * 128)
+    assert capped["splits"] == 4 and capped["workspace_floats"] == 4 * 128 * 128, capped
+    assert d(1, 128, 128, 65536, ws=0)["splits"] == 1
+    monkeypatch.setenv("SGEMM_SPLITK", "3")
+    forced = d(2, 70, 96, 1000)
+    assert (forced["splits"], forced["kc"], forced["k_last"], forced["launches"]) == (3, 384, 232, 3), forced
+    monkeypatch.setenv("SGEMM_SPLITK", "1")
+    assert d(1, 128, 128, 65536)["splits"] == 1
+
+
 def test_two_level_batch_validates_before_the_device():
     """Two batch levels with groups: sizes, groups, strides, C's distinctness
     across both levels and overlap with the inputs are checked before any

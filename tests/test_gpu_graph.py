@@ -1,7 +1,9 @@
 """The entry points under HIP graph capture: a strided batched product that
-accumulates, a fused causal attention and the allocation-free distance entry
-point, captured together on one stream and replayed several times, with eager
-work (resetting C, a host round trip) between the replays.  Every replay must
+accumulates, a fused causal attention, the allocation-free distance entry
+point and a split-k product (its partial products, a shorter last
+partition and the reduction: three launches through a caller workspace),
+captured together on one stream and replayed several times, with eager work
+(resetting C, a host round trip) between the replays.  Every replay must
 give the eager results bit for bit: the library enqueues only kernels (no
 allocation, no memset), so a replay is the same launches on the same bytes.
 """
@@ -41,11 +43,19 @@ def test_graph_replays_match_eager_calls():
     do = dev(attn.O.storage)
     dX, dY = dev(X), dev(Y)
     dD = torch.zeros(batch * m * n, device="cuda")
+    deep = wl.random_problem(5104, 1, 96, 96, 16284, a_major="col", b_major="row", dist="normal",
+                             alpha=0.5, accumulate=True)
+    plan = sg.sgemm_splitk_describe(*deep.call_args(1 << 40, 1 << 41, 1 << 42))
+    assert plan["splits"] > 1 and plan["launches"] == 3, plan
+    dA2, dB2, E0 = dev(deep.A.storage), dev(deep.B.storage), dev(deep.C.storage)
+    dE = E0.clone()
+    W = torch.empty(plan["workspace_floats"], device="cuda")
 
     def enqueue(stream):
         sg.sgemm_strided_batched(*gemm.call_args(dA, dB, dC), stream=stream)
         sg.sgemm_attention(*attn.call_args(dq, dk, dv, do), stream=stream)
         sg.sgemm_pairwise_sqdist_noalloc(batch, m, n, k, dX, *sX, dY, *sY, dD, *sD, stream=stream)
+        sg.sgemm_strided_batched_splitk(*deep.call_args(dA2, dB2, dE), W, W.numel(), stream=stream)
 
     # Eager results (this also does any one-time set-up outside the capture).
     side = torch.cuda.Stream()
@@ -54,10 +64,11 @@ def test_graph_replays_match_eager_calls():
         enqueue(side)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    want = [dC.cpu().numpy(), do.cpu().numpy(), dD.cpu().numpy()]
+    want = [dC.cpu().numpy(), do.cpu().numpy(), dD.cpu().numpy(), dE.cpu().numpy()]
 
     graph = torch.cuda.CUDAGraph()
     dC.copy_(C0)
+    dE.copy_(E0)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
         enqueue(torch.cuda.current_stream())
@@ -65,11 +76,13 @@ def test_graph_replays_match_eager_calls():
         # Eager work between replays: C back to its initial values (the
         # product accumulates), the other outputs poisoned, a host round trip.
         dC.copy_(C0)
+        dE.copy_(E0)
         do.fill_(float("nan"))
         dD.fill_(float("nan"))
+        W.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = [dC.cpu().numpy(), do.cpu().numpy(), dD.cpu().numpy()]
-        for name, g_, w_ in zip(("product", "attention", "distances"), got, want):
+        got = [dC.cpu().numpy(), do.cpu().numpy(), dD.cpu().numpy(), dE.cpu().numpy()]
+        for name, g_, w_ in zip(("product", "attention", "distances", "split-k product"), got, want):
             assert np.array_equal(g_, w_), (replay, name)
