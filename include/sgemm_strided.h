@@ -20,8 +20,11 @@
  *
  * Memory and ownership: A, B and C are device pointers allocated by the
  * caller (e.g. by PyTorch); the library allocates nothing, keeps no
- * per-call state and never frees caller memory.  It may be called from
- * several host threads on different streams.
+ * per-call state and never frees caller memory.  It remembers, per host
+ * thread, the plans of the last few products it planned (a plan depends on
+ * the arguments and the device's CU count alone), so a repeated call skips
+ * validation and planning.  It may be called from several host threads on
+ * different streams.
  *
  * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL means the
  * null stream) and the call returns without synchronising.  Argument errors

@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -76,18 +77,80 @@ sgemm::GemmArgs pack(int64_t batch, int64_t m, int64_t n, int64_t k, float alpha
 
 bool path_ok(int path) { return path >= SGEMM_PATH_AUTO && path <= SGEMM_PATH_GENERIC; }
 
+uint32_t bits(float x) {
+    uint32_t u;
+    std::memcpy(&u, &x, sizeof u);
+    return u;
+}
+
+// Every field of two argument sets equal (floats bit for bit).
+bool same_args(const sgemm::GemmArgs &x, const sgemm::GemmArgs &y) {
+    return x.batch == y.batch && x.m == y.m && x.n == y.n && x.k == y.k && bits(x.alpha) == bits(y.alpha) &&
+           x.A == y.A && x.sA_batch == y.sA_batch && x.sA_row == y.sA_row && x.sA_col == y.sA_col &&
+           x.B == y.B && x.sB_batch == y.sB_batch && x.sB_row == y.sB_row && x.sB_col == y.sB_col &&
+           x.accumulate == y.accumulate && x.C == y.C && x.sC_batch == y.sC_batch && x.sC_row == y.sC_row &&
+           x.sC_col == y.sC_col && bits(x.beta) == bits(y.beta) && x.row_add == y.row_add &&
+           x.sR_batch == y.sR_batch && x.sR_row == y.sR_row && x.col_add == y.col_add &&
+           x.sL_batch == y.sL_batch && x.sL_col == y.sL_col && x.inner == y.inner && x.sA_inner == y.sA_inner &&
+           x.gA == y.gA && x.sB_inner == y.sB_inner && x.gB == y.gB && x.sC_inner == y.sC_inner;
+}
+
+// The plans of the last few products planned on this thread.  A plan is a
+// function of the arguments, the path and the CU count alone, and only
+// arguments that validated are stored, so a call that repeats one (the same
+// tensors in a loop) skips validation and planning on the host, about 2.5 us.
+// Tuning overrides in the environment (which the planner reads) bypass it.
+struct CachedPlan {
+    sgemm::GemmArgs args{};
+    int path = -1, cus = 0;
+    sgemm::Plan plan;
+};
+constexpr int kPlanCacheSize = 8;
+thread_local CachedPlan g_plans[kPlanCacheSize];
+thread_local int g_plan_next = 0;
+
+struct CachedSplit {
+    sgemm::GemmArgs args{};
+    int cus = 0;
+    uintptr_t workspace = 0;
+    int64_t floats = -1;
+    sgemm::SplitPlan plan;
+};
+thread_local CachedSplit g_splits[kPlanCacheSize];
+thread_local int g_split_next = 0;
+
+bool planner_overrides() {
+    return std::getenv("SGEMM_FORCE_TILE") || std::getenv("SGEMM_PERSIST_WGS") || std::getenv("SGEMM_WAVE_SPLIT");
+}
+
 // Validate, plan and enqueue one product.
 int run_gemm(const sgemm::GemmArgs &a, int path, void *stream) {
     std::string why;
+    int cus = 0;
+    const bool cacheable = !planner_overrides();
+    if (cacheable && current_cus(cus, why) == sgemm::kOk) {
+        for (const CachedPlan &c : g_plans)
+            if (c.path == path && c.cus == cus && same_args(c.args, a)) {
+                const int st = sgemm::launch_plan(c.plan, static_cast<hipStream_t>(stream), why);
+                return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
+            }
+    }
     int st = sgemm::validate(a, why);
     if (st != sgemm::kOk) return fail(st, why);
     if (a.batch == 0 || a.m == 0 || a.n == 0) return SGEMM_OK;
-    int cus = 0;
     st = current_cus(cus, why);
     if (st != sgemm::kOk) return fail(st, why);
     sgemm::Plan plan;
     st = sgemm::make_plan(a, static_cast<sgemm::Family>(path), cus, plan, why);
     if (st != sgemm::kOk) return fail(st, why);
+    if (cacheable) {
+        CachedPlan &c = g_plans[g_plan_next];
+        g_plan_next = (g_plan_next + 1) % kPlanCacheSize;
+        c.args = a;
+        c.path = path;
+        c.cus = cus;
+        c.plan = plan;
+    }
     st = sgemm::launch_plan(plan, static_cast<hipStream_t>(stream), why);
     if (st != sgemm::kOk) return fail(st, why);
     return SGEMM_OK;
@@ -504,10 +567,29 @@ int sgemm_strided_batched_splitk(int64_t batch, int64_t m, int64_t n, int64_t k,
     int cus = 0;
     st = current_cus(cus, why);
     if (st != sgemm::kOk) return fail(st, why);
-    sgemm::SplitPlan sp;
     const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
-    st = sgemm::make_split_plan(a, cus, w, workspace ? workspace_floats : 0, sp, why);
+    const int64_t floats = workspace ? workspace_floats : 0;
+    // The split plan (up to nine product plans) is cached per thread like
+    // the product's, keyed by the workspace as well.
+    const bool cacheable = !planner_overrides() && !std::getenv("SGEMM_SPLITK");
+    if (cacheable)
+        for (const CachedSplit &c : g_splits)
+            if (c.cus == cus && c.workspace == w && c.floats == floats && same_args(c.args, a)) {
+                st = sgemm::launch_split_plan(a, c.plan, w, static_cast<hipStream_t>(stream), why);
+                return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
+            }
+    sgemm::SplitPlan sp;
+    st = sgemm::make_split_plan(a, cus, w, floats, sp, why);
     if (st != sgemm::kOk) return fail(st, why);
+    if (cacheable) {
+        CachedSplit &c = g_splits[g_split_next];
+        g_split_next = (g_split_next + 1) % kPlanCacheSize;
+        c.args = a;
+        c.cus = cus;
+        c.workspace = w;
+        c.floats = floats;
+        c.plan = sp;
+    }
     st = sgemm::launch_split_plan(a, sp, w, static_cast<hipStream_t>(stream), why);
     return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
 }

@@ -108,6 +108,20 @@ def test_forced_splits_every_layout(splits, monkeypatch):
                     assert np.array_equal(got[mask], p.C.storage[mask])
 
 
+def test_shared_weight_and_integer_data(monkeypatch):
+    """A B shared by every batch entry (batch stride 0, the partitions
+    advance along its k only), and integer data in [-3, 3], where every
+    partial sum and their total are exact in fp32, so the split result
+    equals the oracle bit for bit."""
+    monkeypatch.setenv("SGEMM_SPLITK", "4")
+    for a_major, b_major in LAYOUTS:
+        p = wl.random_problem(93, 3, 80, 72, 1100, a_major=a_major, b_major=b_major, dist="int",
+                              b_broadcast=True, accumulate=True)
+        got, info = split_call(p)
+        assert info["splits"] == 4 and p.B.strides[0] == 0, info
+        assert np.array_equal(out(p, got), out(p, oracle_call(p))), (a_major, b_major)
+
+
 def test_column_major_c_and_determinism(monkeypatch):
     """A column-major C (element-wise reduction with a row stride of 1) and
     two calls with the same arguments giving the same bits."""
