@@ -102,8 +102,10 @@ int make_split_plan(const GemmArgs &a, int num_cus, uintptr_t workspace, int64_t
         int64_t floats;
         if (!mul64(outputs, splits, floats)) break;
         if (workspace_floats >= 0 && floats > workspace_floats) continue;
-        const int full = int(a.k / kc);
+        const int full = int(a.k / kc);   // at most splits <= P
         const int64_t k_last = a.k - (splits - 1) * kc;
+        int64_t flat;
+        if (!mul64(a.batch, full, flat)) break;
         Plan parts, tail;
         std::string ignore;
         if (make_plan(parts_args(a, W, int(splits), full, kc), Family::Auto, num_cus, parts, ignore) != kOk)
