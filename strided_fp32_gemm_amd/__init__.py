@@ -12,6 +12,7 @@ runs in hand-written HIP kernels behind a C ABI (include/sgemm_strided.h);
 this package only marshals arguments.  PyTorch is used for device memory and
 streams.
 """
+from . import _binding  # noqa: F401
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
@@ -53,7 +54,7 @@ def _strides3(t, name):
 
 
 def sgemm(A, B, C, alpha: float = 1.0, accumulate: bool = False, path: int = PATH_AUTO,
-          stream=None):
+          stream=None, splitk: bool = False):
     """C <- alpha*A@B (+C) for torch float32 views on one GPU.
 
     A is [batch,] m x k, B is [batch,] k x n, C is [batch,] m x n; any of them
@@ -61,6 +62,11 @@ def sgemm(A, B, C, alpha: float = 1.0, accumulate: bool = False, path: int = PAT
     strides, no copy).  A 2-D operand next to 3-D ones is broadcast over the
     batch (batch stride 0).  Runs on ``stream`` (default: torch's current
     stream) and returns C.
+
+    splitk=True goes through sgemm_strided_batched_splitk (k split across
+    workgroups, for small outputs over a deep k): the workspace the library's
+    plan asks for is allocated here with torch (the library allocates
+    nothing); ``path`` does not apply.
     """
     import torch
 
@@ -91,6 +97,17 @@ def sgemm(A, B, C, alpha: float = 1.0, accumulate: bool = False, path: int = PAT
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
     with torch.cuda.device(C.device):
-        sgemm_strided_batched_path(batch, m, n, k, alpha, A, *sa, B, *sb, accumulate, C, *sc,
-                                   path=path, stream=stream)
+        if splitk:
+            plan = sgemm_splitk_describe(batch, m, n, k, alpha, A, *sa, B, *sb, accumulate, C, *sc, num_cus=0)
+            floats = plan["workspace_floats"]
+            work = torch.empty(floats, dtype=torch.float32, device=C.device) if floats else None
+            sgemm_strided_batched_splitk(batch, m, n, k, alpha, A, *sa, B, *sb, accumulate, C, *sc,
+                                         work, floats, stream=stream)
+            if work is not None:
+                # The workspace must outlive the enqueued launches on `stream`.
+                work.record_stream(stream if isinstance(stream, torch.cuda.Stream) else
+                                   torch.cuda.ExternalStream(_binding._stream(stream)))
+        else:
+            sgemm_strided_batched_path(batch, m, n, k, alpha, A, *sa, B, *sb, accumulate, C, *sc,
+                                       path=path, stream=stream)
     return C

@@ -190,3 +190,26 @@ def test_workload_full_size(name):
     assert np.array_equal(got, split_call(p, poison=False)[0])
     e = err_ratio(p, out(p, got), out(p, oracle_call(p)))
     assert e <= TOL, (name, info["splits"], e)
+
+
+def test_torch_helper_splitk():
+    """sgemm(..., splitk=True) on torch views: the weight gradient dy^T x
+    (dy.t() passed as a view, no copy), on a side stream, accumulating; the
+    helper allocates the workspace the plan asks for with torch."""
+    g = torch.Generator().manual_seed(5)
+    dy = torch.randn(12288, 192, generator=g)
+    x = torch.randn(12288, 160, generator=g)
+    c0 = torch.randn(192, 160, generator=g)
+    ref = (dy.double().t() @ x.double()) * 0.5 + c0.double()
+    dyd, xd = dy.cuda(), x.cuda()
+    C = c0.cuda()
+    plan = sg.sgemm_splitk_describe(1, 192, 160, 12288, 0.5, dyd, 0, 1, 192, xd, 0, 160, 1, 1, C, 0, 160, 1)
+    assert plan["splits"] > 1, plan
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sg.sgemm(dyd.t(), xd, C, alpha=0.5, accumulate=True, splitk=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    e = float((C.cpu().double() - ref).abs().max()) / (12288 * float(dy.abs().max()) * float(x.abs().max()))
+    assert e <= TOL, e
