@@ -156,10 +156,17 @@ def cpu_baseline_attention(p, seconds: float) -> dict:
     while t < seconds / 8 and heads < total:
         heads, t = run(min(total, heads * 4) if heads * 4 <= p.nb_inner
                        else min(total, max(p.nb_inner, heads * 4) // p.nb_inner * p.nb_inner))
-    flops = 4.0 * p.d * p.visible_pairs * heads
+    reps = 1
+    if heads == total and t < seconds / 4:
+        # The whole call is quick (a decode step): repeat it to fill the time.
+        reps = max(2, int(seconds / 2 / max(t, 1e-6)))
+        t = sum(run(heads)[1] for _ in range(reps))
+    flops = 4.0 * p.d * p.visible_pairs * heads * reps
+    sample = f"all {p.tq} query rows of the first {heads} (sequence, head) pairs"
+    if reps > 1:
+        sample = f"the whole call ({heads} (sequence, head) pairs) x {reps} repetitions"
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", **host_cores(threads), "kind": "oracle",
-            "sample": f"all {p.tq} query rows of the first {heads} (sequence, head) pairs "
-                      f"({flops / 1e9:.2f} GFLOP in {t:.1f} s)"}
+            "sample": f"{sample} ({flops / 1e9:.2f} GFLOP in {t:.1f} s)"}
 
 
 def cpu_baseline(p, seconds: float) -> dict:
@@ -167,7 +174,7 @@ def cpu_baseline(p, seconds: float) -> dict:
     the run takes roughly `seconds`."""
     import oracle
     from strided_fp32_gemm_amd import workloads as wl
-    if wl.kind(p.name) == "attention":
+    if wl.kind(p.name) in ("attention", "attention_splitkv"):
         return cpu_baseline_attention(p, seconds)
     threads = oracle.num_threads()
     kind = wl.kind(p.name)
@@ -258,6 +265,16 @@ def _step_fn(p, dev, stream):
         info = sg.sgemm_attention_describe(*p.call_args(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                                         do.data_ptr()))
         return (lambda: sg.sgemm_attention(*args, stream=stream)), info, (dq, dk, dv, do)
+    if kind == "attention_splitkv":
+        dq, dk, dv, do = (torch.from_numpy(x.storage).to(dev) for x in (p.Q, p.K, p.V, p.O))
+        args = p.call_args(dq, dk, dv, do)
+        plan = sg.sgemm_attention_splitkv_describe(*p.call_args(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                                                do.data_ptr()), num_cus=0)
+        floats = plan["workspace_floats"]
+        W = torch.empty(max(floats, 1), device=dev)
+        info = {"kernel": f"attn_splitkv_d64 (keys in {plan['chunks']} chunks of {plan['chunk_keys']}, then the"
+                          f" merge: 2 launches per step)", "workgroups": None}
+        return (lambda: sg.sgemm_attention_splitkv(*args, W, floats, stream=stream)), info, (dq, dk, dv, do, W)
     dA, dB = torch.from_numpy(p.A.storage).to(dev), torch.from_numpy(p.B.storage).to(dev)
     dC = torch.from_numpy(p.C.storage).to(dev)
     if kind == "batched2":
@@ -422,7 +439,7 @@ def _roofline_bound(flops: float, alg_bytes: int, mean_ms: float) -> dict:
 def _config(p, info) -> dict:
     from strided_fp32_gemm_amd import workloads as wl
 
-    if wl.kind(p.name) == "attention":
+    if wl.kind(p.name) in ("attention", "attention_splitkv"):
         return {"workload": p.name, "op": "softmax(alpha Q K^T) V, fused", "nb_outer": p.nb_outer,
                 "nb_inner": p.nb_inner, "tq": p.tq, "tk": p.tk, "d": p.d, "g": p.g, "alpha": p.alpha,
                 "causal": bool(p.causal),

@@ -48,6 +48,7 @@
  *   sgemm_sqnorms, sgemm_pairwise_sqdist   squared norms, squared distances
  *   sgemm_pairwise_sqdist_noalloc      the same distances without a workspace
  *   sgemm_attention[_path]             softmax(alpha Q K^T) V, fused, over two batch levels
+ *   sgemm_attention_splitkv[_describe] the same for decode, keys split across the GPU (caller's workspace)
  *   sgemm_plan_describe[2], sgemm_splitk_describe, sgemm_attention_describe
  *                                      the launch a call would make
  *   sgemm_status_string, sgemm_last_error   status text
@@ -438,6 +439,59 @@ int sgemm_attention_path(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t
 /* The plan of a sgemm_attention_path call (validated the same way, no
  * device access): tile_m = query rows per workgroup.  Returns an
  * sgemm_status. */
+/*
+ * sgemm_attention for decode-shaped calls (few queries per head, a long KV
+ * cache), with the keys split across the GPU through a caller workspace.
+ * Same arguments, operation and status codes as sgemm_attention, plus the
+ * workspace.  The g query heads of a KV head and their tq queries are
+ * stacked as the rows of one 16-row matrix-core tile (g * tq <= 16; the rvllm
+ * post, "Matmuls go to cuBLAS", stacks a group's query heads as rows of one
+ * product), so K and V are read once per group; the keys are cut into
+ * chunks, one wavefront per (outer, KV head, chunk) forms that chunk's
+ * online softmax (unnormalised output rows, reference maxima, weight sums:
+ * kael book ch. 09 and the rvllm post's softmax in three steps, done in one
+ * pass) into `workspace`, and a second launch merges each output row's
+ * chunks in chunk order: O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,
+ * M = max_c m_c.  Results are reproducible bit for bit; they differ from
+ * sgemm_attention's (the keys' sum is grouped by chunk) within the same
+ * bound.
+ * Serves head dimension 64, unit column strides and 16-byte aligned rows
+ * with g * tq <= 16 (g capped at nb_inner); any other call, or a workspace
+ * too small for one chunk per (outer, KV head), runs as sgemm_attention.
+ * workspace: caller-owned device memory of workspace_floats floats, NULL
+ * only with workspace_floats == 0, not overlapping Q, K, V or O
+ * (SGEMM_ERR_C_ALIAS); sgemm_attention_splitkv_describe gives the size.
+ * Returns an sgemm_status.
+ */
+int sgemm_attention_splitkv(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                            float alpha, int causal,
+                            const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row, int64_t sQ_col,
+                            const float *K, int64_t sK_outer, int64_t sK_inner, int64_t g,
+                            int64_t sK_row, int64_t sK_col,
+                            const float *V, int64_t sV_outer, int64_t sV_inner, int64_t sV_row, int64_t sV_col,
+                            float *O, int64_t sO_outer, int64_t sO_inner, int64_t sO_row, int64_t sO_col,
+                            float *workspace, int64_t workspace_floats,
+                            void *stream);
+
+/*
+ * The split sgemm_attention_splitkv would make with a workspace of
+ * workspace_floats floats (< 0: no cap, a size query): *chunks key chunks
+ * per (outer, KV head) of *chunk_keys keys, *floats_used floats of
+ * workspace (0 and 0: not split).  Validates like sgemm_attention; touches
+ * no device when num_cus > 0.  Returns an sgemm_status.
+ */
+int sgemm_attention_splitkv_describe(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                                     float alpha, int causal,
+                                     const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row,
+                                     int64_t sQ_col,
+                                     const float *K, int64_t sK_outer, int64_t sK_inner, int64_t g,
+                                     int64_t sK_row, int64_t sK_col,
+                                     const float *V, int64_t sV_outer, int64_t sV_inner, int64_t sV_row,
+                                     int64_t sV_col,
+                                     float *O, int64_t sO_outer, int64_t sO_inner, int64_t sO_row, int64_t sO_col,
+                                     int64_t workspace_floats, int num_cus,
+                                     int64_t *chunks, int64_t *chunk_keys, int64_t *floats_used);
+
 int sgemm_attention_describe(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
                              float alpha, int causal,
                              const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row,

@@ -27,6 +27,8 @@ from ._binding import (  # noqa: F401
     sgemm_attention,
     sgemm_attention_describe,
     sgemm_attention_path,
+    sgemm_attention_splitkv,
+    sgemm_attention_splitkv_describe,
     sgemm_last_error,
     sgemm_pairwise_sqdist,
     sgemm_pairwise_sqdist_noalloc,

@@ -32,7 +32,7 @@ EXPORTS = ("sgemm_strided_batched", "sgemm_strided_batched_path", "sgemm_strided
            "sgemm_strided_batched_ex_path", "sgemm_strided_batched2", "sgemm_strided_batched2_path",
            "sgemm_strided_batched_splitk", "sgemm_splitk_describe",
            "sgemm_sqnorms", "sgemm_pairwise_sqdist", "sgemm_pairwise_sqdist_noalloc",
-           "sgemm_attention", "sgemm_attention_path",
+           "sgemm_attention", "sgemm_attention_path", "sgemm_attention_splitkv", "sgemm_attention_splitkv_describe",
            "sgemm_attention_describe",
            "sgemm_plan_describe", "sgemm_plan_describe2", "sgemm_status_string", "sgemm_last_error")
 
@@ -143,6 +143,11 @@ def load(path: str = LIB_PATH):
     lib.sgemm_attention.argtypes = _ATTN_ARGS + [_vp]
     lib.sgemm_attention_path.restype = _int
     lib.sgemm_attention_path.argtypes = _ATTN_ARGS + [_int, _vp]
+    lib.sgemm_attention_splitkv.restype = _int
+    lib.sgemm_attention_splitkv.argtypes = _ATTN_ARGS + [_vp, _i64, _vp]
+    lib.sgemm_attention_splitkv_describe.restype = _int
+    lib.sgemm_attention_splitkv_describe.argtypes = _ATTN_ARGS + [_i64, _int, ctypes.POINTER(_i64),
+                                                                  ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
     lib.sgemm_attention_describe.restype = _int
     lib.sgemm_attention_describe.argtypes = _ATTN_ARGS + [_int, ctypes.POINTER(PlanInfo)]
     lib.sgemm_sqnorms.restype = _int
@@ -350,6 +355,38 @@ def sgemm_attention_path(nb_outer, nb_inner, tq, tk, d, alpha, causal,
                       sQ_col, K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer, sV_inner, sV_row,
                       sV_col, O, sO_outer, sO_inner, sO_row, sO_col)
     _check(load().sgemm_attention_path(*args, int(path), _stream(stream)))
+
+
+def sgemm_attention_splitkv(nb_outer, nb_inner, tq, tk, d, alpha, causal,
+                            Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+                            K, sK_outer, sK_inner, g, sK_row, sK_col,
+                            V, sV_outer, sV_inner, sV_row, sV_col,
+                            O, sO_outer, sO_inner, sO_row, sO_col,
+                            workspace, workspace_floats, stream=None) -> None:
+    """Fused attention with the keys split across the GPU through `workspace`
+    (decode-shaped calls) through the C ABI."""
+    args = _attn_list(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+                      K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer, sV_inner, sV_row, sV_col,
+                      O, sO_outer, sO_inner, sO_row, sO_col)
+    _check(load().sgemm_attention_splitkv(*args, _ptr(workspace), int(workspace_floats), _stream(stream)))
+
+
+def sgemm_attention_splitkv_describe(nb_outer, nb_inner, tq, tk, d, alpha, causal,
+                                     Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+                                     K, sK_outer, sK_inner, g, sK_row, sK_col,
+                                     V, sV_outer, sV_inner, sV_row, sV_col,
+                                     O, sO_outer, sO_inner, sO_row, sO_col,
+                                     workspace_floats=-1, num_cus=256) -> dict:
+    """The split sgemm_attention_splitkv would make: chunks, chunk_keys and
+    workspace_floats (all 0: not split).  workspace_floats < 0 asks what
+    the planned split needs."""
+    args = _attn_list(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer, sQ_inner, sQ_row, sQ_col,
+                      K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer, sV_inner, sV_row, sV_col,
+                      O, sO_outer, sO_inner, sO_row, sO_col)
+    ch, ck, fl = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(load().sgemm_attention_splitkv_describe(*args, int(workspace_floats), int(num_cus), ctypes.byref(ch),
+                                                   ctypes.byref(ck), ctypes.byref(fl)))
+    return {"chunks": ch.value, "chunk_keys": ck.value, "workspace_floats": fl.value}
 
 
 def sgemm_attention_describe(nb_outer, nb_inner, tq, tk, d, alpha, causal,

@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
 SOURCES = ["plan.cpp", "attention.cpp", "splitk.cpp", "abi.cpp", "kernels.hip", "attn_kernel.hip",
-           "strip_kernel.hip", "splitk_kernel.hip", "scratch.hip"] + [f"mfma_t{t}.hip" for t in range(13)] + \
+           "strip_kernel.hip", "splitk_kernel.hip", "attn_splitkv_kernel.hip", "scratch.hip"] + [f"mfma_t{t}.hip" for t in range(13)] + \
     [f"wave_w{t}.hip" for t in range(8)] + [f"persist_p{t}.hip" for t in range(3)]
 
 

@@ -270,6 +270,67 @@ int sgemm_attention(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, 
                                 SGEMM_PATH_AUTO, stream);
 }
 
+int sgemm_attention_splitkv(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d, float alpha,
+                            int causal, const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row,
+                            int64_t sQ_col, const float *K, int64_t sK_outer, int64_t sK_inner, int64_t g,
+                            int64_t sK_row, int64_t sK_col, const float *V, int64_t sV_outer, int64_t sV_inner,
+                            int64_t sV_row, int64_t sV_col, float *O, int64_t sO_outer, int64_t sO_inner,
+                            int64_t sO_row, int64_t sO_col, float *workspace, int64_t workspace_floats,
+                            void *stream) {
+    const sgemm::AttnCall c = pack_attention(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer, sQ_inner,
+                                             sQ_row, sQ_col, K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer,
+                                             sV_inner, sV_row, sV_col, O, sO_outer, sO_inner, sO_row, sO_col);
+    std::string why;
+    int st = sgemm::validate_attention(c, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    if (workspace_floats < 0) return fail(SGEMM_ERR_INVALID_SIZE, "workspace_floats must be >= 0");
+    if (workspace_floats > 0 && !workspace)
+        return fail(SGEMM_ERR_NULL_POINTER, "workspace is NULL but workspace_floats > 0");
+    if (sgemm::attention_overlaps(c, reinterpret_cast<uintptr_t>(workspace), workspace_floats))
+        return fail(SGEMM_ERR_C_ALIAS, "workspace overlaps Q, K, V or O");
+    int cus = 0;
+    st = current_cus(cus, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    sgemm::SplitKvPlan sp;
+    sgemm::make_splitkv_plan(c, cus, reinterpret_cast<uintptr_t>(workspace), workspace ? workspace_floats : 0, sp);
+    if (sp.chunks > 0) {
+        st = sgemm::launch_splitkv(sp, static_cast<hipStream_t>(stream), why);
+        return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
+    }
+    sgemm::AttnPlan plan;
+    st = plan_attention(c, SGEMM_PATH_AUTO, plan);
+    if (st != SGEMM_OK) return st;
+    st = sgemm::launch_attention(plan, static_cast<hipStream_t>(stream), why);
+    return st == sgemm::kOk ? SGEMM_OK : fail(st, why);
+}
+
+int sgemm_attention_splitkv_describe(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
+                                     float alpha, int causal, const float *Q, int64_t sQ_outer, int64_t sQ_inner,
+                                     int64_t sQ_row, int64_t sQ_col, const float *K, int64_t sK_outer,
+                                     int64_t sK_inner, int64_t g, int64_t sK_row, int64_t sK_col, const float *V,
+                                     int64_t sV_outer, int64_t sV_inner, int64_t sV_row, int64_t sV_col, float *O,
+                                     int64_t sO_outer, int64_t sO_inner, int64_t sO_row, int64_t sO_col,
+                                     int64_t workspace_floats, int num_cus, int64_t *chunks, int64_t *chunk_keys,
+                                     int64_t *floats_used) {
+    if (!chunks || !chunk_keys || !floats_used) return fail(SGEMM_ERR_NULL_POINTER, "an output pointer is NULL");
+    const sgemm::AttnCall c = pack_attention(nb_outer, nb_inner, tq, tk, d, alpha, causal, Q, sQ_outer, sQ_inner,
+                                             sQ_row, sQ_col, K, sK_outer, sK_inner, g, sK_row, sK_col, V, sV_outer,
+                                             sV_inner, sV_row, sV_col, O, sO_outer, sO_inner, sO_row, sO_col);
+    std::string why;
+    int st = sgemm::validate_attention(c, why);
+    if (st != sgemm::kOk) return fail(st, why);
+    if (num_cus <= 0) {
+        st = current_cus(num_cus, why);
+        if (st != sgemm::kOk) return fail(st, why);
+    }
+    sgemm::SplitKvPlan sp;
+    sgemm::make_splitkv_plan(c, num_cus, 0, workspace_floats, sp);
+    *chunks = sp.chunks;
+    *chunk_keys = sp.chunk_keys;
+    *floats_used = sp.workspace_floats;
+    return SGEMM_OK;
+}
+
 int sgemm_attention_describe(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
                              float alpha, int causal, const float *Q, int64_t sQ_outer,
                              int64_t sQ_inner, int64_t sQ_row, int64_t sQ_col, const float *K,

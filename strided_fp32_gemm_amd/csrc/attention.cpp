@@ -126,6 +126,65 @@ bool mfma_serves(const AttnCall &c, std::string &why) {
 
 }  // namespace
 
+bool attention_overlaps(const AttnCall &c, uintptr_t p, int64_t floats) {
+    if (!p || floats <= 0) return false;
+    int64_t last[4];
+    last_offsets(c, last);
+    const uintptr_t ptr[4] = {c.Q, c.K, c.V, c.O};
+    for (int x = 0; x < 4; ++x)
+        if (last[x] >= 0 && ranges_overlap(p, floats - 1, ptr[x], last[x])) return true;
+    return false;
+}
+
+void make_splitkv_plan(const AttnCall &c, int num_cus, uintptr_t workspace, int64_t workspace_floats,
+                       SplitKvPlan &sp) {
+    sp = SplitKvPlan{};
+    std::string ignore;
+    const int64_t g = std::min(c.g, c.nb_inner);
+    if (c.nb_outer == 0 || c.tq == 0 || c.tk == 0 || c.d == 0 || !mfma_serves(c, ignore)) return;
+    if (g * c.tq > kSkvRows) return;
+    // One group's query rows are addressed from one base with 32-bit offsets.
+    const int64_t qlast = last_offset(g, c.sQ[1], c.tq, c.sQ[2], c.d, 1);
+    int64_t qbytes;
+    if (qlast < 0 || !mul64(qlast + 1, 4, qbytes) || qbytes >= kSliceBytes) return;
+    const int64_t n_kv = kv_heads(c);
+    int64_t groups;
+    if (!mul64(c.nb_outer, n_kv, groups) || groups > kInt32Max) return;
+    // About eight wavefronts per CU over all chunks (enough loads in flight
+    // to stream the cache at HBM speed), chunks of a multiple of 32 keys.
+    // SGEMM_ATTN_CHUNKS=<n> fixes the count (tests and sweeps).
+    const int64_t max_chunks = (c.tk + 31) / 32;
+    int64_t chunks = std::max<int64_t>(1, (8 * int64_t(std::max(num_cus, 1)) + groups - 1) / groups);
+    if (const char *f = std::getenv("SGEMM_ATTN_CHUNKS")) chunks = std::max(1, std::atoi(f));
+    chunks = std::min(chunks, max_chunks);
+    if (workspace_floats >= 0) chunks = std::min<int64_t>(chunks, workspace_floats / (groups * kSkvItemFloats));
+    if (chunks < 1) return;
+    const int64_t chunk_keys = ((c.tk + chunks - 1) / chunks + 31) / 32 * 32;
+    chunks = (c.tk + chunk_keys - 1) / chunk_keys;
+    int64_t items, floats;
+    if (!mul64(groups, chunks, items) || !mul64(items, kSkvItemFloats, floats) || items > 4 * kInt32Max) return;
+
+    SplitKvArgs &a = sp.args;
+    a.Q = reinterpret_cast<const float *>(c.Q);
+    a.K = reinterpret_cast<const float *>(c.K);
+    a.V = reinterpret_cast<const float *>(c.V);
+    a.O = reinterpret_cast<float *>(c.O);
+    a.W = reinterpret_cast<float *>(workspace);
+    a.sQ_o = c.sQ[0]; a.sQ_i = c.sQ[1]; a.sQ_r = c.sQ[2];
+    a.sK_o = c.sK[0]; a.sK_i = c.sK[1]; a.sK_r = c.sK[2];
+    a.sV_o = c.sV[0]; a.sV_i = c.sV[1]; a.sV_r = c.sV[2];
+    a.sO_o = c.sO[0]; a.sO_i = c.sO[1]; a.sO_r = c.sO[2];
+    a.nb_inner = int(c.nb_inner); a.n_kv = int(n_kv); a.g = int(g);
+    a.tq = int(c.tq); a.tk = int(c.tk); a.causal = c.causal ? 1 : 0;
+    a.scale_log2 = float(double(c.alpha) * 1.4426950408889634);   // alpha * log2(e)
+    a.chunks = int(chunks);
+    a.chunk_keys = int(chunk_keys);
+    a.items = items;
+    sp.chunks = int(chunks);
+    sp.chunk_keys = int(chunk_keys);
+    sp.workspace_floats = floats;
+}
+
 int make_attention_plan(const AttnCall &c, AttnPath path, AttnPlan &plan, std::string &why) {
     plan = AttnPlan{};
     int64_t rows = c.nb_outer * c.nb_inner * c.tq;

@@ -73,9 +73,50 @@ struct AttnPlan {
     std::string kernel_name;
 };
 
+// Split-KV attention (decode): the g query heads of a KV head and their tq
+// queries (g * tq <= 16) stacked as the 16 rows of one wavefront's tile, the
+// keys cut into chunks, one wavefront per (outer, KV head, chunk) reading
+// its chunk of K and V straight from memory, its partial result (the
+// unnormalised output rows, their reference maxima and weight sums) written
+// to a workspace; then one merge per output row over the chunks in order.
+constexpr int kSkvRows = 16;                          // query rows of a wavefront's tile
+constexpr int kSkvItemFloats = kSkvRows * 64 + 2 * kSkvRows;   // partial: O rows, m, l
+struct SplitKvArgs {
+    const float *Q, *K, *V;
+    float *O;
+    float *W;                        // workspace: item (o, kv, chunk) at W + item * kSkvItemFloats
+    long long sQ_o, sQ_i, sQ_r;      // unit column strides (checked by the planner)
+    long long sK_o, sK_i, sK_r;
+    long long sV_o, sV_i, sV_r;
+    long long sO_o, sO_i, sO_r;
+    int nb_inner, n_kv, g, tq, tk, causal;
+    float scale_log2;                // alpha * log2(e)
+    int chunks, chunk_keys;
+    long long items;                 // nb_outer * n_kv * chunks
+};
+struct SplitKvPlan {
+    int chunks = 0;                  // 0: not split (the call is sgemm_attention)
+    int chunk_keys = 0;
+    int64_t workspace_floats = 0;
+    SplitKvArgs args{};
+};
+
 // Returns kOk or a status (kErrSize, kErrStride, kErrNull, kErrAlias,
 // kErrUnsupported) with `why` filled; touches no device.
 int validate_attention(const AttnCall &c, std::string &why);
+
+// Plans the split-KV form of a validated call for a workspace of at most
+// `workspace_floats` floats (< 0: no cap) at `workspace` (0 for a size
+// query): chunks = 0 when it does not apply (head dimension other than 64,
+// non-unit column strides, unaligned rows, g * tq > 16) or no chunk fits.
+void make_splitkv_plan(const AttnCall &c, int num_cus, uintptr_t workspace, int64_t workspace_floats,
+                       SplitKvPlan &sp);
+
+// True if the `floats` floats at p meet any element range of Q, K, V or O.
+bool attention_overlaps(const AttnCall &c, uintptr_t p, int64_t floats);
+
+// Enqueues the chunk launch and the merge; kErrHip on a rejected launch.
+int launch_splitkv(const SplitKvPlan &sp, hipStream_t stream, std::string &why);
 
 // Chooses the kernel.  `path` Auto picks the matrix-core kernel when it
 // serves the call; forcing Mfma on a call it cannot serve is kErrUnsupported.

@@ -1,0 +1,267 @@
+// attn_splitkv_kernel.hip -- split-KV attention for decode (few queries).
+//
+// With one or a few query rows per head, the fused kernel's workgroup of 128
+// query rows has one busy wavefront and streams the whole KV cache at one
+// wavefront's pace.  Here the g query heads that share a KV head, times their
+// tq queries, are the rows of one 16-row tile (rvllm post, "Matmuls go to
+// cuBLAS": grouped query heads stacked as rows of one product), so K and V
+// are read once per group; and the keys are cut into chunks, one wavefront
+// per (outer, KV head, chunk), so the whole chip streams the cache.
+//
+// attn_splitkv_d64: per chunk, the online softmax of the fused kernel (the
+// same score layout, S^T = K Q^T on v_mfma_f32_16x16x4_f32 with Q scaled by
+// alpha*log2(e) and the products started from minus the reference maximum,
+// the reference moved only past a slack of 2^8) over 32-key blocks whose K
+// and V fragments come straight from global memory (no other wavefront
+// shares them); it writes the chunk's unnormalised output rows, reference
+// maxima and weight sums.
+// attn_splitkv_merge: per output row, M = max m_c and
+// O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c (softmax over the union
+// of the chunks' keys), formed over four runs of consecutive chunks and then
+// over the runs, each in order.  Fixed orders throughout: reproducible bits.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "attention.hpp"
+#include "buffer.hpp"
+
+namespace sgemm {
+
+namespace {
+
+constexpr int kBlock = 32;             // keys per block (two 16-key MFMA blocks)
+constexpr float kSlackSkv = 8.0f;      // log2 of the largest weight before the reference moves
+
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine the four lanes l%16 + 16*h (h = 0..3) with `op` (xor shuffles over
+// the lane bits 4 and 5; every lane of the four ends with the same bits:
+// (l0 op l1) op (l2 op l3) in both orders the shuffles pair them).
+template <typename Op>
+__device__ __forceinline__ float across_quads(float v, Op op) {
+    v = op(v, __shfl_xor(v, 16));
+    return op(v, __shfl_xor(v, 32));
+}
+
+__global__ __launch_bounds__(256) void attn_splitkv_d64(SplitKvArgs p) {
+    const int lane = threadIdx.x & 63, lq = lane & 15, lh = lane >> 4;
+    const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= p.items) return;   // uniform across the wavefront; no barrier in this kernel
+    const int c = int(item % p.chunks);
+    const long long okv = item / p.chunks;
+    const int kv = int(okv % p.n_kv);
+    const long long o = okv / p.n_kv;
+
+    // Row lq of the tile: query head kv*g + qi, query t (rows past gq*tq idle).
+    const int gq = min(p.g, p.nb_inner - kv * p.g);
+    const bool rok = lq < gq * p.tq;
+    const int qi = rok ? lq / p.tq : 0, t = rok ? lq - qi * p.tq : 0;
+    const int shift = p.tk - p.tq;                  // causal: query t sees keys j <= t + shift
+    const int k0 = c * p.chunk_keys, k1 = min(p.tk, k0 + p.chunk_keys);
+    // Last key of the chunk any row sees, and the keys every row sees.
+    const int wave_last = p.causal ? min(k1 - 1, p.tq - 1 + shift) : k1 - 1;
+    const int all_see = p.causal ? min(k1, shift + 1) : k1;
+    int lim = k1 - 1;                               // last key this lane's query sees
+    if (p.causal) lim = min(lim, t + shift);
+    const int nblocks = wave_last >= k0 ? (wave_last - k0) / kBlock + 1 : 0;
+
+    const __amdgpu_buffer_rsrc_t rQ =
+        make_rsrc(p.Q + o * p.sQ_o + (long long)kv * p.g * p.sQ_i);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.K + o * p.sK_o + (long long)kv * p.sK_i + (long long)k0 * p.sK_r);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.V + o * p.sV_o + (long long)kv * p.sV_i + (long long)k0 * p.sV_r);
+    const unsigned sKr = unsigned(p.sK_r), sVr = unsigned(p.sV_r);
+    const float c2 = p.scale_log2;
+
+    f32x4 qf[4];   // dims 16*lh + 4*j .. +3 of this lane's query, scaled
+    const unsigned qrow = unsigned(qi) * unsigned(p.sQ_i) + unsigned(t) * unsigned(p.sQ_r);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        qf[j] = c2 * load4(rQ, rok ? (qrow + unsigned(16 * lh + 4 * j)) * 4u : kOutOfRange);
+
+    float m = 0.0f, l = 0.0f;
+    f32x4 negm = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 oacc[4];   // oacc[nb][e]: output dim 16*lh + 4*e + nb, unnormalised
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) oacc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int b = 0; b < nblocks; ++b) {
+        const int kb0 = k0 + b * kBlock;   // first key of the block
+        // K fragments: key kb0 + 16*kb + lq, dims 16*lh + 4*j; V fragments:
+        // key kb0 + 16*kb + 4*lh + r, dims 4*lq .. +3.  Keys past tk are
+        // never read (out-of-range offset: zeros); keys past the chunk are
+        // read but masked.
+        f32x4 kf[4][2], vf[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = kb0 + 16 * kb + lq;
+            const unsigned rowo = unsigned(key - k0) * sKr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                kf[j][kb] = load4(rK, key < p.tk ? (rowo + unsigned(16 * lh + 4 * j)) * 4u : kOutOfRange);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kb0 + 16 * kb + 4 * lh + r;
+                vf[kb][r] = load4(rV, key < p.tk ? (unsigned(key - k0) * sVr + unsigned(4 * lq)) * 4u : kOutOfRange);
+            }
+        // sacc[kb][r]: alpha*log2(e)*score - m for key kb0 + 16*kb + 4*lh + r.
+        f32x4 sacc[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    sacc[kb] = mfma16(kf[j][kb][e], qf[j][e], j == 0 && e == 0 ? negm : sacc[kb]);
+        if (kb0 + kBlock > all_see) {
+            const int rel = lim - (kb0 + 4 * lh);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (16 * kb + r > rel) sacc[kb][r] = -INFINITY;
+        }
+        float lm = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (kb + r > 0) lm = fmaxf(lm, sacc[kb][r]);
+        if (b == 0 || __builtin_amdgcn_ballot_w64(lm > kSlackSkv)) {
+            // First block: the reference goes to the row maxima (a row that
+            // sees none of the chunk's keys keeps 0; its weights are all 0).
+            float dm = across_quads(lm, [](float x, float y) { return fmaxf(x, y); });
+            if (b == 0) {
+                if (dm == -INFINITY) dm = 0.0f;
+            } else {
+                dm = fmaxf(dm, 0.0f);
+                const float corr = exp2_fast(-dm);
+                l *= corr;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) oacc[nb] *= corr;
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sacc[kb] -= dm;
+            m += dm;
+            negm = f32x4{-m, -m, -m, -m};
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sacc[kb][r] = exp2_fast(sacc[kb][r]);
+                l += sacc[kb][r];
+            }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) oacc[nb] = mfma16(vf[kb][r][nb], sacc[kb][r], oacc[nb]);
+    }
+
+    // Partial of this chunk: rows lq < gq*tq only.
+    l = across_quads(l, [](float x, float y) { return x + y; });
+    float *w = p.W + item * kSkvItemFloats;
+    if (rok) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<f32x4 *>(w + lq * 64 + 16 * lh + 4 * e) =
+                f32x4{oacc[0][e], oacc[1][e], oacc[2][e], oacc[3][e]};
+        if (lh == 0) {
+            w[kSkvRows * 64 + lq] = l > 0.0f ? m : -INFINITY;   // an empty chunk weighs nothing
+            w[kSkvRows * 64 + kSkvRows + lq] = l;
+        }
+    }
+}
+
+// One workgroup per output row (outer, KV head, tile row), lane = head
+// dimension.  Its four wavefronts take consecutive runs of the chunks (each
+// with four chunks' loads in flight), each forming its run's maximum M_w,
+// weighted output sum and weight sum in chunk order; the first wavefront
+// then combines the four runs in run order through LDS.
+__global__ __launch_bounds__(256) void attn_splitkv_merge(SplitKvArgs p) {
+    __shared__ float run_m[4], run_den[4], run_num[4][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const long long rowi = blockIdx.x;
+    const int r = int(rowi % kSkvRows);
+    const long long okv = rowi / kSkvRows;
+    const int kv = int(okv % p.n_kv);
+    const long long o = okv / p.n_kv;
+    const int gq = min(p.g, p.nb_inner - kv * p.g);
+    if (r >= gq * p.tq) return;   // uniform across the workgroup
+    const int per = (p.chunks + 3) / 4;
+    const int c0 = min(wv * per, p.chunks), c1 = min(c0 + per, p.chunks);
+    const float *w = p.W + okv * p.chunks * kSkvItemFloats;
+    const float *wm = w + kSkvRows * 64 + r;        // m of chunk c at wm[c * kSkvItemFloats]
+    float M = -INFINITY;
+    int c = c0;
+    for (; c + 4 <= c1; c += 4) {
+        const float a0 = wm[c * kSkvItemFloats], a1 = wm[(c + 1) * kSkvItemFloats];
+        const float a2 = wm[(c + 2) * kSkvItemFloats], a3 = wm[(c + 3) * kSkvItemFloats];
+        M = fmaxf(fmaxf(fmaxf(fmaxf(M, a0), a1), a2), a3);
+    }
+    for (; c < c1; ++c) M = fmaxf(M, wm[c * kSkvItemFloats]);
+    float num = 0.0f, den = 0.0f;
+    auto add = [&](float mc, float oc, float lc) {
+        const float f = mc == -INFINITY ? 0.0f : exp2_fast(mc - M);
+        num += f * oc;
+        den += f * lc;
+    };
+    const float *wo = w + r * 64 + lane, *wl = w + kSkvRows * 64 + kSkvRows + r;
+    c = c0;
+    for (; c + 4 <= c1; c += 4) {
+        float mc[4], oc[4], lc[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            mc[x] = wm[(c + x) * kSkvItemFloats];
+            oc[x] = wo[(c + x) * kSkvItemFloats];
+            lc[x] = wl[(c + x) * kSkvItemFloats];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) add(mc[x], oc[x], lc[x]);
+    }
+    for (; c < c1; ++c) add(wm[c * kSkvItemFloats], wo[c * kSkvItemFloats], wl[c * kSkvItemFloats]);
+    run_num[wv][lane] = num;
+    if (lane == 0) {
+        run_m[wv] = M;
+        run_den[wv] = den;
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    float Mt = run_m[0];
+    for (int x = 1; x < 4; ++x) Mt = fmaxf(Mt, run_m[x]);
+    float tn = 0.0f, td = 0.0f;
+    for (int x = 0; x < 4; ++x) {
+        if (run_m[x] == -INFINITY) continue;   // an empty run (or one whose chunks saw no key)
+        const float f = exp2_fast(run_m[x] - Mt);
+        tn += f * run_num[x][lane];
+        td += f * run_den[x];
+    }
+    const int qi = r / p.tq, t = r - qi * p.tq;
+    p.O[o * p.sO_o + (long long)(kv * p.g + qi) * p.sO_i + (long long)t * p.sO_r + lane] = tn / td;
+}
+
+}  // namespace
+
+int launch_splitkv(const SplitKvPlan &sp, hipStream_t stream, std::string &why) {
+    const SplitKvArgs &a = sp.args;
+    const long long rows = a.items / a.chunks * kSkvRows;
+    hipLaunchKernelGGL(attn_splitkv_d64, dim3(unsigned((a.items + 3) / 4)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_splitkv_merge, dim3(unsigned(rows)), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        why = std::string("split-KV attention launch failed: ") + hipGetErrorString(e);
+        return kErrHip;
+    }
+    return kOk;
+}
+
+}  // namespace sgemm

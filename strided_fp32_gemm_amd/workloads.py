@@ -36,14 +36,15 @@ ROOT_SEED = 2024
 WORKLOADS = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
              "linear_bwd_dx", "linear_bwd_dw", "linear_xT", "linear_bias", "sqdist",
              "attn_qk_gqa", "attn_pv_gqa", "attn_fused", "attn_fused_causal", "skinny_xWt",
-             "linear_dw_deep")
+             "linear_dw_deep", "attn_decode")
 # Entry point each workload goes through: "plain" (sgemm_strided_batched),
 # "ex" (sgemm_strided_batched_ex), "dist" (sgemm_pairwise_sqdist) or
 # "batched2" (sgemm_strided_batched2), "attention" (sgemm_attention) or
-# "splitk" (sgemm_strided_batched_splitk, with the workspace its plan asks for).
+# "splitk" (sgemm_strided_batched_splitk, with the workspace its plan asks for)
+# or "attention_splitkv" (sgemm_attention_splitkv, likewise).
 KINDS = {"linear_bias": "ex", "sqdist": "dist", "attn_qk_gqa": "batched2",
          "attn_pv_gqa": "batched2", "attn_fused": "attention", "attn_fused_causal": "attention",
-         "linear_dw_deep": "splitk"}
+         "linear_dw_deep": "splitk", "attn_decode": "attention_splitkv"}
 
 
 def kind(name: str) -> str:
@@ -54,7 +55,7 @@ def kind(name: str) -> str:
 # layer's backward pass share one draw of dy, W and x).
 SEED_NAMES = ("square64", "linear_xWt", "attn_qk", "attn_pv", "spectrogram", "square4096_acc",
               "linear_bwd", "linear_xT", "linear_bias", "sqdist", "attn_qk_gqa", "attn_pv_gqa",
-              "attn_fused", "skinny_xWt", "linear_dw_deep")
+              "attn_fused", "skinny_xWt", "linear_dw_deep", "attn_decode")
 
 
 @dataclasses.dataclass
@@ -541,6 +542,26 @@ def attn_fused() -> AttnProblem:
     return _attn_fused("attn_fused", False)
 
 
+def attn_decode() -> AttnProblem:
+    """One decode step of the same layer over a 4096-token context: for each
+    of 8 sequences and 15 query heads one new query (the last position,
+    causal) against a KV cache of 4096 positions, 5 KV heads (three query
+    heads each), head_dim 64, token-major Q [8][1][15][64] and K, V
+    [8][4096][5][64] N(0,1), alpha 1/8, O zero-filled; through
+    sgemm_attention_splitkv.  The context length is not one the pages
+    print: the cache is long enough that reading it, 84 MB, sets the time."""
+    gq, gk, gv = _gens("attn_decode", 3)
+    no, h, hk, d, ctx = GQA_SEQS, GQA_Q_HEADS, GQA_KV_HEADS, GQA_HEAD_DIM, 4096
+    nq, sq = layout2(no, h, 1, d, "tokens")
+    nk, sk = layout2(no, hk, ctx, d, "tokens")
+    Q = _f32(gq.normal(0.0, 1.0, nq))
+    K = _f32(gk.normal(0.0, 1.0, nk))
+    V = _f32(gv.normal(0.0, 1.0, nk))
+    O = np.zeros(nq, np.float32)
+    return AttnProblem("attn_decode", no, h, 1, ctx, d, h // hk, 1.0 / math.sqrt(d), True,
+                       Operand2(Q, sq), Operand2(K, sk), Operand2(V, sk), Operand2(O, sq))
+
+
 def attn_fused_causal() -> AttnProblem:
     """attn_fused with the causal mask of a prefill (query q sees keys <= q);
     the same draw of Q, K, V."""
@@ -565,6 +586,7 @@ BUILDERS = {
     "attn_fused_causal": attn_fused_causal,
     "skinny_xWt": skinny_xWt,
     "linear_dw_deep": linear_dw_deep,
+    "attn_decode": attn_decode,
 }
 
 

@@ -283,6 +283,33 @@ def test_extended_entry_points_validate_before_the_device():
 
 
 
+def test_splitkv_attention_validates_and_plans_before_the_device(monkeypatch):
+    """Split-KV attention checks the attention arguments and its workspace
+    (size >= 0, NULL only when empty, no overlap with Q, K, V or O) before
+    any device call, and plans without a device: a decode step (one query,
+    g = 3 query heads per KV head, 4096 keys, 8 x 5 groups) takes 43 chunks of
+    96 keys, 1056 floats of workspace per chunk; a prefill, g * tq above 16,
+    a head dimension other than 64 and a workspace below one chunk per group
+    are not split; SGEMM_ATTN_CHUNKS fixes the count."""
+    def args(no=8, h=15, tq=1, tk=4096, d=64, g=3, V=PB + (1 << 26), O=PC):
+        hk = -(-h // g)
+        sQ, sK = (tq * h * d, d, h * d, 1), (tk * hk * d, d, hk * d, 1)
+        return [no, h, tq, tk, d, 0.125, 1, PA, *sQ, PB, sK[0], sK[1], g, sK[2], sK[3], V, *sK, O, *sQ]
+    d = lambda ws=-1, **kw: sg.sgemm_attention_splitkv_describe(*args(**kw), workspace_floats=ws)
+    assert d() == {"chunks": 43, "chunk_keys": 96, "workspace_floats": 43 * 40 * 1056}
+    assert d(tq=512, tk=512)["chunks"] == 0                                   # prefill
+    assert d(g=5, tq=4)["chunks"] == 0 and d(g=5, tq=3)["chunks"] > 0       # 20 rows, 15 rows
+    assert d(d=32)["chunks"] == 0
+    assert d(ws=40 * 1056 - 1)["chunks"] == 0 and d(ws=3 * 40 * 1056)["chunks"] == 3
+    monkeypatch.setenv("SGEMM_ATTN_CHUNKS", "7")
+    assert d()["chunks"] == 7
+    run = lambda ws, floats: sg.sgemm_attention_splitkv(*args(), ws, floats)
+    assert status_of(lambda: run(None, -1)) == -1
+    assert status_of(lambda: run(None, 10)) == -3
+    assert status_of(lambda: run(PB + 64, 1 << 12)) == -4      # inside K
+    assert status_of(lambda: run(PC - 16, 1 << 12)) == -4      # reaching into O
+
+
 def test_splitk_validates_and_plans_before_the_device(monkeypatch):
     """The split-k entry point checks the product's arguments and its
     workspace (size >= 0, NULL only when empty, no overlap with A, B or C)

@@ -1,7 +1,8 @@
 """The entry points under HIP graph capture: a strided batched product that
 accumulates, a fused causal attention, the allocation-free distance entry
-point and a split-k product (its partial products, a shorter last
-partition and the reduction: three launches through a caller workspace),
+point, a split-k product (its partial products, a shorter last
+partition and the reduction: three launches through a caller workspace) and
+a split-KV decode attention (chunks and merge through a workspace),
 captured together on one stream and replayed several times, with eager work
 (resetting C, a host round trip) between the replays.  Every replay must
 give the eager results bit for bit: the library enqueues only kernels (no
@@ -50,12 +51,18 @@ def test_graph_replays_match_eager_calls():
     dA2, dB2, E0 = dev(deep.A.storage), dev(deep.B.storage), dev(deep.C.storage)
     dE = E0.clone()
     W = torch.empty(plan["workspace_floats"], device="cuda")
+    dec = wl.random_attention(5105, 2, 6, 1, 700, 64, g=3, causal=True, order="tokens")
+    dplan = sg.sgemm_attention_splitkv_describe(*dec.call_args(1 << 40, 1 << 41, 1 << 42, 1 << 43))
+    assert dplan["chunks"] > 1, dplan
+    eq, ek, ev, eo = dev(dec.Q.storage), dev(dec.K.storage), dev(dec.V.storage), dev(dec.O.storage)
+    W2 = torch.empty(dplan["workspace_floats"], device="cuda")
 
     def enqueue(stream):
         sg.sgemm_strided_batched(*gemm.call_args(dA, dB, dC), stream=stream)
         sg.sgemm_attention(*attn.call_args(dq, dk, dv, do), stream=stream)
         sg.sgemm_pairwise_sqdist_noalloc(batch, m, n, k, dX, *sX, dY, *sY, dD, *sD, stream=stream)
         sg.sgemm_strided_batched_splitk(*deep.call_args(dA2, dB2, dE), W, W.numel(), stream=stream)
+        sg.sgemm_attention_splitkv(*dec.call_args(eq, ek, ev, eo), W2, W2.numel(), stream=stream)
 
     # Eager results (this also does any one-time set-up outside the capture).
     side = torch.cuda.Stream()
@@ -64,7 +71,7 @@ def test_graph_replays_match_eager_calls():
         enqueue(side)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    want = [dC.cpu().numpy(), do.cpu().numpy(), dD.cpu().numpy(), dE.cpu().numpy()]
+    want = [dC.cpu().numpy(), do.cpu().numpy(), dD.cpu().numpy(), dE.cpu().numpy(), eo.cpu().numpy()]
 
     graph = torch.cuda.CUDAGraph()
     dC.copy_(C0)
@@ -80,9 +87,12 @@ def test_graph_replays_match_eager_calls():
         do.fill_(float("nan"))
         dD.fill_(float("nan"))
         W.fill_(float("nan"))
+        W2.fill_(float("nan"))
+        eo.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = [dC.cpu().numpy(), do.cpu().numpy(), dD.cpu().numpy(), dE.cpu().numpy()]
-        for name, g_, w_ in zip(("product", "attention", "distances", "split-k product"), got, want):
+        got = [dC.cpu().numpy(), do.cpu().numpy(), dD.cpu().numpy(), dE.cpu().numpy(), eo.cpu().numpy()]
+        for name, g_, w_ in zip(("product", "attention", "distances", "split-k product", "split-KV decode"),
+                                got, want):
             assert np.array_equal(g_, w_), (replay, name)
