@@ -150,15 +150,46 @@ void make_splitkv_plan(const AttnCall &c, int num_cus, uintptr_t workspace, int6
     const int64_t n_kv = kv_heads(c);
     int64_t groups;
     if (!mul64(c.nb_outer, n_kv, groups) || groups > kInt32Max) return;
-    // About eight wavefronts per CU over all chunks (enough loads in flight
-    // to stream the cache at HBM speed), chunks of a multiple of 32 keys.
-    // SGEMM_ATTN_CHUNKS=<n> fixes the count (tests and sweeps).
-    const int64_t max_chunks = (c.tk + 31) / 32;
-    int64_t chunks = std::max<int64_t>(1, (8 * int64_t(std::max(num_cus, 1)) + groups - 1) / groups);
-    if (const char *f = std::getenv("SGEMM_ATTN_CHUNKS")) chunks = std::max(1, std::atoi(f));
-    chunks = std::min(chunks, max_chunks);
-    if (workspace_floats >= 0) chunks = std::min<int64_t>(chunks, workspace_floats / (groups * kSkvItemFloats));
-    if (chunks < 1) return;
+    // Chunks of a whole number of 32-key blocks.  The kernel's time is taken
+    // as that of the busiest CU, ceil(workgroups / CUs) workgroups of four
+    // wavefronts each streaming one chunk (the dispatcher spreads them
+    // evenly), plus a little merge work per chunk.  The cheapest count that
+    // gives every CU a workgroup is taken; where the keys allow none, the
+    // cheapest count overall.  SGEMM_ATTN_CHUNKS=<n> fixes the count (tests
+    // and sweeps).
+    const int64_t blocks = (c.tk + 31) / 32;
+    int64_t cap = blocks;
+    if (workspace_floats >= 0) cap = std::min<int64_t>(cap, workspace_floats / (groups * kSkvItemFloats));
+    if (cap < 1) return;
+    int64_t chunks = 0;
+    if (const char *f = std::getenv("SGEMM_ATTN_CHUNKS")) {
+        chunks = std::min<int64_t>(std::max(1, std::atoi(f)), cap);
+    } else {
+        const int64_t cus = std::max(num_cus, 1);
+        int64_t fill = 0, any = 0;   // best count filling every CU, best count overall
+        double fill_cost = 0.0, any_cost = 0.0;
+        // b = blocks per chunk, visiting each distinct chunk count once.
+        for (int64_t b = 1; b <= blocks;) {
+            const int64_t n = (blocks + b - 1) / b;
+            if (n <= cap) {
+                const int64_t per = (blocks + n - 1) / n;   // blocks of the longest chunk
+                const int64_t wgs = (groups * n + 3) / 4;
+                const double cost =
+                    double((wgs + cus - 1) / cus) * 4.0 * double(per) + kSkvMergePerChunk * double(n);
+                if (wgs >= cus && (fill == 0 || cost < fill_cost)) {
+                    fill = n;
+                    fill_cost = cost;
+                }
+                if (any == 0 || cost < any_cost) {
+                    any = n;
+                    any_cost = cost;
+                }
+            }
+            if (n == 1) break;
+            b = (blocks + n - 2) / (n - 1);   // the smallest b that gives fewer chunks
+        }
+        chunks = fill ? fill : any;
+    }
     const int64_t chunk_keys = ((c.tk + chunks - 1) / chunks + 31) / 32 * 32;
     chunks = (c.tk + chunk_keys - 1) / chunk_keys;
     int64_t items, floats;

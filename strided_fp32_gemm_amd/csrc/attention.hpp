@@ -81,6 +81,9 @@ struct AttnPlan {
 // to a workspace; then one merge per output row over the chunks in order.
 constexpr int kSkvRows = 16;                          // query rows of a wavefront's tile
 constexpr int kSkvItemFloats = kSkvRows * 64 + 2 * kSkvRows;   // partial: O rows, m, l
+// Merge cost of one more chunk, in units of one wavefront streaming one
+// 32-key block on the busiest CU (fitted: about 0.06 us against 0.7 us).
+constexpr double kSkvMergePerChunk = 0.1;
 struct SplitKvArgs {
     const float *Q, *K, *V;
     float *O;

@@ -6,7 +6,10 @@
 // tq queries, are the rows of one 16-row tile (rvllm post, "Matmuls go to
 // cuBLAS": grouped query heads stacked as rows of one product), so K and V
 // are read once per group; and the keys are cut into chunks, one wavefront
-// per (outer, KV head, chunk), so the whole chip streams the cache.
+// per (outer, KV head, chunk), so the whole chip streams the cache.  The KV
+// head varies fastest across wavefronts: the four wavefronts of a workgroup
+// read the same key positions of neighbouring heads, which sit side by side
+// in a token-major cache.
 //
 // attn_splitkv_d64: per chunk, the online softmax of the fused kernel (the
 // same score layout, S^T = K Q^T on v_mfma_f32_16x16x4_f32 with Q scaled by
@@ -17,7 +20,8 @@
 // maxima and weight sums.
 // attn_splitkv_merge: per output row, M = max m_c and
 // O = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c (softmax over the union
-// of the chunks' keys), formed over four runs of consecutive chunks and then
+// of the chunks' keys), formed over four runs of consecutive chunks (one
+// pass per run, its reference moving up to each new chunk maximum) and then
 // over the runs, each in order.  Fixed orders throughout: reproducible bits.
 #include <hip/hip_runtime.h>
 
@@ -48,14 +52,17 @@ __device__ __forceinline__ float across_quads(float v, Op op) {
     return op(v, __shfl_xor(v, 32));
 }
 
-__global__ __launch_bounds__(256) void attn_splitkv_d64(SplitKvArgs p) {
+// Three wavefronts per SIMD fit without spills (the compiler would otherwise
+// take a few registers more and drop to two).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_splitkv_d64(SplitKvArgs p) {
     const int lane = threadIdx.x & 63, lq = lane & 15, lh = lane >> 4;
     const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= p.items) return;   // uniform across the wavefront; no barrier in this kernel
-    const int c = int(item % p.chunks);
-    const long long okv = item / p.chunks;
-    const int kv = int(okv % p.n_kv);
-    const long long o = okv / p.n_kv;
+    const int kv = int(item % p.n_kv);
+    const long long oc = item / p.n_kv;
+    const int c = int(oc % p.chunks);
+    const long long o = oc / p.chunks;
+    const long long slot = (o * p.n_kv + kv) * p.chunks + c;   // partials of a group are consecutive
 
     // Row lq of the tile: query head kv*g + qi, query t (rows past gq*tq idle).
     const int gq = min(p.g, p.nb_inner - kv * p.g);
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(256) void attn_splitkv_d64(SplitKvArgs p) {
 
     // Partial of this chunk: rows lq < gq*tq only.
     l = across_quads(l, [](float x, float y) { return x + y; });
-    float *w = p.W + item * kSkvItemFloats;
+    float *w = p.W + slot * kSkvItemFloats;
     if (rok) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -183,10 +190,11 @@ __global__ __launch_bounds__(256) void attn_splitkv_d64(SplitKvArgs p) {
 }
 
 // One workgroup per output row (outer, KV head, tile row), lane = head
-// dimension.  Its four wavefronts take consecutive runs of the chunks (each
-// with four chunks' loads in flight), each forming its run's maximum M_w,
-// weighted output sum and weight sum in chunk order; the first wavefront
-// then combines the four runs in run order through LDS.
+// dimension.  Its four wavefronts take consecutive runs of the chunks; each
+// issues the loads of up to sixteen chunks at once and folds them in chunk
+// order into its run's maximum M_w, weighted output sum and weight sum
+// (rescaling both sums when a chunk raises M_w); the first wavefront then
+// combines the four runs in run order through LDS.
 __global__ __launch_bounds__(256) void attn_splitkv_merge(SplitKvArgs p) {
     __shared__ float run_m[4], run_den[4], run_num[4][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -200,35 +208,36 @@ __global__ __launch_bounds__(256) void attn_splitkv_merge(SplitKvArgs p) {
     const int per = (p.chunks + 3) / 4;
     const int c0 = min(wv * per, p.chunks), c1 = min(c0 + per, p.chunks);
     const float *w = p.W + okv * p.chunks * kSkvItemFloats;
-    const float *wm = w + kSkvRows * 64 + r;        // m of chunk c at wm[c * kSkvItemFloats]
-    float M = -INFINITY;
-    int c = c0;
-    for (; c + 4 <= c1; c += 4) {
-        const float a0 = wm[c * kSkvItemFloats], a1 = wm[(c + 1) * kSkvItemFloats];
-        const float a2 = wm[(c + 2) * kSkvItemFloats], a3 = wm[(c + 3) * kSkvItemFloats];
-        M = fmaxf(fmaxf(fmaxf(fmaxf(M, a0), a1), a2), a3);
-    }
-    for (; c < c1; ++c) M = fmaxf(M, wm[c * kSkvItemFloats]);
-    float num = 0.0f, den = 0.0f;
-    auto add = [&](float mc, float oc, float lc) {
-        const float f = mc == -INFINITY ? 0.0f : exp2_fast(mc - M);
-        num += f * oc;
-        den += f * lc;
-    };
-    const float *wo = w + r * 64 + lane, *wl = w + kSkvRows * 64 + kSkvRows + r;
-    c = c0;
-    for (; c + 4 <= c1; c += 4) {
-        float mc[4], oc[4], lc[4];
+    // Chunk c's m, l and output element sit at these plus c * kSkvItemFloats.
+    const float *wm = w + kSkvRows * 64 + r, *wl = w + kSkvRows * 64 + kSkvRows + r, *wo = w + r * 64 + lane;
+    float M = -INFINITY, num = 0.0f, den = 0.0f;
+    for (int c = c0; c < c1; c += 16) {
+        float mc[16], oc[16], lc[16];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            mc[x] = wm[(c + x) * kSkvItemFloats];
-            oc[x] = wo[(c + x) * kSkvItemFloats];
-            lc[x] = wl[(c + x) * kSkvItemFloats];
+        for (int x = 0; x < 16; ++x) {
+            mc[x] = -INFINITY;
+            oc[x] = lc[x] = 0.0f;
+            if (c + x < c1) {   // uniform: nothing past the run is read
+                const long long off = (long long)(c + x) * kSkvItemFloats;
+                mc[x] = wm[off];
+                oc[x] = wo[off];
+                lc[x] = wl[off];
+            }
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x) add(mc[x], oc[x], lc[x]);
+        for (int x = 0; x < 16; ++x) {
+            if (mc[x] == -INFINITY) continue;   // past the run, or a chunk that saw no key
+            if (mc[x] > M) {
+                const float f = exp2_fast(M - mc[x]);   // 0 while M is still -inf
+                num *= f;
+                den *= f;
+                M = mc[x];
+            }
+            const float f = exp2_fast(mc[x] - M);
+            num += f * oc[x];
+            den += f * lc[x];
+        }
     }
-    for (; c < c1; ++c) add(wm[c * kSkvItemFloats], wo[c * kSkvItemFloats], wl[c * kSkvItemFloats]);
     run_num[wv][lane] = num;
     if (lane == 0) {
         run_m[wv] = M;

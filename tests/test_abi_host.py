@@ -290,7 +290,14 @@ def test_splitkv_attention_validates_and_plans_before_the_device(monkeypatch):
     g = 3 query heads per KV head, 4096 keys, 8 x 5 groups) takes 43 chunks of
     96 keys, 1056 floats of workspace per chunk; a prefill, g * tq above 16,
     a head dimension other than 64 and a workspace below one chunk per group
-    are not split; SGEMM_ATTN_CHUNKS fixes the count."""
+    are not split; SGEMM_ATTN_CHUNKS fixes the count.  Other chunk counts
+    worked by hand from the planner's rule (the busiest CU's workgroups times
+    their blocks, plus 0.1 per chunk, over the counts that give each of the
+    256 CUs a workgroup): 16384 keys over 40 groups take 74 chunks of 224
+    keys (740 workgroups, 3 on the busiest CU: 84 + 7.4, where 128 chunks
+    cost 80 + 12.8); 32 x 4 groups over 4096 keys take 8 of 512 (64 + 0.8);
+    2 groups over 8192 keys fill no CU count and take the cheapest overall,
+    86 chunks of 96 keys (12 + 8.6, against 8 + 12.8 for 128 chunks)."""
     def args(no=8, h=15, tq=1, tk=4096, d=64, g=3, V=PB + (1 << 26), O=PC):
         hk = -(-h // g)
         sQ, sK = (tq * h * d, d, h * d, 1), (tk * hk * d, d, hk * d, 1)
@@ -301,6 +308,9 @@ def test_splitkv_attention_validates_and_plans_before_the_device(monkeypatch):
     assert d(g=5, tq=4)["chunks"] == 0 and d(g=5, tq=3)["chunks"] > 0       # 20 rows, 15 rows
     assert d(d=32)["chunks"] == 0
     assert d(ws=40 * 1056 - 1)["chunks"] == 0 and d(ws=3 * 40 * 1056)["chunks"] == 3
+    assert (d(tk=16384)["chunks"], d(tk=16384)["chunk_keys"]) == (74, 224)
+    assert (d(no=32, h=32, g=8)["chunks"], d(no=32, h=32, g=8)["chunk_keys"]) == (8, 512)
+    assert (d(no=1, h=8, g=4, tk=8192)["chunks"], d(no=1, h=8, g=4, tk=8192)["chunk_keys"]) == (86, 96)
     monkeypatch.setenv("SGEMM_ATTN_CHUNKS", "7")
     assert d()["chunks"] == 7
     run = lambda ws, floats: sg.sgemm_attention_splitkv(*args(), ws, floats)
