@@ -283,6 +283,47 @@ def test_extended_entry_points_validate_before_the_device():
 
 
 
+def test_splitkv_chunk_count_is_the_cheapest_by_exhaustive_search(monkeypatch):
+    """The planner visits only the distinct chunk counts (jumping over block
+    counts that give the same number of chunks); an exhaustive search over
+    every count 1..blocks with the same rule (the busiest CU's workgroups
+    times the blocks of the longest chunk, plus 0.1 per chunk; the cheapest
+    count giving each of the 256 CUs a workgroup, else the cheapest overall;
+    ties to the most chunks, as the planner meets them first) must agree on
+    random decode shapes, with and without a workspace cap."""
+    monkeypatch.delenv("SGEMM_ATTN_CHUNKS", raising=False)
+    rng = np.random.default_rng(404)
+    cus, item = 256, 16 * 64 + 32
+    for _ in range(60):
+        no, hk, g = int(rng.integers(1, 65)), int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        tk = int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(600, 70000))]))
+        h = hk * g
+        groups, blocks = no * hk, -(-tk // 32)
+        cap = blocks
+        ws = -1
+        if rng.random() < 0.3:
+            ws = int(rng.integers(groups * item, groups * item * (blocks + 1)))
+            cap = min(cap, ws // (groups * item))
+        best = {}
+        for n in sorted({-(-blocks // b) for b in range(1, blocks + 1)}, reverse=True):
+            if n > cap:
+                continue
+            per = -(-blocks // n)
+            wgs = -(-(groups * n) // 4)
+            cost = -(-wgs // cus) * 4.0 * per + 0.1 * n
+            for key, ok in (("fill", wgs >= cus), ("any", True)):
+                if ok and (key not in best or cost < best[key][0]):
+                    best[key] = (cost, n)
+        want = (best.get("fill") or best["any"])[1]
+        keys = -(-(-(-tk // want)) // 32) * 32
+        want = -(-tk // keys)
+        sQ, sK = (h * 64, 64, h * 64, 1), (tk * hk * 64, 64, hk * 64, 1)
+        got = sg.sgemm_attention_splitkv_describe(no, h, 1, tk, 64, 0.125, 1, PA, *sQ, PB, sK[0], sK[1], g, sK[2],
+                                                  sK[3], PB + (1 << 35), *sK, PC, *sQ, workspace_floats=ws)
+        assert (got["chunks"], got["chunk_keys"]) == (want, keys), (no, hk, g, tk, ws, got, want, keys)
+        assert got["workspace_floats"] == groups * want * item and (want - 1) * keys < tk <= want * keys
+
+
 def test_splitkv_attention_validates_and_plans_before_the_device(monkeypatch):
     """Split-KV attention checks the attention arguments and its workspace
     (size >= 0, NULL only when empty, no overlap with Q, K, V or O) before
