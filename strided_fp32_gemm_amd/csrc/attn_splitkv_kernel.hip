@@ -84,11 +84,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const unsigned sKr = unsigned(p.sK_r), sVr = unsigned(p.sV_r);
     const float c2 = p.scale_log2;
 
-    f32x4 qf[4];   // dims 16*lh + 4*j .. +3 of this lane's query, scaled
+    f32x4 qf[4];   // dims 16*j + 4*lh .. +3 of this lane's query, scaled
     const unsigned qrow = unsigned(qi) * unsigned(p.sQ_i) + unsigned(t) * unsigned(p.sQ_r);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        qf[j] = c2 * load4(rQ, rok ? (qrow + unsigned(16 * lh + 4 * j)) * 4u : kOutOfRange);
+        qf[j] = c2 * load4(rQ, rok ? (qrow + unsigned(16 * j + 4 * lh)) * 4u : kOutOfRange);
 
     float m = 0.0f, l = 0.0f;
     f32x4 negm = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
     for (int b = 0; b < nblocks; ++b) {
         const int kb0 = k0 + b * kBlock;   // first key of the block
-        // K fragments: key kb0 + 16*kb + lq, dims 16*lh + 4*j; V fragments:
+        // K fragments: key kb0 + 16*kb + lq, dims 16*j + 4*lh (one load reads
+        // 64 contiguous bytes of each of 16 key rows); V fragments:
         // key kb0 + 16*kb + 4*lh + r, dims 4*lq .. +3.  Keys past tk are
         // never read (out-of-range offset: zeros); keys past the chunk are
         // read but masked.
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
             const unsigned rowo = unsigned(key - k0) * sKr;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                kf[j][kb] = load4(rK, key < p.tk ? (rowo + unsigned(16 * lh + 4 * j)) * 4u : kOutOfRange);
+                kf[j][kb] = load4(rK, key < p.tk ? (rowo + unsigned(16 * j + 4 * lh)) * 4u : kOutOfRange);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
