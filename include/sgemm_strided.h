@@ -436,9 +436,6 @@ int sgemm_attention_path(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t
                          float *O, int64_t sO_outer, int64_t sO_inner, int64_t sO_row, int64_t sO_col,
                          int path, void *stream);
 
-/* The plan of a sgemm_attention_path call (validated the same way, no
- * device access): tile_m = query rows per workgroup.  Returns an
- * sgemm_status. */
 /*
  * sgemm_attention for decode-shaped calls (few queries per head, a long KV
  * cache), with the keys split across the GPU through a caller workspace.
@@ -455,6 +452,10 @@ int sgemm_attention_path(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t
  * M = max_c m_c.  Results are reproducible bit for bit; they differ from
  * sgemm_attention's (the keys' sum is grouped by chunk) within the same
  * bound.
+ * Chunks are whole 32-key blocks; their count is the one that keeps the
+ * busiest CU's work least (its workgroups times their blocks, plus a small
+ * merge cost per chunk) among the counts giving every CU a workgroup, capped
+ * by the workspace.
  * Serves head dimension 64, unit column strides and 16-byte aligned rows
  * with g * tq <= 16 (g capped at nb_inner); any other call, or a workspace
  * too small for one chunk per (outer, KV head), runs as sgemm_attention.
@@ -492,6 +493,9 @@ int sgemm_attention_splitkv_describe(int64_t nb_outer, int64_t nb_inner, int64_t
                                      int64_t workspace_floats, int num_cus,
                                      int64_t *chunks, int64_t *chunk_keys, int64_t *floats_used);
 
+/* The plan of a sgemm_attention_path call (validated the same way, no
+ * device access): tile_m = query rows per workgroup.  Returns an
+ * sgemm_status. */
 int sgemm_attention_describe(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t tk, int64_t d,
                              float alpha, int causal,
                              const float *Q, int64_t sQ_outer, int64_t sQ_inner, int64_t sQ_row,
