@@ -441,10 +441,11 @@ int sgemm_attention_path(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t
  * cache), with the keys split across the GPU through a caller workspace.
  * Same arguments, operation and status codes as sgemm_attention, plus the
  * workspace.  The g query heads of a KV head and their tq queries are
- * stacked as the rows of one 16-row matrix-core tile (g * tq <= 16; the rvllm
- * post, "Matmuls go to cuBLAS", stacks a group's query heads as rows of one
- * product), so K and V are read once per group; the keys are cut into
- * chunks, one wavefront per (outer, KV head, chunk) forms that chunk's
+ * stacked as the rows of 16-row matrix-core tiles (g * tq <= 64, up to four
+ * tiles; the rvllm post, "Matmuls go to cuBLAS", stacks a group's query
+ * heads as rows of one product), so K and V are read once per tile rather
+ * than once per query head; the keys are cut into chunks, one wavefront per
+ * (outer, KV head, row tile, chunk) forms that chunk's
  * online softmax (unnormalised output rows, reference maxima, weight sums:
  * kael book ch. 09 and the rvllm post's softmax in three steps, done in one
  * pass) into `workspace`, and a second launch merges each output row's
@@ -457,8 +458,9 @@ int sgemm_attention_path(int64_t nb_outer, int64_t nb_inner, int64_t tq, int64_t
  * merge cost per chunk) among the counts giving every CU a workgroup, capped
  * by the workspace.
  * Serves head dimension 64, unit column strides and 16-byte aligned rows
- * with g * tq <= 16 (g capped at nb_inner); any other call, or a workspace
- * too small for one chunk per (outer, KV head), runs as sgemm_attention.
+ * with g * tq <= 64 (g capped at nb_inner); any other call, or a workspace
+ * too small for one chunk per (outer, KV head, row tile), runs as
+ * sgemm_attention.
  * workspace: caller-owned device memory of workspace_floats floats, NULL
  * only with workspace_floats == 0, not overlapping Q, K, V or O
  * (SGEMM_ERR_C_ALIAS); sgemm_attention_splitkv_describe gives the size.

@@ -142,14 +142,16 @@ void make_splitkv_plan(const AttnCall &c, int num_cus, uintptr_t workspace, int6
     std::string ignore;
     const int64_t g = std::min(c.g, c.nb_inner);
     if (c.nb_outer == 0 || c.tq == 0 || c.tk == 0 || c.d == 0 || !mfma_serves(c, ignore)) return;
-    if (g * c.tq > kSkvRows) return;
+    int64_t rows;   // query rows of a group
+    if (!mul64(g, c.tq, rows) || rows > kSkvMaxRows) return;
+    const int64_t row_tiles = (rows + kSkvRows - 1) / kSkvRows;
     // One group's query rows are addressed from one base with 32-bit offsets.
     const int64_t qlast = last_offset(g, c.sQ[1], c.tq, c.sQ[2], c.d, 1);
     int64_t qbytes;
     if (qlast < 0 || !mul64(qlast + 1, 4, qbytes) || qbytes >= kSliceBytes) return;
     const int64_t n_kv = kv_heads(c);
-    int64_t groups;
-    if (!mul64(c.nb_outer, n_kv, groups) || groups > kInt32Max) return;
+    int64_t groups;   // (outer, KV head, row tile) triples: wavefronts per chunk
+    if (!mul64(c.nb_outer, n_kv, groups) || !mul64(groups, row_tiles, groups) || groups > kInt32Max) return;
     // Chunks of a whole number of 32-key blocks.  The kernel's time is taken
     // as that of the busiest CU, ceil(workgroups / CUs) workgroups of four
     // wavefronts each streaming one chunk (the dispatcher spreads them
@@ -210,6 +212,7 @@ void make_splitkv_plan(const AttnCall &c, int num_cus, uintptr_t workspace, int6
     a.scale_log2 = float(double(c.alpha) * 1.4426950408889634);   // alpha * log2(e)
     a.chunks = int(chunks);
     a.chunk_keys = int(chunk_keys);
+    a.row_tiles = int(row_tiles);
     a.items = items;
     sp.chunks = int(chunks);
     sp.chunk_keys = int(chunk_keys);

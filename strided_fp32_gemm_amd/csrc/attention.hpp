@@ -74,12 +74,13 @@ struct AttnPlan {
 };
 
 // Split-KV attention (decode): the g query heads of a KV head and their tq
-// queries (g * tq <= 16) stacked as the 16 rows of one wavefront's tile, the
-// keys cut into chunks, one wavefront per (outer, KV head, chunk) reading
-// its chunk of K and V straight from memory, its partial result (the
+// queries (g * tq <= 64) stacked as the rows of up to four 16-row tiles, the
+// keys cut into chunks, one wavefront per (outer, KV head, row tile, chunk)
+// reading its chunk of K and V straight from memory, its partial result (the
 // unnormalised output rows, their reference maxima and weight sums) written
 // to a workspace; then one merge per output row over the chunks in order.
 constexpr int kSkvRows = 16;                          // query rows of a wavefront's tile
+constexpr int kSkvMaxRows = 4 * kSkvRows;             // rows of a group the split serves
 constexpr int kSkvItemFloats = kSkvRows * 64 + 2 * kSkvRows;   // partial: O rows, m, l
 // Merge cost of one more chunk, in units of one wavefront streaming one
 // 32-key block on the busiest CU (fitted: about 0.06 us against 0.7 us).
@@ -87,7 +88,7 @@ constexpr double kSkvMergePerChunk = 0.1;
 struct SplitKvArgs {
     const float *Q, *K, *V;
     float *O;
-    float *W;                        // workspace: item (o, kv, chunk) at W + item * kSkvItemFloats
+    float *W;                        // workspace: (o, kv, row tile, chunk) at W + index * kSkvItemFloats
     long long sQ_o, sQ_i, sQ_r;      // unit column strides (checked by the planner)
     long long sK_o, sK_i, sK_r;
     long long sV_o, sV_i, sV_r;
@@ -95,7 +96,8 @@ struct SplitKvArgs {
     int nb_inner, n_kv, g, tq, tk, causal;
     float scale_log2;                // alpha * log2(e)
     int chunks, chunk_keys;
-    long long items;                 // nb_outer * n_kv * chunks
+    int row_tiles;                   // 16-row tiles per group, ceil(g * tq / 16)
+    long long items;                 // nb_outer * n_kv * row_tiles * chunks
 };
 struct SplitKvPlan {
     int chunks = 0;                  // 0: not split (the call is sgemm_attention)

@@ -3,13 +3,14 @@
 // With one or a few query rows per head, the fused kernel's workgroup of 128
 // query rows has one busy wavefront and streams the whole KV cache at one
 // wavefront's pace.  Here the g query heads that share a KV head, times their
-// tq queries, are the rows of one 16-row tile (rvllm post, "Matmuls go to
-// cuBLAS": grouped query heads stacked as rows of one product), so K and V
-// are read once per group; and the keys are cut into chunks, one wavefront
-// per (outer, KV head, chunk), so the whole chip streams the cache.  The KV
-// head varies fastest across wavefronts: the four wavefronts of a workgroup
-// read the same key positions of neighbouring heads, which sit side by side
-// in a token-major cache.
+// tq queries, are the rows of 16-row tiles, up to four (rvllm post, "Matmuls
+// go to cuBLAS": grouped query heads stacked as rows of one product), so K and
+// V are read once per tile rather than once per query head; and the keys are
+// cut into chunks, one wavefront per (outer, KV head, row tile, chunk), so the
+// whole chip streams the cache.  Row tile, then KV head, vary fastest across
+// wavefronts: the four wavefronts of a workgroup read the same key positions,
+// of one head (several row tiles) or of neighbouring heads, which sit side by
+// side in a token-major cache.
 //
 // attn_splitkv_d64: per chunk, the online softmax of the fused kernel (the
 // same score layout, S^T = K Q^T on v_mfma_f32_16x16x4_f32 with Q scaled by
@@ -58,16 +59,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const int lane = threadIdx.x & 63, lq = lane & 15, lh = lane >> 4;
     const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= p.items) return;   // uniform across the wavefront; no barrier in this kernel
-    const int kv = int(item % p.n_kv);
-    const long long oc = item / p.n_kv;
+    // Row tile fastest, then KV head: the wavefronts of a workgroup read the
+    // same keys (one KV head's for several row tiles, or neighbouring heads').
+    const int rt = int(item % p.row_tiles);
+    const long long rest = item / p.row_tiles;
+    const int kv = int(rest % p.n_kv);
+    const long long oc = rest / p.n_kv;
     const int c = int(oc % p.chunks);
     const long long o = oc / p.chunks;
-    const long long slot = (o * p.n_kv + kv) * p.chunks + c;   // partials of a group are consecutive
+    // Partials of one (outer, KV head, row tile) are consecutive.
+    const long long slot = ((o * p.n_kv + kv) * p.row_tiles + rt) * p.chunks + c;
 
-    // Row lq of the tile: query head kv*g + qi, query t (rows past gq*tq idle).
+    // Row lq of the tile is row rt*16 + lq of the group: query head
+    // kv*g + row / tq, query row % tq (rows past gq*tq idle).
     const int gq = min(p.g, p.nb_inner - kv * p.g);
-    const bool rok = lq < gq * p.tq;
-    const int qi = rok ? lq / p.tq : 0, t = rok ? lq - qi * p.tq : 0;
+    if (rt * kSkvRows >= gq * p.tq) return;   // a tile of the short last group with no row
+    const int row = rt * kSkvRows + lq;
+    const bool rok = row < gq * p.tq;
+    const int qi = rok ? row / p.tq : 0, t = rok ? row - qi * p.tq : 0;
     const int shift = p.tk - p.tq;                  // causal: query t sees keys j <= t + shift
     const int k0 = c * p.chunk_keys, k1 = min(p.tk, k0 + p.chunk_keys);
     // Last key of the chunk any row sees, and the keys every row sees.
@@ -190,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     }
 }
 
-// One workgroup per output row (outer, KV head, tile row), lane = head
+// One workgroup per output row (outer, KV head, row tile, tile row), lane = head
 // dimension.  Its four wavefronts take consecutive runs of the chunks; each
 // issues the loads of up to sixteen chunks at once and folds them in chunk
 // order into its run's maximum M_w, weighted output sum and weight sum
@@ -200,15 +209,18 @@ __global__ __launch_bounds__(256) void attn_splitkv_merge(SplitKvArgs p) {
     __shared__ float run_m[4], run_den[4], run_num[4][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const long long rowi = blockIdx.x;
-    const int r = int(rowi % kSkvRows);
-    const long long okv = rowi / kSkvRows;
+    const int r = int(rowi % kSkvRows);          // row of the tile
+    const long long tile = rowi / kSkvRows;      // (outer, KV head, row tile)
+    const int rt = int(tile % p.row_tiles);
+    const long long okv = tile / p.row_tiles;
     const int kv = int(okv % p.n_kv);
     const long long o = okv / p.n_kv;
     const int gq = min(p.g, p.nb_inner - kv * p.g);
-    if (r >= gq * p.tq) return;   // uniform across the workgroup
+    const int row = rt * kSkvRows + r;           // row of the group
+    if (row >= gq * p.tq) return;   // uniform across the workgroup
     const int per = (p.chunks + 3) / 4;
     const int c0 = min(wv * per, p.chunks), c1 = min(c0 + per, p.chunks);
-    const float *w = p.W + okv * p.chunks * kSkvItemFloats;
+    const float *w = p.W + tile * p.chunks * kSkvItemFloats;
     // Chunk c's m, l and output element sit at these plus c * kSkvItemFloats.
     const float *wm = w + kSkvRows * 64 + r, *wl = w + kSkvRows * 64 + kSkvRows + r, *wo = w + r * 64 + lane;
     float M = -INFINITY, num = 0.0f, den = 0.0f;
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(256) void attn_splitkv_merge(SplitKvArgs p) {
         tn += f * run_num[x][lane];
         td += f * run_den[x];
     }
-    const int qi = r / p.tq, t = r - qi * p.tq;
+    const int qi = row / p.tq, t = row - qi * p.tq;
     p.O[o * p.sO_o + (long long)(kv * p.g + qi) * p.sO_i + (long long)t * p.sO_r + lane] = tn / td;
 }
 

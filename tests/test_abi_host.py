@@ -290,15 +290,18 @@ def test_splitkv_chunk_count_is_the_cheapest_by_exhaustive_search(monkeypatch):
     times the blocks of the longest chunk, plus 0.1 per chunk; the cheapest
     count giving each of the 256 CUs a workgroup, else the cheapest overall;
     ties to the most chunks, as the planner meets them first) must agree on
-    random decode shapes, with and without a workspace cap."""
+    random decode shapes (1 to 64 rows per group, so 1 to 4 row tiles), with
+    and without a workspace cap."""
     monkeypatch.delenv("SGEMM_ATTN_CHUNKS", raising=False)
     rng = np.random.default_rng(404)
     cus, item = 256, 16 * 64 + 32
     for _ in range(60):
         no, hk, g = int(rng.integers(1, 65)), int(rng.integers(1, 9)), int(rng.integers(1, 9))
-        tk = int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(600, 70000))]))
+        tq = int(rng.integers(1, 64 // g + 1))
+        tk = int(rng.choice([int(rng.integers(tq, 600)), int(rng.integers(600, 70000))]))
         h = hk * g
-        groups, blocks = no * hk, -(-tk // 32)
+        tiles = -(-(g * tq) // 16)                  # 16-row tiles per (outer, KV head)
+        groups, blocks = no * hk * tiles, -(-tk // 32)
         cap = blocks
         ws = -1
         if rng.random() < 0.3:
@@ -317,10 +320,10 @@ def test_splitkv_chunk_count_is_the_cheapest_by_exhaustive_search(monkeypatch):
         want = (best.get("fill") or best["any"])[1]
         keys = -(-(-(-tk // want)) // 32) * 32
         want = -(-tk // keys)
-        sQ, sK = (h * 64, 64, h * 64, 1), (tk * hk * 64, 64, hk * 64, 1)
-        got = sg.sgemm_attention_splitkv_describe(no, h, 1, tk, 64, 0.125, 1, PA, *sQ, PB, sK[0], sK[1], g, sK[2],
+        sQ, sK = (tq * h * 64, 64, h * 64, 1), (tk * hk * 64, 64, hk * 64, 1)
+        got = sg.sgemm_attention_splitkv_describe(no, h, tq, tk, 64, 0.125, 1, PA, *sQ, PB, sK[0], sK[1], g, sK[2],
                                                   sK[3], PB + (1 << 35), *sK, PC, *sQ, workspace_floats=ws)
-        assert (got["chunks"], got["chunk_keys"]) == (want, keys), (no, hk, g, tk, ws, got, want, keys)
+        assert (got["chunks"], got["chunk_keys"]) == (want, keys), (no, hk, g, tq, tk, ws, got, want, keys)
         assert got["workspace_floats"] == groups * want * item and (want - 1) * keys < tk <= want * keys
 
 
@@ -329,9 +332,11 @@ def test_splitkv_attention_validates_and_plans_before_the_device(monkeypatch):
     (size >= 0, NULL only when empty, no overlap with Q, K, V or O) before
     any device call, and plans without a device: a decode step (one query,
     g = 3 query heads per KV head, 4096 keys, 8 x 5 groups) takes 43 chunks of
-    96 keys, 1056 floats of workspace per chunk; a prefill, g * tq above 16,
-    a head dimension other than 64 and a workspace below one chunk per group
-    are not split; SGEMM_ATTN_CHUNKS fixes the count.  Other chunk counts
+    96 keys, 1056 floats of workspace per chunk; 20 rows per group (g = 5,
+    tq = 4) take two 16-row tiles, so twice the partials per chunk; a
+    prefill, g * tq above 64, a head dimension other than 64 and a workspace
+    below one chunk per group and tile are not split; SGEMM_ATTN_CHUNKS fixes
+    the count.  Other chunk counts
     worked by hand from the planner's rule (the busiest CU's workgroups times
     their blocks, plus 0.1 per chunk, over the counts that give each of the
     256 CUs a workgroup): 16384 keys over 40 groups take 74 chunks of 224
@@ -346,7 +351,9 @@ def test_splitkv_attention_validates_and_plans_before_the_device(monkeypatch):
     d = lambda ws=-1, **kw: sg.sgemm_attention_splitkv_describe(*args(**kw), workspace_floats=ws)
     assert d() == {"chunks": 43, "chunk_keys": 96, "workspace_floats": 43 * 40 * 1056}
     assert d(tq=512, tk=512)["chunks"] == 0                                   # prefill
-    assert d(g=5, tq=4)["chunks"] == 0 and d(g=5, tq=3)["chunks"] > 0       # 20 rows, 15 rows
+    two = d(g=5, tq=4)                                                        # 20 rows: 2 tiles
+    assert two["workspace_floats"] == two["chunks"] * 8 * 3 * 2 * 1056, two
+    assert d(g=5, tq=13)["chunks"] == 0 and d(g=5, tq=12)["chunks"] > 0     # 65 rows, 60 rows
     assert d(d=32)["chunks"] == 0
     assert d(ws=40 * 1056 - 1)["chunks"] == 0 and d(ws=3 * 40 * 1056)["chunks"] == 3
     assert (d(tk=16384)["chunks"], d(tk=16384)["chunk_keys"]) == (74, 224)

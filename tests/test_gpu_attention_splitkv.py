@@ -5,10 +5,11 @@ The chunked softmax and the merge regroup the keys' sums; the result must
 meet the same derived bound as the fused kernel (tests/test_gpu_attention.py:
 2 max|V| (2 Delta + (5 tk + 16) u), Delta the scores' rounding), be
 reproducible bit for bit, and, when the call is not split (a prefill, g * tq
-above 16, no workspace), equal sgemm_attention exactly.  Decode shapes cover
-grouped KV heads with a partial last group, several queries per head, causal
-and not, both layouts, ragged key counts and chunk edges, forced chunk
-counts, and a workspace filled with NaN on entry.
+above 64, no workspace), equal sgemm_attention exactly.  Decode shapes cover
+grouped KV heads with a partial last group, several queries per head (one to
+four 16-row tiles per group, partial tiles, a last group whose second tile
+has no row), causal and not, both layouts, ragged key counts and chunk
+edges, forced chunk counts, and a workspace filled with NaN on entry.
 """
 import numpy as np
 import pytest
@@ -97,6 +98,11 @@ DECODE = [  # (nb_outer, nb_inner, g, tq, tk, causal, order)
     (1, 7, 3, 1, 300, True, "tokens"),     # groups of 3, 3 and 1 query heads
     (2, 4, 2, 8, 129, True, "tokens"),     # 16 rows, causal within the last 8 positions
     (1, 2, 1, 1, 17, False, "heads"),      # fewer keys than a block
+    (2, 8, 8, 4, 700, True, "tokens"),     # 32 rows: two tiles
+    (1, 12, 4, 16, 1000, True, "heads"),   # 64 rows: four tiles, causal over the last 16 positions
+    (2, 6, 3, 7, 300, False, "tokens"),    # 21 rows: a partial second tile
+    (1, 7, 7, 9, 257, True, "tokens"),     # 63 rows
+    (3, 10, 4, 5, 400, True, "tokens"),    # groups of 4, 4, 2 heads: the last group's second tile is empty
 ]
 
 
@@ -129,7 +135,7 @@ def test_large_scores_move_the_reference():
 
 
 def test_unsplit_calls_run_as_sgemm_attention():
-    """A prefill (g * tq above 16) and a decode without a workspace are not
+    """A prefill (g * tq above 64) and a decode without a workspace are not
     split: the same bits as sgemm_attention."""
     pre = wl.random_attention(81, 1, 4, 96, 96, 64, g=2, causal=True, order="tokens")
     assert describe(pre)["chunks"] == 0
