@@ -151,7 +151,9 @@ void make_splitkv_plan(const AttnCall &c, int num_cus, uintptr_t workspace, int6
     if (qlast < 0 || !mul64(qlast + 1, 4, qbytes) || qbytes >= kSliceBytes) return;
     const int64_t n_kv = kv_heads(c);
     int64_t groups;   // (outer, KV head, row tile) triples: wavefronts per chunk
-    if (!mul64(c.nb_outer, n_kv, groups) || !mul64(groups, row_tiles, groups) || groups > kInt32Max) return;
+    // The merge launches 16 workgroups per triple.
+    if (!mul64(c.nb_outer, n_kv, groups) || !mul64(groups, row_tiles, groups) || groups > kInt32Max / kSkvRows)
+        return;
     // Chunks of a whole number of 32-key blocks.  The kernel's time is taken
     // as that of the busiest CU, ceil(workgroups / CUs) workgroups of four
     // wavefronts each streaming one chunk (the dispatcher spreads them

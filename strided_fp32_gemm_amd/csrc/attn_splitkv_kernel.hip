@@ -277,8 +277,11 @@ int launch_splitkv(const SplitKvPlan &sp, hipStream_t stream, std::string &why) 
     const SplitKvArgs &a = sp.args;
     const long long rows = a.items / a.chunks * kSkvRows;
     hipLaunchKernelGGL(attn_splitkv_d64, dim3(unsigned((a.items + 3) / 4)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_splitkv_merge, dim3(unsigned(rows)), dim3(256), 0, stream, a);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {   // the merge only after the partials' launch went in
+        hipLaunchKernelGGL(attn_splitkv_merge, dim3(unsigned(rows)), dim3(256), 0, stream, a);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) {
         why = std::string("split-KV attention launch failed: ") + hipGetErrorString(e);
         return kErrHip;
