@@ -200,10 +200,13 @@ double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
 // of the split partials through LDS, and memory latency the round cannot
 // hide (a SIMD with a single wavefront hides less of it: kLoneWave); then
 // the HBM floor.  Rates and constants were fitted to tile and split sweeps
-// on MI355X.
+// on MI355X; every tile competes on every shape (the 16-wide tiles too: on
+// 270 random shapes with m or n above 16 they were often the fastest), and
+// the narrow-contiguous factor was set on those sweeps (mean regret against
+// the fastest tile and split 10.4% -> 6.9% on 120 shapes not used to set it).
 double wave_cost(const Plan &p, const WaveCfg &t, int splits, int num_cus) {
     const double kFlopPerSimdCycle = 64.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 11.0;
-    const double kLdsBytesPerCycle = 128.0, kLatency = 2720.0, kLoneWave = 0.8;
+    const double kLdsBytesPerCycle = 128.0, kLatency = 2720.0, kLoneWave = 0.8, kNarrowContiguous = 0.85;
     const double tiles = double(p.batch) * double((p.m + t.bm - 1) / t.bm) * double((p.n + t.bn - 1) / t.bn);
     const double cus = double(std::max(num_cus, 1));
     const double fit = std::max(1.0, std::floor(4.0 * t.waves_per_simd / splits));
@@ -212,7 +215,11 @@ double wave_cost(const Plan &p, const WaveCfg &t, int splits, int num_cus) {
     const double groups = double((p.k + 15) / 16);
     const double kwave = std::ceil(groups / splits) * 16.0;   // k of one wavefront
     const double per_simd = std::max(1.0, occ * splits / 4.0);
-    const double rate = t.rate * (occ * splits <= 4.0 ? kLoneWave : 1.0);
+    // A 16-wide tile along an operand's contiguous axis (A m-fast with 16
+    // rows, B n-fast with 16 columns) reads that operand in short segments.
+    const double narrow = (!p.a_kfast && t.bm == 16 ? kNarrowContiguous : 1.0) *
+                          (!p.b_kfast && t.bn == 16 ? kNarrowContiguous : 1.0);
+    const double rate = t.rate * narrow * (occ * splits <= 4.0 ? kLoneWave : 1.0);
     const double compute = per_simd * t.bm * t.bn * 2.0 * kwave / kFlopPerSimdCycle / rate;
     const double operands = occ * double(t.bm + t.bn) * groups * 16.0 * 4.0 / kOperandBytesPerCycle;
     const double epilogue = occ * t.bm * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
@@ -422,9 +429,6 @@ int make_plan(const GemmArgs &a, Family family, int num_cus, Plan &p, std::strin
             const int64_t groups = (p.k + 15) / 16;
             for (int t = 0; t < kNumWaveTiles; ++t) {
                 if (!allowed(kWaveTiles[t].name)) continue;
-                // 16-wide tiles serve a dimension of at most 16 (unforced).
-                if (!force && ((kWaveTiles[t].bm == 16 && p.m > 16) || (kWaveTiles[t].bn == 16 && p.n > 16)))
-                    continue;
                 const int most = std::min(kWaveTiles[t].max_split, fixed_split ? fixed_split : kWaveMaxSplit);
                 const int64_t tiles = p.batch * ((p.m + kWaveTiles[t].bm - 1) / kWaveTiles[t].bm) *
                                       ((p.n + kWaveTiles[t].bn - 1) / kWaveTiles[t].bn);

@@ -138,7 +138,7 @@ def test_column_major_output_is_solved_transposed():
 
 
 def test_offsets_beyond_32_bits_use_the_generic_path():
-    huge = 1 << 25  # row stride of 2^25 floats: even 32 rows span > 2^31 bytes
+    huge = 1 << 27  # row stride of 2^27 floats: even 16 rows span > 2^31 bytes
     p = plan(1, 256, 256, 64, (0, huge, 1), (0, 256, 1), (0, 256, 1))
     assert p["path_name"] == "generic"
     forced = plan(1, 256, 256, 64, (0, huge, 1), (0, 256, 1), (0, 256, 1), path=sg.PATH_MFMA)
@@ -498,16 +498,18 @@ def test_skinny_products_split_k_over_wavefronts(monkeypatch):
     """Products with too few tiles to occupy the SIMDs unsplit and a long k
     plan the wavefront kernel with k split over several wavefronts of a
     workgroup (measured on MI355X: 1 x 4096 x 4096 from 100 us unsplit on
-    32 x 32 tiles to 18 us on 16 x 32 tiles split 8 ways); the 16-wide
-    tiles serve dimensions of at most 16; products with enough tiles, or
-    too short a k, stay unsplit.  SGEMM_WAVE_SPLIT forces a split (rounded
+    32 x 32 tiles to 18 us on 16 x 32 tiles split 8 ways); 16-wide tiles
+    compete on any shape (4096 x 1 x 4096 on 16 x 32 split 8: 15.7 us
+    against 20.0 on 32 x 16; 24 x 4096 x 4096 on 16 x 32: 21.2 against 27.6
+    on 32 x 32); products with enough tiles, or too short a k, stay
+    unsplit.  SGEMM_WAVE_SPLIT forces a split (rounded
     down to a power of two, capped by the tile), and the describe call
     reports the wavefronts per workgroup."""
     gemv = plan(1, 1, 4096, 4096, (0, 4096, 1), (0, 4096, 1), (0, 4096, 1))
     assert gemv["kernel"] == "wave_w16x32_ak_bn_s8" and gemv["waves"] == 8, gemv
     assert gemv["tile_m"] == 16 and gemv["tile_n"] == 32 and gemv["workgroups"] == 128
     tall = plan(1, 4096, 1, 4096, (0, 4096, 1), (0, 1, 1), (0, 1, 1))
-    assert tall["kernel"].startswith("wave_w32x16_") and tall["waves"] == 8, tall
+    assert tall["kernel"] == "wave_w16x32_ak_bk_s8", tall
     few = plan(1, 1, 1000, 16384, (0, 16384, 1), (0, 1, 16384), (0, 1000, 1))
     assert few["waves"] == 8 and few["workgroups"] == 32, few
     # Enough tiles to give every SIMD a wavefront: no split.
@@ -516,10 +518,9 @@ def test_skinny_products_split_k_over_wavefronts(monkeypatch):
     # k of 64 is four 16-deep groups: too short to split.
     short = plan(1, 1, 4096, 64, (0, 64, 1), (0, 4096, 1), (0, 4096, 1))
     assert not re.search(r"_s\d+$", short["kernel"]), short
-    # 16-wide tiles only for a dimension of at most 16.
-    for m in (24, 64):
-        p = plan(1, m, 4096, 4096, (0, 4096, 1), (0, 4096, 1), (0, 4096, 1))
-        assert p["tile_m"] != 16, p
+    # 16-wide tiles beyond 16 rows where they measured faster.
+    p = plan(1, 24, 4096, 4096, (0, 4096, 1), (0, 4096, 1), (0, 4096, 1))
+    assert p["kernel"] == "wave_w16x32_ak_bn_s8", p
     # Forced splits.
     monkeypatch.setenv("SGEMM_FORCE_TILE", "w32x64")
     monkeypatch.setenv("SGEMM_WAVE_SPLIT", "16")
