@@ -169,10 +169,11 @@ double stream_floor(const Plan &p, double cost, double workgroups, int num_cus) 
 // too few tiles) a CU's matrix cores idle more, so the rate drops by up to
 // kLowOccupancy.  The first two slices' memory latency is not hidden.  Rates
 // and constants were fitted to tile sweeps on MI355X (the benchmark
-// workloads and twelve other shapes; mean regret 0.5%).
+// workloads and twelve other shapes; mean regret 0.5%); the single-slice term
+// for 16x16 tiles to a sweep of every tile on 270 random products.
 double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
     const double kFlopPerCuCycle = 256.0, kOperandBytesPerCycle = 64.0, kStoreBytesPerCycle = 11.0;
-    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 368.0, kLowOccupancy = 0.05;
+    const double kLdsBytes = 160.0 * 1024.0, kSliceLatency = 368.0, kLowOccupancy = 0.05, kShortK16 = 0.1;
     const long long slices = (p.k + t.bk - 1) / t.bk;
     const double tiles = double(p.batch) * double((p.m + t.bm - 1) / t.bm) * double((p.n + t.bn - 1) / t.bn);
     const double cus = double(std::max(num_cus, 1));
@@ -184,7 +185,10 @@ double tile_cost(const Plan &p, const TileCfg &t, int num_cus) {
     const double compute = double(t.bm) * t.bn * 2.0 * kpad / kFlopPerCuCycle / rate;
     const double operands = double(t.bm + t.bn) * kpad * 4.0 / kOperandBytesPerCycle;
     const double epilogue = double(t.bm) * t.bn * 4.0 * (p.accumulate ? 2.0 : 1.0) / kStoreBytesPerCycle;
-    return stream_floor(p, per_cu * (std::max(compute, operands) + epilogue) +
+    // With a single k slice the 16x16 tiles' longer fragment bookkeeping is
+    // not amortised: there the 32x32 tiles measured 10-21% faster.
+    const double short_k = t.mf == 16 && slices <= 1 ? kShortK16 * t.bm * t.bn : 0.0;
+    return stream_floor(p, per_cu * (std::max(compute, operands) + epilogue + short_k) +
                                kSliceLatency * std::min<double>(double(slices), 2.0), tiles, num_cus);
 }
 
