@@ -113,3 +113,54 @@ def sgemm(A, B, C, alpha: float = 1.0, accumulate: bool = False, path: int = PAT
             sgemm_strided_batched_path(batch, m, n, k, alpha, A, *sa, B, *sb, accumulate, C, *sc,
                                        path=path, stream=stream)
     return C
+
+
+def attention(Q, K, V, O, alpha: float = None, causal: bool = False, stream=None, splitkv: bool = True):
+    """O <- softmax(alpha Q K^T [causal]) V for torch float32 views on one GPU.
+
+    Q and O are [outer, heads, tq, d], K and V [outer, kv_heads, tk, d], any
+    strides (a token-major cache [outer, t, heads, d] passes as
+    ``x.transpose(1, 2)``, no copy); query head i reads KV head
+    i // (heads // kv_heads).  alpha defaults to 1/sqrt(d).  With
+    splitkv=True (the default) a decode-shaped call goes through
+    sgemm_attention_splitkv with the workspace its plan asks for, allocated
+    here with torch; any other call, and splitkv=False, through
+    sgemm_attention.  Runs on ``stream`` (default: torch's current stream)
+    and returns O.
+    """
+    import math
+    import torch
+
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{nm} must be a torch.Tensor")
+        if t.dtype != torch.float32 or t.device.type != "cuda" or t.dim() != 4:
+            raise ValueError(f"{nm} must be a 4-D float32 tensor on the GPU")
+    if not (Q.device == K.device == V.device == O.device):
+        raise ValueError("Q, K, V and O must be on the same device")
+    no, h, tq, d = Q.shape
+    hk, tk = K.shape[1], K.shape[2]
+    if tuple(O.shape) != (no, h, tq, d) or tuple(K.shape) != (no, hk, tk, d) or tuple(V.shape) != (no, hk, tk, d):
+        raise ValueError(f"shape mismatch: Q {tuple(Q.shape)}, K {tuple(K.shape)}, V {tuple(V.shape)}, "
+                         f"O {tuple(O.shape)}")
+    if hk == 0 or h % hk:
+        raise ValueError(f"{h} query heads do not split evenly over {hk} KV heads")
+    g = h // hk
+    if alpha is None:
+        alpha = 1.0 / math.sqrt(d) if d else 1.0
+    args = [no, h, tq, tk, d, alpha, int(causal), Q, *Q.stride(), K, K.stride(0), K.stride(1), g,
+            K.stride(2), K.stride(3), V, *V.stride(), O, *O.stride()]
+    if stream is None:
+        stream = torch.cuda.current_stream(O.device)
+    with torch.cuda.device(O.device):
+        plan = sgemm_attention_splitkv_describe(*args, num_cus=0) if splitkv else {"chunks": 0}
+        if plan["chunks"]:
+            floats = plan["workspace_floats"]
+            work = torch.empty(floats, dtype=torch.float32, device=O.device)
+            sgemm_attention_splitkv(*args, work, floats, stream=stream)
+            # The workspace must outlive the enqueued launches on `stream`.
+            work.record_stream(stream if isinstance(stream, torch.cuda.Stream) else
+                               torch.cuda.ExternalStream(_binding._stream(stream)))
+        else:
+            sgemm_attention(*args, stream=stream)
+    return O

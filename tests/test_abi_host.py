@@ -588,3 +588,14 @@ def test_fixed_offsets_where_the_buffer_size_bounds_k():
     assert plan(1, 128, 128, 1, (0, 1, 1 << 30), (0, 128, 1), (0, 128, 1), path=mfma)["fixed_offsets"] == 0
     # Other kernel families never use it.
     assert plan(1, 100, 90, 70, (0, 70, 1), (0, 90, 1), (0, 90, 1), path=sg.PATH_WAVE)["fixed_offsets"] == 0
+
+
+def test_torch_attention_helper_checks_its_arguments():
+    """sg.attention refuses non-tensors and tensors off the GPU before any
+    device call."""
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 3, 64)
+    with pytest.raises(TypeError):
+        sg.attention(x.numpy(), x, x, x)
+    with pytest.raises(ValueError, match="on the GPU"):
+        sg.attention(x, x, x, x)

@@ -163,3 +163,31 @@ def test_workload_full_size(name):
     got, plan = check(p)
     assert plan["chunks"] > 1, plan
     assert np.array_equal(got, split_call(p, poison=False)[0])
+
+
+@pytest.mark.parametrize("tq,causal", [(1, True), (4, True), (96, True), (3, False)])
+def test_torch_attention_helper(tq, causal):
+    """sg.attention on torch views of token-major buffers ([outer, t, heads,
+    d] passed as .transpose(1, 2), no copy), grouped KV heads, on a side
+    stream: decode-shaped calls take the split (workspace allocated by the
+    helper), a prefill the fused kernel; both within the fused kernel's
+    bound against the oracle."""
+    no, h, g, tk, d = 2, 6, 3, 700, 64
+    p = wl.random_attention(300 + tq, no, h, tq, tk, d, g=g, causal=causal, order="tokens")
+    hk = h // g
+    Q = dev(p.Q.storage).view(no, tq, h, d).transpose(1, 2)
+    K = dev(p.K.storage).view(no, tk, hk, d).transpose(1, 2)
+    V = dev(p.V.storage).view(no, tk, hk, d).transpose(1, 2)
+    Ot = dev(p.O.storage)
+    O = Ot.view(no, tq, h, d).transpose(1, 2)
+    split = describe(p)["chunks"] > 0
+    assert split == (tq * g <= 64), describe(p)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sg.attention(Q, K, V, O, alpha=p.alpha, causal=causal)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    got, ref = out(p, Ot.cpu().numpy()), out(p, oracle_call(p))
+    err = float(np.abs(got.astype(np.float64) - ref).max())
+    assert err <= tolerance(p), (tq, causal, err, tolerance(p))
