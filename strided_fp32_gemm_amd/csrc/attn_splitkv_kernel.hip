@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     }
 }
 
-// One workgroup per output row (outer, KV head, row tile, tile row), lane = head
+// One workgroup per output row (outer, KV head, row of the group), lane = head
 // dimension.  Its four wavefronts take consecutive runs of the chunks; each
 // issues the loads of up to sixteen chunks at once and folds them in chunk
 // order into its run's maximum M_w, weighted output sum and weight sum
@@ -208,16 +208,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 __global__ __launch_bounds__(256) void attn_splitkv_merge(SplitKvArgs p) {
     __shared__ float run_m[4], run_den[4], run_num[4][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    // One workgroup per row of a group (g * tq of them; the short last
+    // group's surplus rows return at once).
     const long long rowi = blockIdx.x;
-    const int r = int(rowi % kSkvRows);          // row of the tile
-    const long long tile = rowi / kSkvRows;      // (outer, KV head, row tile)
-    const int rt = int(tile % p.row_tiles);
-    const long long okv = tile / p.row_tiles;
+    const int row = int(rowi % (p.g * p.tq));    // row of the group
+    const long long okv = rowi / (p.g * p.tq);   // (outer, KV head)
     const int kv = int(okv % p.n_kv);
     const long long o = okv / p.n_kv;
     const int gq = min(p.g, p.nb_inner - kv * p.g);
-    const int row = rt * kSkvRows + r;           // row of the group
     if (row >= gq * p.tq) return;   // uniform across the workgroup
+    const int r = row % kSkvRows;                // row of its tile
+    const long long tile = okv * p.row_tiles + row / kSkvRows;   // (outer, KV head, row tile)
     const int per = (p.chunks + 3) / 4;
     const int c0 = min(wv * per, p.chunks), c1 = min(c0 + per, p.chunks);
     const float *w = p.W + tile * p.chunks * kSkvItemFloats;
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(256) void attn_splitkv_merge(SplitKvArgs p) {
 
 int launch_splitkv(const SplitKvPlan &sp, hipStream_t stream, std::string &why) {
     const SplitKvArgs &a = sp.args;
-    const long long rows = a.items / a.chunks * kSkvRows;
+    const long long rows = a.items / a.chunks / a.row_tiles * a.g * a.tq;   // (outer, KV head) x g * tq
     hipLaunchKernelGGL(attn_splitkv_d64, dim3(unsigned((a.items + 3) / 4)), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) {   // the merge only after the partials' launch went in
