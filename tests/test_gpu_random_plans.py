@@ -22,7 +22,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-6
-CASES = 120
+CASES = 240
 
 
 @pytest.fixture(scope="module", autouse=True)
