@@ -63,6 +63,10 @@ DEFAULT_WORKLOAD = "square4096_acc"
 # attention scores Q K^T and the product P V, and the spectrogram.
 CONFIG_WORKLOADS = (("1", "square64"), ("2", "linear_xWt"), ("3a", "attn_qk"), ("3b", "attn_pv"),
                     ("4", "spectrogram"))
+# Workloads beyond the method's set, timed after it in the default run (no
+# oracle slice): fused attention plain and causal, the skinny product, the
+# split-k weight gradient and the split-KV decode step.
+EXTRA_WORKLOADS = ("attn_fused", "attn_fused_causal", "skinny_xWt", "linear_dw_deep", "attn_decode")
 CONFIG_CPU_SECONDS = 1.5          # oracle slice per configuration (the headline's is --cpu-seconds)
 CONFIG_STEPS = 100                # timed launches per configuration
 
@@ -382,6 +386,19 @@ def config_entry(label: str, name: str) -> dict:
     return e
 
 
+def extra_entry(name: str) -> dict:
+    """A workload beyond the method's set: its step's mean time (every launch
+    of the step) against the roof its arithmetic intensity sets."""
+    from strided_fp32_gemm_amd import workloads as wl
+
+    p, info, _, mean_ms, _, warmup = measure(name, CONFIG_STEPS, None, CONFIG_WARMUP_SECONDS)
+    flops = float(p.flops)
+    e = {"config": "extra", "workload": name, "kernel": info["kernel"], "steps": CONFIG_STEPS, "warmup": warmup,
+         "launch_ms_mean": round(mean_ms, 5), "tflops": round(flops / (mean_ms * 1e-3) / 1e12, 3)}
+    e["roofline"] = _roofline_bound(flops, wl.algorithmic_bytes(p), mean_ms)
+    return e
+
+
 def bench_one(name: str, steps: int, warmup, cpu_seconds: float) -> dict:
     from strided_fp32_gemm_amd import workloads as wl
 
@@ -535,6 +552,9 @@ def configs_object(headline: dict, cpu_seconds: float) -> dict:
     out["attn_qk_plus_pv"] = {"config": "3", "workload": "attn_qk + attn_pv",
                               "launch_ms_mean": round(ms, 5), "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
                               "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP32_MATRIX_TFLOPS, 4)}
+    for name in EXTRA_WORKLOADS:
+        print(f"[bench] extra: {name}", file=sys.stderr, flush=True)
+        out[name] = extra_entry(name)
     r = headline["roofline"]
     out["square4096_acc"] = {"config": "5", "workload": DEFAULT_WORKLOAD, "kernel": r["kernel"],
                              "launch_ms_mean": r["launch_ms_mean"], "tflops": r["achieved"],
